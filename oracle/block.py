@@ -1,0 +1,386 @@
+"""CPU oracle of one Llama-shaped decoder block (plain, slow, eager numpy).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or
+executes this module: only the tests, the smoke check and the bench's CPU
+baseline leg do.  It shares no code with the HIP path (no kernels, tables,
+constants or helpers); the two meet only at the seeded inputs.
+
+What it computes is the block of the mojolearn ``TransformerBlock`` API page
+("Llama-style transformer decoder block"; the class description says it
+computes Hugging Face's LlamaDecoderLayer.forward): input RMSNorm, q/k/v
+projections with [out, in] weights, RoPE, grouped-query causal attention over
+a caller-owned KV cache (optionally a sliding window over a ring of W slots),
+o_proj plus residual, post-attention RMSNorm, gated MLP plus residual.  The
+component formulas are the ones printed on the DantinoX "Core Layers — Deep
+Reference" page: RMSNorm (Normalisation / RMSNorm equations), RoPE (Positional
+Encoding / RoPE rotation and frequency), GELU and SwiGLU (Feed-Forward
+Network), and the pre-norm residual block (`Block` — the unified transformer
+block).
+
+Readings of points the pages leave open (each is listed with its reason in the
+design notes of the repository):
+  * RoPE rotates the Hugging Face "rotate-half" pairs (i, i + hd/2) with the
+    page's frequencies theta_i = base^(-2i/hd); the DantinoX page prints the
+    interleaved pairs (2i, 2i+1), which is the same map up to a fixed
+    permutation of each head's dimensions.  Angles and cos/sin are formed in
+    float64 and rounded to the oracle's working precision.
+  * A window W means W keys including the query's own position: keys
+    [max(0, p - W + 1), p] (mojolearn ``window`` parameter).
+  * Masked keys are excluded from the softmax (not given a -1e9 bias).
+  * The softcap is c * tanh(s / c) applied to the scaled score
+    s = q.k / sqrt(hd), before the mask and the softmax.
+  * The attention scale is 1 / sqrt(hd).
+  * qk_norm normalises each head's q and k over head_dim after the
+    projection (and its bias) and before RoPE, with the block's eps and norm
+    kind.
+  * The cache holds post-RoPE keys and raw values; under a window each
+    (row, kv head) keeps a ring of W slots with slot = position mod W.
+  * Each batch row carries its own cached length (positions of row b in a
+    call are lengths[b] + t).
+  * Keys of positions produced in the same call are read from the call's
+    fresh k/v, so a windowed prefill longer than W is exact; afterwards the
+    ring holds the last W positions.
+
+Precision: float32 by default (the page's block is float32 in and out);
+``dtype=np.float64`` gives a float64 run used to bound the float32 oracle's
+own rounding error.  ``layout="rowwise"`` computes every token with the same
+vector operations whether it arrives in a prefill or in a decode step, so
+decode and prefill agree bit for bit (the page's "identical" mode claim).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "rms_norm", "rope_cos_sin", "apply_rope", "silu", "gelu_tanh", "attention_row",
+    "OracleState", "block_forward", "block_step",
+]
+
+
+# --------------------------------------------------------------------------
+# Sublayers
+# --------------------------------------------------------------------------
+def rms_norm(x: np.ndarray, w: np.ndarray, eps: float, offset: bool = False) -> np.ndarray:
+    """RMSNorm over the last axis: x / sqrt(mean(x^2) + eps) * g.
+
+    DantinoX "Core Layers" page, Normalisation / RMSNorm: RMS(x) =
+    sqrt(mean(x_i^2) + eps), y = x / RMS(x) * gamma (eps inside the square
+    root, no bias).  mojolearn ``norm='rmsnorm_offset'`` scales by 1 + w
+    (Gemma) instead of w.  Computed in the dtype of ``x``.
+    """
+    dt = x.dtype
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    g = w.astype(dt)
+    if offset:
+        g = dt.type(1.0) + g
+    return x / np.sqrt(ms + dt.type(eps)) * g
+
+
+def rope_cos_sin(positions: np.ndarray, head_dim: int, theta: float) -> tuple[np.ndarray, np.ndarray]:
+    """cos and sin of p * theta_i for i in [0, hd/2), in float64.
+
+    DantinoX "Core Layers" page, Positional Encoding / RoPE: rotation of each
+    dimension pair by p * theta_i with theta_i = base^(-2i/d_h); the base is
+    the block's ``rope_theta`` (mojolearn parameter).  Returns arrays of shape
+    positions.shape + (hd/2,).
+    """
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    inv_freq = np.float64(theta) ** (-2.0 * i / head_dim)
+    ang = np.asarray(positions, dtype=np.float64)[..., None] * inv_freq
+    return np.cos(ang), np.sin(ang)
+
+
+def apply_rope(u: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """Rotate pairs (i, i + hd/2) of the last axis by the given angles.
+
+    u' _i        = u_i cos a_i - u_{i+hd/2} sin a_i
+    u'_{i+hd/2}  = u_{i+hd/2} cos a_i + u_i sin a_i
+    (the page's 2x2 rotation, applied to Hugging Face's rotate-half pairs).
+    ``cos``/``sin`` broadcast against u[..., :hd/2].
+    """
+    half = u.shape[-1] // 2
+    a, b = u[..., :half], u[..., half:]
+    c, s = cos.astype(u.dtype), sin.astype(u.dtype)
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU / swish: z * sigmoid(z) = z / (1 + exp(-z)) (DantinoX page, SwiGLU)."""
+    with np.errstate(over="ignore"):
+        return z / (z.dtype.type(1.0) + np.exp(-z))
+
+
+def gelu_tanh(z: np.ndarray) -> np.ndarray:
+    """GELU, tanh approximation: 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
+
+    DantinoX page, Feed-Forward Network / GELU equation; dew's GatedMLP calls
+    this form "geglu" when it gates.
+    """
+    t = z.dtype.type
+    c = t(np.sqrt(2.0 / np.pi))
+    return t(0.5) * z * (t(1.0) + np.tanh(c * (z + t(0.044715) * z * z * z)))
+
+
+def attention_row(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos: np.ndarray,
+                  k_pos: np.ndarray, window: int, softcap: float,
+                  q_chunk: int = 1024) -> np.ndarray:
+    """Grouped-query causal attention for one batch row.
+
+    q [Lq, H, hd], k/v [Lk, KV, hd] with absolute positions q_pos [Lq] and
+    k_pos [Lk].  Query head h reads kv head h // G with G = H / KV (DantinoX
+    page, MHA and GQA: a group of n_heads // kv_heads query heads shares one
+    kv head).  Key s is in the set of query t iff k_pos[s] <= q_pos[t] and,
+    with a window W > 0, k_pos[s] >= q_pos[t] - W + 1 (mojolearn ``window``).
+    Scores q.k / sqrt(hd), optional softcap c * tanh(s / c), softmax over the
+    key set (excluded keys take no part), weighted sum of values.
+
+    Queries are processed in chunks of ``q_chunk`` rows to bound memory; each
+    row's arithmetic does not depend on the chunking.
+    """
+    Lq, H, hd = q.shape
+    KV = k.shape[1]
+    G = H // KV
+    dt = q.dtype
+    scale = dt.type(1.0 / np.sqrt(hd))
+    out = np.zeros((Lq, H, hd), dtype=dt)
+    for c0 in range(0, Lq, q_chunk):
+        c1 = min(Lq, c0 + q_chunk)
+        qp = q_pos[c0:c1]
+        allowed = k_pos[None, :] <= qp[:, None]
+        if window > 0:
+            allowed &= k_pos[None, :] >= qp[:, None] - (window - 1)
+        cols = np.nonzero(allowed.any(axis=0))[0]
+        if cols.size == 0:
+            continue
+        lo, hi = cols[0], cols[-1] + 1
+        allowed = allowed[:, lo:hi]
+        for h in range(H):
+            j = h // G
+            s = (q[c0:c1, h, :] @ k[lo:hi, j, :].T) * scale
+            if softcap:
+                cap = dt.type(softcap)
+                s = cap * np.tanh(s / cap)
+            s = np.where(allowed, s, dt.type(-np.inf))
+            m = np.max(s, axis=-1, keepdims=True)
+            e = np.exp(s - m)
+            p = e / np.sum(e, axis=-1, keepdims=True)
+            out[c0:c1, h, :] = p @ v[lo:hi, j, :]
+    return out
+
+
+def _attention_token(q_t: np.ndarray, k: np.ndarray, v: np.ndarray, window: int,
+                     softcap: float, p: int) -> np.ndarray:
+    """Rowwise attention of one query token at position p over keys at 0..p
+    (k, v hold exactly positions 0..p).  Same definition as attention_row."""
+    H, hd = q_t.shape
+    KV = k.shape[1]
+    G = H // KV
+    dt = q_t.dtype
+    lo = max(0, p - window + 1) if window > 0 else 0
+    scale = dt.type(1.0 / np.sqrt(hd))
+    out = np.empty((H, hd), dtype=dt)
+    for h in range(H):
+        j = h // G
+        s = (k[lo:p + 1, j, :] @ q_t[h]) * scale
+        if softcap:
+            cap = dt.type(softcap)
+            s = cap * np.tanh(s / cap)
+        e = np.exp(s - np.max(s))
+        out[h] = (e / np.sum(e)) @ v[lo:p + 1, j, :]
+    return out
+
+
+# --------------------------------------------------------------------------
+# State (the caller-owned KV cache)
+# --------------------------------------------------------------------------
+class OracleState:
+    """KV cache of the oracle block.
+
+    mojolearn ``TransformerState``: per (row, kv head) a buffer of ``capacity``
+    slots; without a window slot j holds position j and capacity is
+    ``max_tokens``; with a window W it is a ring of W slots, slot = p mod W.
+    Unlike the page's single ``cached_tokens``, each row carries its own
+    length.
+    """
+
+    def __init__(self, cfg: dict, batch: int, max_tokens: int, dtype=np.float32):
+        self.window = int(cfg.get("window", 0))
+        self.capacity = self.window if self.window > 0 else int(max_tokens)
+        self.max_tokens = int(max_tokens)
+        KV, hd = cfg["n_kv_heads"], cfg["head_dim"]
+        self.k = np.zeros((batch, KV, self.capacity, hd), dtype=dtype)
+        self.v = np.zeros((batch, KV, self.capacity, hd), dtype=dtype)
+        self.lengths = np.zeros(batch, dtype=np.int64)
+
+    @classmethod
+    def from_fill(cls, cfg, k_fill, v_fill, lengths, dtype=np.float32):
+        st = cls(cfg, k_fill.shape[0], k_fill.shape[2], dtype)
+        st.k[...] = k_fill
+        st.v[...] = v_fill
+        st.lengths[...] = lengths
+        return st
+
+    def slot(self, pos):
+        return pos % self.window if self.window > 0 else pos
+
+    def copy(self):
+        st = object.__new__(OracleState)
+        st.window, st.capacity, st.max_tokens = self.window, self.capacity, self.max_tokens
+        st.k, st.v, st.lengths = self.k.copy(), self.v.copy(), self.lengths.copy()
+        return st
+
+
+# --------------------------------------------------------------------------
+# The block
+# --------------------------------------------------------------------------
+def _linear(h, w, b=None):
+    y = h @ w.T
+    if b is not None:
+        y = y + b
+    return y
+
+
+def _project(cfg, W, x, dt, positions, layout):
+    """Steps up to RoPE: returns q [B,L,H,hd], k, v [B,L,KV,hd] (k, q rotated)."""
+    B, L, d = x.shape
+    H, KV, hd = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    offset = cfg.get("norm", "rmsnorm") == "rmsnorm_offset"
+    eps = cfg["norm_eps"]
+    w = {k: v.astype(dt) for k, v in W.items()}
+    h = rms_norm(x, w["input_layernorm.weight"], eps, offset)
+    if layout == "rowwise":
+        q = np.stack([np.stack([w["q_proj.weight"] @ h[b, t] for t in range(L)]) for b in range(B)])
+        k = np.stack([np.stack([w["k_proj.weight"] @ h[b, t] for t in range(L)]) for b in range(B)])
+        v = np.stack([np.stack([w["v_proj.weight"] @ h[b, t] for t in range(L)]) for b in range(B)])
+        if cfg.get("qkv_bias"):
+            q, k, v = q + w["q_proj.bias"], k + w["k_proj.bias"], v + w["v_proj.bias"]
+    else:
+        q = _linear(h, w["q_proj.weight"], w.get("q_proj.bias"))
+        k = _linear(h, w["k_proj.weight"], w.get("k_proj.bias"))
+        v = _linear(h, w["v_proj.weight"], w.get("v_proj.bias"))
+    q = q.reshape(B, L, H, hd)
+    k = k.reshape(B, L, KV, hd)
+    v = v.reshape(B, L, KV, hd)
+    if cfg.get("qk_norm"):
+        q = rms_norm(q, w["q_norm.weight"], eps, offset)
+        k = rms_norm(k, w["k_norm.weight"], eps, offset)
+    cos, sin = rope_cos_sin(positions, hd, cfg["rope_theta"])  # [B, L, hd/2]
+    q = apply_rope(q, cos[:, :, None, :], sin[:, :, None, :])
+    k = apply_rope(k, cos[:, :, None, :], sin[:, :, None, :])
+    return w, q, k, v
+
+
+def _mlp(cfg, w, x1, layout):
+    offset = cfg.get("norm", "rmsnorm") == "rmsnorm_offset"
+    h2 = rms_norm(x1, w["post_attention_layernorm.weight"], cfg["norm_eps"], offset)
+    act = gelu_tanh if cfg.get("mlp", "swiglu") == "geglu_tanh" else silu
+    if layout == "rowwise":
+        B, L, _ = x1.shape
+        out = np.empty_like(x1)
+        for b in range(B):
+            for t in range(L):
+                g = w["gate_proj.weight"] @ h2[b, t]
+                u = w["up_proj.weight"] @ h2[b, t]
+                out[b, t] = x1[b, t] + w["down_proj.weight"] @ (act(g) * u)
+        return out
+    m = act(h2 @ w["gate_proj.weight"].T) * (h2 @ w["up_proj.weight"].T)
+    return x1 + m @ w["down_proj.weight"].T
+
+
+def block_forward(cfg: dict, W: dict, x: np.ndarray, state: OracleState | None = None,
+                  *, dtype=np.float32, layout: str = "batched") -> np.ndarray:
+    """Run the block on x [B, L, d]; returns y [B, L, d] in ``dtype``.
+
+    mojolearn ``TransformerBlock.forward``: with ``state=None`` a
+    self-contained prefill from an empty cache; with a state, row b continues
+    at position state.lengths[b], the cache is read at entry and updated, and
+    the lengths advance by L.  Positions must stay below ``max_positions``
+    and, without a window, within the state's capacity (the page's errors
+    before any computation).
+    """
+    dt = np.dtype(dtype)
+    x = np.asarray(x).astype(dt)
+    B, L, d = x.shape
+    if d != cfg["d_model"]:
+        raise ValueError("x last dim must equal d_model")
+    H, KV, hd = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    window = int(cfg.get("window", 0))
+    start = np.zeros(B, dtype=np.int64) if state is None else state.lengths.astype(np.int64)
+    if state is not None:
+        if state.k.shape[0] != B:
+            raise ValueError("batch size differs from the state's")
+        if window == 0 and np.any(start + L > state.capacity):
+            raise ValueError("state capacity exceeded")
+        if np.any(start + L > state.max_tokens):
+            raise ValueError("state max_tokens exceeded")
+    if np.any(start + L > cfg["max_positions"]):
+        raise ValueError("position at or beyond max_positions")
+    positions = start[:, None] + np.arange(L)[None, :]            # [B, L]
+    w, q, k, v = _project(cfg, W, x, dt, positions, layout)
+
+    ctx = np.empty((B, L, H, hd), dtype=dt)
+    for b in range(B):
+        s0 = int(start[b])
+        # keys of this row: cached positions [lo, s0) then the call's own [s0, s0+L)
+        lo = max(0, s0 - window) if window > 0 else 0
+        if state is not None and s0 > lo:
+            cpos = np.arange(lo, s0)
+            slots = state.slot(cpos)
+            kc = np.transpose(state.k[b][:, slots, :], (1, 0, 2)).astype(dt)
+            vc = np.transpose(state.v[b][:, slots, :], (1, 0, 2)).astype(dt)
+            kall = np.concatenate([kc, k[b]], axis=0)
+            vall = np.concatenate([vc, v[b]], axis=0)
+            kpos = np.concatenate([cpos, positions[b]])
+        else:
+            kall, vall, kpos = k[b], v[b], positions[b]
+        if layout == "rowwise":
+            for t in range(L):
+                p = s0 + t
+                n = p + 1 - int(kpos[0])
+                ctx[b, t] = _attention_token(q[b, t], _pad_front(kall[:n], kpos[0]),
+                                             _pad_front(vall[:n], kpos[0]), window,
+                                             cfg.get("attn_softcap", 0.0), p)
+        else:
+            ctx[b] = attention_row(q[b], kall, vall, positions[b], kpos, window,
+                                   cfg.get("attn_softcap", 0.0))
+
+    if state is not None:
+        for b in range(B):
+            s0 = int(start[b])
+            first = max(s0, s0 + L - window) if window > 0 else s0
+            for p in range(first, s0 + L):
+                sl = state.slot(p)
+                state.k[b, :, sl, :] = k[b, p - s0]
+                state.v[b, :, sl, :] = v[b, p - s0]
+        state.lengths += L
+
+    ctx2 = ctx.reshape(B, L, H * hd)
+    if layout == "rowwise":
+        x1 = np.empty_like(x)
+        for b in range(B):
+            for t in range(L):
+                x1[b, t] = x[b, t] + w["o_proj.weight"] @ ctx2[b, t]
+    else:
+        x1 = x + ctx2 @ w["o_proj.weight"].T
+    return _mlp(cfg, w, x1, layout)
+
+
+def _pad_front(a: np.ndarray, first_pos: int) -> np.ndarray:
+    """Place keys that start at absolute position ``first_pos`` at index
+    first_pos of an array indexed by position (rows before it are unused)."""
+    first_pos = int(first_pos)
+    if first_pos == 0:
+        return a
+    pad = np.zeros((first_pos,) + a.shape[1:], dtype=a.dtype)
+    return np.concatenate([pad, a], axis=0)
+
+
+def block_step(cfg: dict, W: dict, x: np.ndarray, state: OracleState, **kw) -> np.ndarray:
+    """mojolearn ``TransformerBlock.step``: forward with L = 1 on a required state.
+    x may be (B, 1, d) or (B, d); returns (B, 1, d)."""
+    if state is None:
+        raise ValueError("step requires a state")
+    x = np.asarray(x)
+    if x.ndim == 2:
+        x = x[:, None, :]
+    return block_forward(cfg, W, x, state, **kw)
