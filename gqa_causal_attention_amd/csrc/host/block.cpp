@@ -1,0 +1,665 @@
+// Host runtime of the decoder-block library: the C ABI of include/gqa_block.h.
+//
+// It follows the mojolearn "mojolearn.transformer" API page (TransformerBlock,
+// allocate_state, forward, step, TransformerState): weights keyed by Hugging
+// Face names in [out, in] layout, a caller-owned KV cache, every argument
+// check made on the host before any device work is enqueued.  Per call it
+// only enqueues kernels on the caller's stream; nothing is allocated, nothing
+// synchronises.
+#include "../../../include/gqa_block.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdio>
+#include <cstdarg>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../kernels/launch.h"
+
+using namespace gqa;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                      \
+  do {                                                                                     \
+    hipError_t e_ = (expr);                                                                \
+    if (e_ != hipSuccess) return fail(GQA_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+enum WIdx {
+  W_IN_NORM, W_POST_NORM, W_Q, W_K, W_V, W_O, W_GATE, W_UP, W_DOWN,
+  W_QB, W_KB, W_VB, W_QN, W_KN, W_COUNT
+};
+const char* const kNames[W_COUNT] = {
+    "input_layernorm.weight", "post_attention_layernorm.weight", "q_proj.weight", "k_proj.weight",
+    "v_proj.weight", "o_proj.weight", "gate_proj.weight", "up_proj.weight", "down_proj.weight",
+    "q_proj.bias", "k_proj.bias", "v_proj.bias", "q_norm.weight", "k_norm.weight"};
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Per-kernel timing with HIP events on the caller's stream.
+struct KernelTimer {
+  struct Entry { std::string name; double ms = 0; int64_t count = 0; };
+  struct Pending { int entry; hipEvent_t a, b; };
+  bool enabled = false;
+  std::vector<Entry> entries;
+  std::vector<Pending> pending;
+  std::vector<hipEvent_t> pool;
+
+  int entry_of(const char* name) {
+    for (size_t i = 0; i < entries.size(); ++i)
+      if (entries[i].name == name) return (int)i;
+    entries.push_back({name, 0, 0});
+    return (int)entries.size() - 1;
+  }
+  hipEvent_t get() {
+    if (!pool.empty()) { hipEvent_t e = pool.back(); pool.pop_back(); return e; }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  void collect() {
+    for (auto& p : pending) {
+      float ms = 0.f;
+      hipEventSynchronize(p.b);
+      if (hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
+        entries[p.entry].ms += ms;
+        entries[p.entry].count += 1;
+      }
+      pool.push_back(p.a);
+      pool.push_back(p.b);
+    }
+    pending.clear();
+  }
+  ~KernelTimer() {
+    collect();
+    for (auto e : pool) hipEventDestroy(e);
+  }
+};
+
+struct Scope {
+  KernelTimer* t;
+  hipStream_t s;
+  int entry = -1;
+  hipEvent_t a = nullptr, b = nullptr;
+  Scope(KernelTimer* t_, const char* name, hipStream_t s_) : t(t_), s(s_) {
+    if (!t->enabled) return;
+    entry = t->entry_of(name);
+    a = t->get();
+    b = t->get();
+    if (a && b) hipEventRecord(a, s);
+  }
+  ~Scope() {
+    if (!t->enabled || !a || !b) return;
+    hipEventRecord(b, s);
+    t->pending.push_back({entry, a, b});
+  }
+};
+
+struct GemmPlan { int tile; int splits; };
+
+}  // namespace
+
+struct gqa_block {
+  gqa_block_config cfg;
+  const void* w[W_COUNT] = {};
+  int QW = 0, KW = 0, G = 0;
+  size_t es = 4;           // activation / weight element size
+  float* cos_tab = nullptr;
+  float* sin_tab = nullptr;
+  int* status = nullptr;   // device word: non-finite input seen
+  std::atomic<int> busy{0};
+  KernelTimer timer;
+};
+
+struct gqa_state {
+  const gqa_block* blk;
+  int batch, max_tokens, capacity;
+  void* k;
+  void* v;
+  int* lengths_dev;
+  std::vector<int> lengths;  // host mirror
+};
+
+namespace {
+
+bool is_bf16(const gqa_block* b) { return b->cfg.weight_dtype == GQA_BF16; }
+
+// Tile and K-split choice for a bf16 GEMM with M rows, N output columns
+// (N_b weight rows), K depth.  Large M: the wave tile count decides between
+// 256x256 and 256x192 (gfx950 has 256 CUs).  Small M (decode): 64x128 tiles,
+// K split until there are >= 2 workgroups per CU.
+GemmPlan plan_gemm(int M, int N, int K, bool gated) {
+  if (M > 128) {
+    if (M <= 512) return {kTile128x128, 1};
+    const int cols256 = gated ? 128 : 256;
+    const long t256 = (long)((M + 255) / 256) * ((N + cols256 - 1) / cols256);
+    if (!gated && N % 192 == 0) {
+      const long t192 = (long)((M + 255) / 256) * (N / 192);
+      auto eff = [](long t) { return (double)t / (double)(((t + 255) / 256) * 256); };
+      if (eff(t192) > eff(t256) + 0.05) return {kTile256x192, 1};
+    }
+    return {kTile256x256, 1};
+  }
+  const int cols = gated ? 64 : 128;
+  const long tiles = (long)((M + 63) / 64) * ((N + cols - 1) / cols);
+  int splits = 1;
+  while (tiles * splits < 512 && K / (splits * 2) >= 256 && (K / 64) % (splits * 2) == 0) splits *= 2;
+  return {kTile64x128, splits};
+}
+
+struct WsLayout {
+  size_t h, qkv, knew, vnew, ctx, x1, h2, act, part, attn_part, total;
+  int max_chunks;
+  GemmPlan p_qkv, p_o, p_gu, p_down;
+  bool decode_attn;
+};
+
+WsLayout layout_for(const gqa_block* blk, int B, int L) {
+  const auto& c = blk->cfg;
+  WsLayout w{};
+  const size_t T = (size_t)B * L, es = blk->es;
+  const int d = c.d_model, QW = blk->QW, KW = blk->KW, IT = c.intermediate;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+  w.h = take(T * d * es);
+  w.qkv = take(T * (QW + 2 * (size_t)KW) * es);
+  w.knew = take(T * KW * es);
+  w.vnew = take(T * KW * es);
+  w.ctx = take(T * QW * es);
+  w.x1 = take(T * d * 4);
+  w.h2 = take(T * d * es);
+  w.act = take(T * IT * es);
+  w.part = w.attn_part = 0;
+  w.max_chunks = 0;
+  w.decode_attn = false;
+  if (is_bf16(blk)) {
+    const int M = (int)T;
+    w.p_qkv = plan_gemm(M, QW + 2 * KW, d, false);
+    w.p_o = plan_gemm(M, d, QW, false);
+    w.p_gu = plan_gemm(M, IT, d, true);
+    w.p_down = plan_gemm(M, d, IT, false);
+    size_t part = 0;
+    auto need = [&](const GemmPlan& p, size_t nb) {
+      if (p.splits > 1) part = std::max(part, (size_t)p.splits * M * nb * 4);
+    };
+    need(w.p_qkv, QW + 2 * (size_t)KW);
+    need(w.p_o, d);
+    need(w.p_gu, 2 * (size_t)IT);
+    need(w.p_down, d);
+    if (part) w.part = take(part);
+    if (L == 1 && attention_decode_bf16_supported(c.head_dim, blk->G)) {
+      w.decode_attn = true;
+      const int span = c.window > 0 ? std::min(c.window, c.max_positions) : c.max_positions;
+      w.max_chunks = (span + attention_decode_chunk() - 1) / attention_decode_chunk();
+      w.attn_part = take((size_t)B * c.n_heads * w.max_chunks * (c.head_dim + 2) * 4);
+    }
+  }
+  w.total = off;
+  return w;
+}
+
+int check_config(const gqa_block_config* c) {
+  if (!c) return fail(GQA_ERR_ARG, "config is NULL");
+  if (c->d_model <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 || c->intermediate <= 0)
+    return fail(GQA_ERR_SHAPE, "d_model, n_heads, n_kv_heads, head_dim and intermediate must be positive");
+  if (c->n_heads % c->n_kv_heads != 0)
+    return fail(GQA_ERR_SHAPE, "n_heads (%d) must be a multiple of n_kv_heads (%d)", c->n_heads, c->n_kv_heads);
+  if (c->head_dim % 2 != 0) return fail(GQA_ERR_SHAPE, "head_dim (%d) must be even", c->head_dim);
+  if (c->head_dim > 256) return fail(GQA_ERR_UNSUPPORTED, "head_dim %d > 256 is not supported", c->head_dim);
+  if (c->window < 0) return fail(GQA_ERR_ARG, "window must be >= 0");
+  if (c->max_positions <= 0) return fail(GQA_ERR_ARG, "max_positions must be positive");
+  if (!(c->rope_theta > 0.f) || !std::isfinite(c->rope_theta)) return fail(GQA_ERR_ARG, "rope_theta must be > 0");
+  if (!(c->norm_eps >= 0.f) || !std::isfinite(c->norm_eps)) return fail(GQA_ERR_ARG, "norm_eps must be >= 0");
+  if (!(c->attn_softcap >= 0.f) || !std::isfinite(c->attn_softcap))
+    return fail(GQA_ERR_ARG, "attn_softcap must be >= 0 (0 = off)");
+  if (c->norm != GQA_NORM_RMS && c->norm != GQA_NORM_RMS_OFFSET) return fail(GQA_ERR_ARG, "unknown norm kind");
+  if (c->mlp != GQA_MLP_SWIGLU && c->mlp != GQA_MLP_GEGLU_TANH) return fail(GQA_ERR_ARG, "unknown mlp kind");
+  if ((c->qkv_bias != 0 && c->qkv_bias != 1) || (c->qk_norm != 0 && c->qk_norm != 1))
+    return fail(GQA_ERR_ARG, "qkv_bias and qk_norm must be 0 or 1");
+  if (c->weight_dtype != GQA_F32 && c->weight_dtype != GQA_BF16) return fail(GQA_ERR_DTYPE, "unknown weight dtype");
+  if (c->weight_dtype == GQA_BF16) {
+    const int QW = c->n_heads * c->head_dim;
+    if (c->d_model % 64 || QW % 64 || c->intermediate % 64)
+      return fail(GQA_ERR_UNSUPPORTED,
+                  "bf16 blocks need d_model, n_heads*head_dim and intermediate to be multiples of 64 "
+                  "(got %d, %d, %d)", c->d_model, QW, c->intermediate);
+    if (c->head_dim % 8) return fail(GQA_ERR_UNSUPPORTED, "bf16 blocks need head_dim %% 8 == 0");
+  }
+  return GQA_OK;
+}
+
+int check_weights(const gqa_block_config* c, const gqa_tensor* ws, int n, const void* out[W_COUNT]) {
+  if (n < 0 || (n > 0 && !ws)) return fail(GQA_ERR_ARG, "weights array is NULL");
+  const int64_t d = c->d_model, hd = c->head_dim, QW = (int64_t)c->n_heads * hd,
+                KW = (int64_t)c->n_kv_heads * hd, IT = c->intermediate;
+  const int64_t shapes[W_COUNT][2] = {{d, 0},  {d, 0},  {QW, d}, {KW, d}, {KW, d}, {d, QW}, {IT, d},
+                                      {IT, d}, {d, IT}, {QW, 0}, {KW, 0}, {KW, 0}, {hd, 0}, {hd, 0}};
+  bool wanted[W_COUNT];
+  for (int i = 0; i < W_COUNT; ++i) wanted[i] = i <= W_DOWN;
+  if (c->qkv_bias) wanted[W_QB] = wanted[W_KB] = wanted[W_VB] = true;
+  if (c->qk_norm) wanted[W_QN] = wanted[W_KN] = true;
+  for (int i = 0; i < W_COUNT; ++i) out[i] = nullptr;
+  for (int t = 0; t < n; ++t) {
+    const gqa_tensor& w = ws[t];
+    if (!w.name) return fail(GQA_ERR_ARG, "weight %d has no name", t);
+    int idx = -1;
+    for (int i = 0; i < W_COUNT; ++i)
+      if (!strcmp(w.name, kNames[i])) idx = i;
+    if (idx < 0 || !wanted[idx]) return fail(GQA_ERR_SHAPE, "unexpected weight '%s' for this configuration", w.name);
+    if (out[idx]) return fail(GQA_ERR_SHAPE, "weight '%s' given twice", w.name);
+    if (!w.data_dev) return fail(GQA_ERR_ARG, "weight '%s' has a NULL pointer", w.name);
+    const bool matrix = idx >= W_Q && idx <= W_DOWN;
+    const int nd = matrix ? 2 : 1;
+    if (w.ndim != nd || w.shape[0] != shapes[idx][0] || (nd == 2 && w.shape[1] != shapes[idx][1])) {
+      if (nd == 2)
+        return fail(GQA_ERR_SHAPE, "weight '%s' must have shape (%lld, %lld)", w.name, (long long)shapes[idx][0],
+                    (long long)shapes[idx][1]);
+      return fail(GQA_ERR_SHAPE, "weight '%s' must have shape (%lld,)", w.name, (long long)shapes[idx][0]);
+    }
+    const int want_dt = matrix ? c->weight_dtype : GQA_F32;
+    if (w.dtype != want_dt)
+      return fail(GQA_ERR_DTYPE, "weight '%s' must be %s", w.name, want_dt == GQA_BF16 ? "bfloat16" : "float32");
+    out[idx] = w.data_dev;
+  }
+  for (int i = 0; i < W_COUNT; ++i)
+    if (wanted[i] && !out[i]) return fail(GQA_ERR_SHAPE, "missing weight '%s'", kNames[i]);
+  return GQA_OK;
+}
+
+struct BusyGuard {
+  std::atomic<int>& f;
+  bool ok;
+  explicit BusyGuard(std::atomic<int>& f_) : f(f_) {
+    int z = 0;
+    ok = f.compare_exchange_strong(z, 1);
+  }
+  ~BusyGuard() {
+    if (ok) f.store(0);
+  }
+};
+
+int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, int L, void* ws, size_t wsb,
+              hipStream_t s) {
+  if (!blk) return fail(GQA_ERR_ARG, "block is NULL");
+  const auto& c = blk->cfg;
+  if (B < 0 || L < 0) return fail(GQA_ERR_ARG, "B and L must be >= 0");
+  if (st) {
+    if (st->blk != blk) return fail(GQA_ERR_STATE, "state belongs to another block");
+    if (B != st->batch) return fail(GQA_ERR_STATE, "batch size %d differs from the state's %d", B, st->batch);
+  }
+  if (B == 0 || L == 0) return GQA_OK;
+  if (!x || !y) return fail(GQA_ERR_ARG, "x or y is NULL");
+  for (int b = 0; b < B; ++b) {
+    const long start = st ? st->lengths[b] : 0;
+    if (st && start + L > st->max_tokens)
+      return fail(GQA_ERR_CAPACITY, "row %d: %ld cached + %d new tokens exceed the state's max_tokens %d", b, start, L,
+                  st->max_tokens);
+    if (start + L > c.max_positions)
+      return fail(GQA_ERR_POSITION, "row %d: position %ld is at or beyond max_positions %d", b, start + L - 1,
+                  c.max_positions);
+  }
+  const WsLayout lay = layout_for(blk, B, L);
+  if (!ws || wsb < lay.total)
+    return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? wsb : (size_t)0, lay.total);
+  BusyGuard guard(blk->busy);
+  if (!guard.ok) return fail(GQA_ERR_BUSY, "block is in use by another call");
+
+  char* base = static_cast<char*>(ws);
+  const int T = B * L, d = c.d_model, QW = blk->QW, KW = blk->KW, IT = c.intermediate, hd = c.head_dim;
+  const bool bf = is_bf16(blk);
+  const int et = bf ? kBF16 : kF32;
+  void* h = base + lay.h;
+  void* qkv = base + lay.qkv;
+  void* knew = base + lay.knew;
+  void* vnew = base + lay.vnew;
+  void* ctx = base + lay.ctx;
+  float* x1 = reinterpret_cast<float*>(base + lay.x1);
+  void* h2 = base + lay.h2;
+  void* act = base + lay.act;
+  float* part = lay.part ? reinterpret_cast<float*>(base + lay.part) : nullptr;
+  int* lengths = st ? st->lengths_dev : nullptr;
+  const int offset = c.norm == GQA_NORM_RMS_OFFSET;
+  KernelTimer* tm = &blk->timer;
+
+  // GEMM helper: fused epilogue, or K-split partials + ordered reduce.
+  auto gemm = [&](const char* name, GemmArgs a, int mode, int epi, const GemmPlan& p) -> int {
+    if (!bf) {
+      Scope sc(tm, name, s);
+      HIP_TRY(launch_gemm_f32(a, mode, epi, s));
+      return GQA_OK;
+    }
+    if (p.splits <= 1) {
+      a.splits = 1;
+      a.k_split = a.K;
+      Scope sc(tm, name, s);
+      HIP_TRY(launch_gemm_bf16(a, mode, epi, p.tile, s));
+      return GQA_OK;
+    }
+    GemmArgs pa = a;
+    pa.splits = p.splits;
+    pa.k_split = a.K / p.splits;
+    pa.partial = part;
+    pa.bump = nullptr;
+    {
+      Scope sc(tm, name, s);
+      HIP_TRY(launch_gemm_bf16(pa, mode, kEpiPartial, p.tile, s));
+    }
+    a.splits = p.splits;
+    a.partial = part;
+    {
+      std::string rn = std::string(name) + "_reduce";
+      Scope sc(tm, rn.c_str(), s);
+      HIP_TRY(launch_splitk_reduce(a, mode, epi, et, s));
+    }
+    return GQA_OK;
+  };
+
+  // 1. input RMSNorm (flags non-finite x)
+  {
+    Scope sc(tm, "rmsnorm", s);
+    HIP_TRY(launch_rmsnorm(x, static_cast<const float*>(blk->w[W_IN_NORM]), h, et, T, d, c.norm_eps, offset,
+                           blk->status, s));
+  }
+  // 2. q/k/v projections (+ bias) in one GEMM over three weight segments
+  {
+    GemmArgs a{};
+    a.A = h; a.lda = d;
+    a.B[0] = blk->w[W_Q]; a.B[1] = blk->w[W_K]; a.B[2] = blk->w[W_V];
+    a.seg_end[0] = QW; a.seg_end[1] = QW + KW; a.seg_end[2] = QW + 2 * KW;
+    a.bias[0] = static_cast<const float*>(blk->w[W_QB]);
+    a.bias[1] = static_cast<const float*>(blk->w[W_KB]);
+    a.bias[2] = static_cast<const float*>(blk->w[W_VB]);
+    a.M = T; a.N = QW + 2 * KW; a.K = d;
+    a.C = qkv; a.ldc = QW + 2 * KW;
+    if (int r = gemm("gemm_qkv", a, kModeSeg, kEpiStore, lay.p_qkv)) return r;
+  }
+  // 3. q/k norm + RoPE; keys/values of this call to knew/vnew and into the cache
+  // (a windowed call with L > 1 writes the ring after attention instead)
+  RopeArgs r{};
+  {
+    r.qkv = qkv; r.ld = QW + 2 * KW;
+    r.knew = knew; r.vnew = vnew;
+    r.kcache = st ? st->k : nullptr; r.vcache = st ? st->v : nullptr;
+    r.lengths = lengths;
+    r.cos_tab = blk->cos_tab; r.sin_tab = blk->sin_tab;
+    r.q_norm = static_cast<const float*>(blk->w[W_QN]);
+    r.k_norm = static_cast<const float*>(blk->w[W_KN]);
+    r.B = B; r.L = L; r.H = c.n_heads; r.KV = c.n_kv_heads; r.hd = hd;
+    r.cap = st ? st->capacity : 0; r.window = c.window; r.offset = offset; r.eps = c.norm_eps;
+    r.defer_append = st && c.window > 0 && L > 1;
+    Scope sc(tm, "rope_append", s);
+    HIP_TRY(launch_rope_append(r, et, s));
+  }
+  // 4. attention
+  {
+    AttnArgs a{};
+    a.q = qkv; a.ldq = QW + 2 * KW;
+    a.knew = knew; a.vnew = vnew;
+    a.kcache = st ? st->k : nullptr; a.vcache = st ? st->v : nullptr;
+    a.lengths = lengths; a.ctx = ctx;
+    a.B = B; a.L = L; a.H = c.n_heads; a.KV = c.n_kv_heads; a.hd = hd;
+    a.cap = st ? st->capacity : 0; a.window = c.window; a.softcap = c.attn_softcap;
+    if (bf && lay.decode_attn) {
+      a.part = reinterpret_cast<float*>(base + lay.attn_part);
+      a.max_chunks = lay.max_chunks;
+      a.chunk = attention_decode_chunk();
+      // launch only as many chunks as the longest row needs
+      int maxlen = 0;
+      for (int b = 0; b < B; ++b) maxlen = std::max(maxlen, st ? st->lengths[b] : 0);
+      const int lo = c.window > 0 ? std::max(0, maxlen - c.window + 1) : 0;
+      const int need = (maxlen - lo + 1 + a.chunk - 1) / a.chunk;
+      a.max_chunks = std::min(lay.max_chunks, need);
+      {
+        Scope sc(tm, "attn_decode", s);
+        HIP_TRY(launch_attention_decode_bf16(a, s));
+      }
+      Scope sc(tm, "attn_combine", s);
+      HIP_TRY(launch_attention_decode_combine(a, s));
+    } else if (bf && attention_prefill_bf16_supported(hd, blk->G)) {
+      Scope sc(tm, "attn_prefill", s);
+      HIP_TRY(launch_attention_prefill_bf16(a, s));
+    } else {
+      Scope sc(tm, "attn_generic", s);
+      HIP_TRY(launch_attention_generic(a, et, s));
+    }
+  }
+  if (r.defer_append) {
+    Scope sc(tm, "kv_append", s);
+    HIP_TRY(launch_kv_append(r, et, s));
+  }
+  // 5. o_proj + residual: x1 = x + ctx Wo^T (float32)
+  {
+    GemmArgs a{};
+    a.A = ctx; a.lda = QW;
+    a.B[0] = a.B[1] = a.B[2] = blk->w[W_O];
+    a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = d;
+    a.M = T; a.N = d; a.K = QW;
+    a.C = x1; a.ldc = d; a.resid = x; a.ldr = d;
+    if (int r = gemm("gemm_o", a, kModeSeg, kEpiResid, lay.p_o)) return r;
+  }
+  // 6. post-attention RMSNorm
+  {
+    Scope sc(tm, "rmsnorm", s);
+    HIP_TRY(launch_rmsnorm(x1, static_cast<const float*>(blk->w[W_POST_NORM]), h2, et, T, d, c.norm_eps, offset,
+                           nullptr, s));
+  }
+  // 7. gate/up + act(gate) * up
+  {
+    GemmArgs a{};
+    a.A = h2; a.lda = d;
+    a.B[0] = blk->w[W_GATE]; a.B[1] = blk->w[W_UP]; a.B[2] = nullptr;
+    a.M = T; a.N = IT; a.K = d;
+    a.C = act; a.ldc = IT;
+    a.act = c.mlp == GQA_MLP_GEGLU_TANH ? kActGeluTanh : kActSilu;
+    if (int r = gemm("gemm_gate_up", a, kModeGated, kEpiGated, lay.p_gu)) return r;
+  }
+  // 8. down + residual: y = x1 + act Wd^T; the last kernel also advances the lengths
+  {
+    GemmArgs a{};
+    a.A = act; a.lda = IT;
+    a.B[0] = a.B[1] = a.B[2] = blk->w[W_DOWN];
+    a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = d;
+    a.M = T; a.N = d; a.K = IT;
+    a.C = y; a.ldc = d; a.resid = x1; a.ldr = d;
+    if (st) { a.bump = lengths; a.bump_n = B; a.bump_by = L; }
+    if (int r = gemm("gemm_down", a, kModeSeg, kEpiResid, lay.p_down)) return r;
+  }
+  if (st)
+    for (int b = 0; b < B; ++b) st->lengths[b] += L;
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gqa_last_error(void) { return g_last_error.c_str(); }
+const char* gqa_version(void) { return "gqa_block 0.1 (gfx950)"; }
+
+int gqa_block_create(const gqa_block_config* cfg, const gqa_tensor* weights, int32_t n_weights, gqa_block** out) {
+  if (!out) return fail(GQA_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  if (int r = check_config(cfg)) return r;
+  const void* wp[W_COUNT];
+  if (int r = check_weights(cfg, weights, n_weights, wp)) return r;
+
+  gqa_block* blk = new gqa_block();
+  blk->cfg = *cfg;
+  for (int i = 0; i < W_COUNT; ++i) blk->w[i] = wp[i];
+  blk->QW = cfg->n_heads * cfg->head_dim;
+  blk->KW = cfg->n_kv_heads * cfg->head_dim;
+  blk->G = cfg->n_heads / cfg->n_kv_heads;
+  blk->es = cfg->weight_dtype == GQA_BF16 ? 2 : 4;
+
+  auto cleanup = [&](int code) {
+    gqa_block_destroy(blk);
+    return code;
+  };
+  // RoPE table: angle p * base^(-2i/hd) and its cos/sin in double, stored as float32.
+  const int half = cfg->head_dim / 2;
+  const size_t n = (size_t)cfg->max_positions * half;
+  std::vector<float> ct(n), sn(n);
+  std::vector<double> inv(half);
+  for (int i = 0; i < half; ++i) inv[i] = std::pow((double)cfg->rope_theta, -2.0 * i / cfg->head_dim);
+  for (int p = 0; p < cfg->max_positions; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double a = (double)p * inv[i];
+      ct[(size_t)p * half + i] = (float)std::cos(a);
+      sn[(size_t)p * half + i] = (float)std::sin(a);
+    }
+  hipError_t e;
+  if ((e = hipMalloc(&blk->cos_tab, n * 4)) != hipSuccess || (e = hipMalloc(&blk->sin_tab, n * 4)) != hipSuccess ||
+      (e = hipMalloc(&blk->status, 4)) != hipSuccess)
+    return cleanup(fail(GQA_ERR_HIP, "device allocation failed: %s", hipGetErrorString(e)));
+  if ((e = hipMemcpy(blk->cos_tab, ct.data(), n * 4, hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemcpy(blk->sin_tab, sn.data(), n * 4, hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemset(blk->status, 0, 4)) != hipSuccess)
+    return cleanup(fail(GQA_ERR_HIP, "device copy failed: %s", hipGetErrorString(e)));
+
+  // Non-finite weights are refused before any computation.
+  const int64_t d = cfg->d_model, hd = cfg->head_dim, QW = blk->QW, KW = blk->KW, IT = cfg->intermediate;
+  const int64_t counts[W_COUNT] = {d, d, QW * d, KW * d, KW * d, d * QW, IT * d, IT * d, d * IT, QW, KW, KW, hd, hd};
+  for (int i = 0; i < W_COUNT; ++i) {
+    if (!blk->w[i]) continue;
+    const bool matrix = i >= W_Q && i <= W_DOWN;
+    const int elem = matrix && cfg->weight_dtype == GQA_BF16 ? kBF16 : kF32;
+    if ((e = launch_count_nonfinite(blk->w[i], elem, counts[i], blk->status, nullptr)) != hipSuccess)
+      return cleanup(fail(GQA_ERR_HIP, "weight check launch failed: %s", hipGetErrorString(e)));
+  }
+  int flag = 0;
+  if ((e = hipMemcpy(&flag, blk->status, 4, hipMemcpyDeviceToHost)) != hipSuccess)
+    return cleanup(fail(GQA_ERR_HIP, "weight check failed: %s", hipGetErrorString(e)));
+  if (flag) return cleanup(fail(GQA_ERR_NONFINITE, "a weight holds a non-finite value"));
+  *out = blk;
+  return GQA_OK;
+}
+
+void gqa_block_destroy(gqa_block* blk) {
+  if (!blk) return;
+  blk->timer.collect();
+  if (blk->cos_tab) hipFree(blk->cos_tab);
+  if (blk->sin_tab) hipFree(blk->sin_tab);
+  if (blk->status) hipFree(blk->status);
+  delete blk;
+}
+
+int gqa_state_bytes(const gqa_block* blk, int32_t batch, int32_t max_tokens, size_t* bytes) {
+  if (!blk || !bytes) return fail(GQA_ERR_ARG, "block or output is NULL");
+  if (batch <= 0 || max_tokens <= 0) return fail(GQA_ERR_ARG, "batch and max_tokens must be positive");
+  const int cap = blk->cfg.window > 0 ? blk->cfg.window : max_tokens;
+  *bytes = (size_t)batch * blk->cfg.n_kv_heads * cap * blk->cfg.head_dim * blk->es;
+  return GQA_OK;
+}
+
+int gqa_block_allocate_state(const gqa_block* blk, int32_t batch, int32_t max_tokens, void* k, void* v,
+                             int32_t* lengths_dev, gqa_state** out) {
+  if (!out) return fail(GQA_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  if (!blk) return fail(GQA_ERR_ARG, "block is NULL");
+  if (batch <= 0 || max_tokens <= 0) return fail(GQA_ERR_ARG, "batch and max_tokens must be positive");
+  if (!k || !v || !lengths_dev) return fail(GQA_ERR_ARG, "state buffers must not be NULL");
+  gqa_state* st = new gqa_state();
+  st->blk = blk;
+  st->batch = batch;
+  st->max_tokens = max_tokens;
+  st->capacity = blk->cfg.window > 0 ? blk->cfg.window : max_tokens;
+  st->k = k;
+  st->v = v;
+  st->lengths_dev = lengths_dev;
+  st->lengths.assign(batch, 0);
+  *out = st;
+  return GQA_OK;
+}
+
+int gqa_state_set_lengths(gqa_state* st, const int32_t* lengths_host, void* stream) {
+  if (!st || !lengths_host) return fail(GQA_ERR_ARG, "state or lengths is NULL");
+  for (int b = 0; b < st->batch; ++b) {
+    if (lengths_host[b] < 0 || lengths_host[b] > st->max_tokens)
+      return fail(GQA_ERR_CAPACITY, "row %d: length %d outside [0, max_tokens=%d]", b, lengths_host[b], st->max_tokens);
+    if (lengths_host[b] > st->blk->cfg.max_positions)
+      return fail(GQA_ERR_POSITION, "row %d: length %d beyond max_positions", b, lengths_host[b]);
+  }
+  HIP_TRY(hipMemcpyAsync(st->lengths_dev, lengths_host, (size_t)st->batch * 4, hipMemcpyHostToDevice,
+                         static_cast<hipStream_t>(stream)));
+  st->lengths.assign(lengths_host, lengths_host + st->batch);
+  return GQA_OK;
+}
+
+int gqa_state_get_lengths(const gqa_state* st, int32_t* lengths_host) {
+  if (!st || !lengths_host) return fail(GQA_ERR_ARG, "state or lengths is NULL");
+  std::copy(st->lengths.begin(), st->lengths.end(), lengths_host);
+  return GQA_OK;
+}
+
+void gqa_state_free(gqa_state* st) { delete st; }
+
+int gqa_workspace_bytes(const gqa_block* blk, int32_t B, int32_t L, size_t* out) {
+  if (!blk || !out) return fail(GQA_ERR_ARG, "block or output is NULL");
+  if (B < 0 || L < 0) return fail(GQA_ERR_ARG, "B and L must be >= 0");
+  *out = (B == 0 || L == 0) ? 0 : layout_for(blk, B, L).total;
+  return GQA_OK;
+}
+
+int gqa_block_forward(gqa_block* blk, gqa_state* st, const float* x, float* y, int32_t B, int32_t L, void* ws,
+                      size_t wsb, void* stream) {
+  return run_block(blk, st, x, y, B, L, ws, wsb, static_cast<hipStream_t>(stream));
+}
+
+int gqa_block_step(gqa_block* blk, gqa_state* st, const float* x, float* y, int32_t B, void* ws, size_t wsb,
+                   void* stream) {
+  if (!st) return fail(GQA_ERR_STATE, "step requires a state");
+  return run_block(blk, st, x, y, B, 1, ws, wsb, static_cast<hipStream_t>(stream));
+}
+
+int gqa_block_status(gqa_block* blk, void* stream) {
+  if (!blk) return fail(GQA_ERR_ARG, "block is NULL");
+  HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+  int flag = 0;
+  HIP_TRY(hipMemcpy(&flag, blk->status, 4, hipMemcpyDeviceToHost));
+  if (flag) {
+    HIP_TRY(hipMemset(blk->status, 0, 4));
+    return fail(GQA_ERR_NONFINITE, "a non-finite input value was seen");
+  }
+  return GQA_OK;
+}
+
+int gqa_block_set_timing(gqa_block* blk, int32_t enable) {
+  if (!blk) return fail(GQA_ERR_ARG, "block is NULL");
+  blk->timer.collect();
+  blk->timer.enabled = enable != 0;
+  if (!enable) blk->timer.entries.clear();
+  return GQA_OK;
+}
+
+int gqa_block_kernel_times(gqa_block* blk, const char** names, double* total_ms, int64_t* counts, int32_t cap) {
+  if (!blk) return fail(GQA_ERR_ARG, "block is NULL");
+  blk->timer.collect();
+  const int n = (int)blk->timer.entries.size();
+  for (int i = 0; i < n && i < cap; ++i) {
+    if (names) names[i] = blk->timer.entries[i].name.c_str();
+    if (total_ms) total_ms[i] = blk->timer.entries[i].ms;
+    if (counts) counts[i] = blk->timer.entries[i].count;
+  }
+  return n;
+}
+
+}  // extern "C"

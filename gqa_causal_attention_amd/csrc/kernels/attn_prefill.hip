@@ -1,0 +1,340 @@
+// Flash-style grouped-query causal attention for bf16 activations on gfx950
+// matrix cores (prefill and chunked continuation).
+//
+// What is computed is the plain attention of the block (mojolearn
+// TransformerBlock; DantinoX "Core Layers" page, MHA and GQA / Flash
+// Attention): for query head h (kv head j = h / G) at position p, softmax over
+// keys [max(0, p - W + 1), p] of q.k / sqrt(hd) (optionally c * tanh(s / c)),
+// times the values.  The DantinoX page's flash path (exact attention without
+// an O(T^2) score matrix in HBM) is the idea kept; the kernel is written for
+// CDNA4:
+//
+//  * One workgroup per (row b, kv head j, block of BQ query positions); its
+//    waves cover all G query heads of the group, so every K/V tile staged in
+//    LDS is read from HBM once for the whole group.  Blocks are issued
+//    longest-first (the causal triangle's last query blocks first).
+//  * Transposed products: S^T = K Q^T and O^T += V^T P^T with
+//    v_mfma_f32_32x32x16_bf16.  Each lane then owns one query column, so the
+//    online-softmax statistics are per-lane scalars (one cross-half shuffle),
+//    and the P^T operand of the second product is the lane's own S^T
+//    accumulator converted to bf16 — no data movement — provided V^T's keys
+//    are stored in the same order, which the transposing LDS write arranges.
+//  * Q^T fragments live in registers for the whole key loop; K tiles are
+//    [key][hd] and V^T tiles [hd][key] in LDS, padded rows, double-buffered
+//    (global -> registers -> LDS, one barrier per tile).
+//  * Softmax in float32 (dew CausalTransformer force_fp32_for_softmax), base-2
+//    exponentials with the scale folded in; masks only on tiles that cross the
+//    diagonal or the window edge; tiles a wave cannot see are skipped.
+#include "common.h"
+#include "launch.h"
+
+namespace gqa {
+namespace {
+
+template <int HD>
+struct PrefillCfg {
+  static constexpr int QPW = HD <= 128 ? 64 : 32;   // query columns per wave
+  static constexpr int BKV = HD <= 128 ? 64 : 32;   // keys per LDS tile
+  static constexpr int CT = QPW / 32;               // 32-column tiles per wave
+  static constexpr int KS = HD / 16;                // 16-deep MFMA steps over hd
+  static constexpr int RT = HD / 32;                // 32-row tiles of O^T
+  static constexpr int KLD = HD + 8;                // K tile row (bf16)
+  static constexpr int VLD = BKV + 8;               // V^T tile row (bf16)
+  static constexpr int STAGE = BKV * KLD + HD * VLD;
+};
+
+__device__ __forceinline__ const bf16* kv_row(const AttnArgs& a, const void* fresh, const void* cache, int b, int j,
+                                             int start, int kp) {
+  if (kp >= start)
+    return static_cast<const bf16*>(fresh) + (((int64_t)b * a.KV + j) * a.L + (kp - start)) * a.hd;
+  const int slot = a.window > 0 ? kp % a.window : kp;
+  return static_cast<const bf16*>(cache) + (((int64_t)b * a.KV + j) * a.cap + slot) * a.hd;
+}
+
+// Logical key (within a 64/32-key tile) of physical V^T slot e of 8-key chunk g:
+// each 16-key group is stored as keys [0..3, 8..11, 4..7, 12..15].
+__device__ __forceinline__ int vt_key(int g, int e) {
+  return (g >> 1) * 16 + (e < 4 ? (g & 1) * 4 + e : 8 + (g & 1) * 4 + (e - 4));
+}
+
+template <int HD, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void attn_prefill_kernel(AttnArgs a, int nqb) {
+  using C = PrefillCfg<HD>;
+  constexpr int NT = NW * 64, QPW = C::QPW, BKV = C::BKV, CT = C::CT, KS = C::KS, RT = C::RT;
+  constexpr int KCH = (BKV * HD / 8 + NT - 1) / NT;    // 16-byte K chunks per thread
+  constexpr int VUN = (BKV * HD / 32 + NT - 1) / NT;   // (8 keys x 4 dims) V units per thread
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int G = a.H / a.KV;
+  const int wph = NW / G;          // waves per head
+  const int BQ = QPW * wph;        // query positions per workgroup
+
+  // longest query blocks first
+  const int bkv = a.B * a.KV;
+  const int qb = nqb - 1 - (int)(blockIdx.x / bkv);
+  const int bj = blockIdx.x % bkv;
+  const int b = bj / a.KV, j = bj % a.KV;
+  const int start = a.lengths ? a.lengths[b] : 0;
+  const int L = a.L, W = a.window;
+
+  const int q0 = qb * BQ;
+  const int hh = w / wph, sub = w % wph;
+  const int h = j * G + hh;
+  const int qt0 = q0 + sub * QPW;                    // first token of this wave
+  const int qp_lo = start + qt0;                     // its position
+  const int qp_hi = start + min(qt0 + QPW, L) - 1;   // last valid position of this wave
+
+  const int blk_lo = start + q0, blk_hi = start + min(q0 + BQ, L) - 1;
+  int klo = W > 0 ? max(0, blk_lo - W + 1) : 0;
+  klo = klo / BKV * BKV;
+  const int khi = blk_hi + 1;
+  const int ntiles = (khi - klo + BKV - 1) / BKV;
+
+  // ---- Q^T fragments: column = query token, 8 consecutive dims per lane ----
+  bf16x8 qf[CT][KS];
+  {
+    const bf16* qbase = static_cast<const bf16*>(a.q) + (int64_t)h * HD;
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      const int tok = min(qt0 + c * 32 + (lane & 31), L - 1);
+      const bf16* qr = qbase + ((int64_t)b * L + tok) * a.ldq + (lane >> 5) * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[c][ks] = *reinterpret_cast<const bf16x8*>(qr + ks * 16);
+    }
+  }
+
+  // ---- staging of one K/V tile ----
+  u32x4 kreg[KCH];
+  u32x2 vreg[VUN][8];
+  auto gload = [&](int t) {
+    const int kb = klo + t * BKV;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + i * NT;
+      if (c < BKV * HD / 8) {
+        const int r = c / (HD / 8), ch = c % (HD / 8);
+        const int kp = min(kb + r, khi - 1);
+        kreg[i] = *reinterpret_cast<const u32x4*>(kv_row(a, a.knew, a.kcache, b, j, start, kp) + ch * 8);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VUN; ++i) {
+      const int u = tid + i * NT;
+      if (u < BKV * HD / 32) {
+        const int g = u % (BKV / 8), dg = u / (BKV / 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int kp = min(kb + vt_key(g, e), khi - 1);
+          vreg[i][e] = *reinterpret_cast<const u32x2*>(kv_row(a, a.vnew, a.vcache, b, j, start, kp) + dg * 4);
+        }
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+    bf16* sK = smem + buf * C::STAGE;
+    bf16* sV = sK + BKV * C::KLD;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + i * NT;
+      if (c < BKV * HD / 8) {
+        const int r = c / (HD / 8), ch = c % (HD / 8);
+        *reinterpret_cast<u32x4*>(sK + r * C::KLD + ch * 8) = kreg[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VUN; ++i) {
+      const int u = tid + i * NT;
+      if (u < BKV * HD / 32) {
+        const int g = u % (BKV / 8), dg = u / (BKV / 8);
+        // vreg[i][e] holds dims 4dg..4dg+3 of key vt_key(g, e): transpose into 4 rows of V^T
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          u32x4 row;
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const uint32_t x0 = vreg[i][2 * e2][r / 2], x1 = vreg[i][2 * e2 + 1][r / 2];
+            const uint32_t h0 = (r & 1) ? (x0 >> 16) : (x0 & 0xffffu);
+            const uint32_t h1 = (r & 1) ? (x1 >> 16) : (x1 & 0xffffu);
+            row[e2] = h0 | (h1 << 16);
+          }
+          *reinterpret_cast<u32x4*>(sV + (dg * 4 + r) * C::VLD + g * 8) = row;
+        }
+      }
+    }
+  };
+
+  // ---- accumulators ----
+  f32x16 o[RT][CT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[r][c][e] = 0.f;
+  float m_run[CT], l_run[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) { m_run[c] = -INFINITY; l_run[c] = 0.f; }
+
+  const float scale = 1.0f / sqrtf((float)HD);
+  const float cap = a.softcap;
+  const float s_log2 = scale * kLog2e;          // no softcap: t = s * scale * log2e
+  const float cap_log2 = cap * kLog2e;           // softcap: t = cap * log2e * tanh(s * scale / cap)
+  const float inv_cap = cap > 0.f ? scale / cap : 0.f;
+
+  if (ntiles > 0) {
+    gload(0);
+    sstore(0);
+  }
+  __syncthreads();
+  const bool wave_valid = qt0 < L;
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) gload(t + 1);
+    const bf16* sK = smem + buf * C::STAGE;
+    const bf16* sV = sK + BKV * C::KLD;
+    const int kb = klo + t * BKV;
+#pragma unroll
+    for (int sb = 0; sb < BKV / 32; ++sb) {
+      const int k32 = kb + sb * 32;                       // first key of this 32-key sub-tile
+      const bool all_future = k32 > qp_hi;
+      const bool all_old = W > 0 && k32 + 31 < qp_lo - W + 1;
+      if (!wave_valid || all_future || all_old) continue;
+      const bool need_mask = (k32 + 31 > qp_lo) || (W > 0 && k32 < qp_hi - W + 1);
+
+      // S^T[32 keys][32 cols] per column tile
+      f32x16 s[CT];
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[c][e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + (sb * 32 + (lane & 31)) * C::KLD + ks * 16 +
+                                                          (lane >> 5) * 8);
+#pragma unroll
+        for (int c = 0; c < CT; ++c) s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c][ks], s[c], 0, 0, 0);
+      }
+
+      // online softmax per column (base 2)
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const int qp = start + qt0 + c * 32 + (lane & 31);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float v = cap > 0.f ? cap_log2 * tanh_exp(s[c][e] * inv_cap) : s[c][e] * s_log2;
+          if (need_mask) {
+            const int kp = k32 + (e / 4) * 8 + (lane >> 5) * 4 + (e % 4);
+            const bool ok = kp <= qp && (W == 0 || kp > qp - W);
+            v = ok ? v : -INFINITY;
+          }
+          s[c][e] = v;
+          mx = fmaxf(mx, v);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+        const float m_new = fmaxf(m_run[c], mx);
+        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = exp2_fast(m_run[c] - m_ref);
+        m_run[c] = m_new;
+        float ls = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = exp2_fast(s[c][e] - m_ref);
+          s[c][e] = p;
+          ls += p;
+        }
+        l_run[c] = l_run[c] * alpha + ls;
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[r][c][e] *= alpha;
+      }
+
+      // O^T += V^T P^T over the 32 keys (two 16-key steps)
+#pragma unroll
+      for (int k16 = 0; k16 < 2; ++k16) {
+        bf16x8 pf[CT];
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pf[c][e] = from_f32<bf16>(s[c][k16 * 8 + e]);
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(sV + (r * 32 + (lane & 31)) * C::VLD + sb * 32 +
+                                                            k16 * 16 + (lane >> 5) * 8);
+#pragma unroll
+          for (int c = 0; c < CT; ++c) o[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[c], o[r][c], 0, 0, 0);
+        }
+      }
+    }
+    if (t + 1 < ntiles) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- normalise and write ctx[token, h*HD + d] ----
+  if (!wave_valid) return;
+  bf16* ctx = static_cast<bf16*>(a.ctx);
+  const int64_t QW = (int64_t)a.H * HD;
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    const int tok = qt0 + c * 32 + (lane & 31);
+    const float lt = l_run[c] + __shfl_xor(l_run[c], 32, WAVE);
+    const float inv = 1.0f / lt;
+    if (tok >= L) continue;
+    bf16* out = ctx + ((int64_t)b * L + tok) * QW + (int64_t)h * HD;
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int d = r * 32 + e4 * 8 + (lane >> 5) * 4;
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = from_f32<bf16>(o[r][c][e4 * 4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(out + d) = v;
+      }
+  }
+}
+
+template <int HD, int NW>
+hipError_t launch_hd_nw(const AttnArgs& a, hipStream_t s) {
+  const int G = a.H / a.KV;
+  const int BQ = PrefillCfg<HD>::QPW * (NW / G);
+  const int nqb = (a.L + BQ - 1) / BQ;
+  dim3 grid((unsigned)(nqb * a.B * a.KV));
+  hipLaunchKernelGGL((attn_prefill_kernel<HD, NW>), grid, dim3(NW * 64), 0, s, a, nqb);
+  return hipGetLastError();
+}
+
+// Waves per workgroup for a group size: G query heads, ceil(4 / G) waves each.
+int waves_for(int G) { return G >= 4 ? G : G * ((4 + G - 1) / G); }
+
+template <int HD>
+hipError_t launch_hd(const AttnArgs& a, hipStream_t s) {
+  switch (waves_for(a.H / a.KV)) {
+    case 4: return launch_hd_nw<HD, 4>(a, s);
+    case 5: return launch_hd_nw<HD, 5>(a, s);
+    case 6: return launch_hd_nw<HD, 6>(a, s);
+    case 8: return launch_hd_nw<HD, 8>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool attention_prefill_bf16_supported(int hd, int G) {
+  const int nw = waves_for(G);
+  return (hd == 64 || hd == 128 || hd == 256) && (nw == 4 || nw == 5 || nw == 6 || nw == 8);
+}
+
+hipError_t launch_attention_prefill_bf16(const AttnArgs& a, hipStream_t s) {
+  if (a.B * a.L == 0) return hipSuccess;
+  switch (a.hd) {
+    case 64: return launch_hd<64>(a, s);
+    case 128: return launch_hd<128>(a, s);
+    case 256: return launch_hd<256>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gqa

@@ -1,0 +1,75 @@
+// Device helpers shared by the block's HIP kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define WAVE 64
+
+namespace gqa {
+
+// Storage conversions.  bf16 -> f32 is exact; f32 -> bf16 rounds to nearest
+// even (the hardware conversion on gfx950).
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return static_cast<float>(v); }
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return static_cast<bf16>(v); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// e^x through the hardware base-2 exponential: e^x = 2^(x log2 e).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr float kLog2e = 1.4426950408889634f;
+
+// tanh from its definition tanh(x) = 1 - 2 / (e^{2x} + 1); saturates to +-1
+// (e^{2x} -> inf gives 1, e^{2x} -> 0 gives -1).
+__device__ __forceinline__ float tanh_exp(float x) {
+  float e = exp2_fast(2.0f * kLog2e * x);
+  return 1.0f - 2.0f / (e + 1.0f);
+}
+
+// SiLU(z) = z / (1 + e^{-z}).
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + exp2_fast(-kLog2e * z)); }
+
+// GELU, tanh form: 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
+__device__ __forceinline__ float gelu_tanh(float z) {
+  const float c = 0.7978845608028654f;  // sqrt(2/pi)
+  float u = c * (z + 0.044715f * z * z * z);
+  return 0.5f * z * (1.0f + tanh_exp(u));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+
+// Sum over a workgroup of NT threads (NT a multiple of 64, <= 1024).
+template <int NT>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / WAVE, l = threadIdx.x % WAVE;
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < NT / WAVE; ++i) t += red[i];
+  __syncthreads();
+  return t;
+}
+
+}  // namespace gqa

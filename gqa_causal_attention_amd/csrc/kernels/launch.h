@@ -1,0 +1,101 @@
+// Host-side launchers of the block's kernels (C++ linkage, internal to the
+// library).  Every launcher enqueues on `stream` and returns hipSuccess or the
+// launch error; shapes are validated by the caller.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+enum ElemType { kF32 = 0, kBF16 = 1 };
+
+// B-operand row layouts of a "TN" GEMM  C[m, n] = sum_k A[m, k] * Brow(n)[k].
+enum GemmMode {
+  kModeSeg = 0,    // B rows come from up to 3 stacked [rows, K] matrices (q/k/v)
+  kModeGated = 1,  // gate/up pair: output column n reads gate row n and up row n
+};
+enum GemmEpi {
+  kEpiStore = 0,    // C = acc (+ bias), stored in the activation type
+  kEpiResid = 1,    // C (float32) = resid + acc
+  kEpiGated = 2,    // C = act(acc_gate) * acc_up, stored in the activation type
+  kEpiPartial = 3,  // float32 partial sums of one K split (split-K; raw B-row order)
+};
+enum ActKind { kActSilu = 0, kActGeluTanh = 1 };
+
+struct GemmArgs {
+  const void* A;           // [M, K] activations, row stride lda
+  int64_t lda;
+  const void* B[3];        // weight segments [rows_s, K] (row stride K)
+  int64_t seg_end[3];      // cumulative row ends of the segments (kModeSeg)
+  const float* bias[3];    // per-segment bias (may be null)
+  int M, N, K;             // N = output columns (kModeGated: IT)
+  void* C;                 // output, row stride ldc
+  int64_t ldc;
+  const float* resid;      // kEpiResid: [M, N] float32, row stride ldr
+  int64_t ldr;
+  int act;                 // ActKind for kEpiGated
+  float* partial;          // kEpiPartial: [splits, M, NB] float32, NB = B rows
+  int splits;              // number of K splits (grid z)
+  int k_split;             // K elements per split (multiple of 64)
+  int* bump;               // if non-null: bump[i] += bump_by for i < bump_n (once)
+  int bump_n, bump_by;
+};
+
+// Tile shapes of the bf16 MFMA GEMM.
+enum GemmTile { kTile256x256 = 0, kTile256x192 = 1, kTile64x128 = 2, kTile128x128 = 3 };
+
+hipError_t launch_gemm_bf16(const GemmArgs& a, int mode, int epi, int tile, hipStream_t s);
+hipError_t launch_gemm_f32(const GemmArgs& a, int mode, int epi, hipStream_t s);
+// Sum the K-split partials in split order, then apply `epi` (kEpiStore / kEpiResid /
+// kEpiGated) writing a.C; `out_type` is the element type of a.C for Store/Gated.
+hipError_t launch_splitk_reduce(const GemmArgs& a, int mode, int epi, int out_type, hipStream_t s);
+
+hipError_t launch_rmsnorm(const float* x, const float* w, void* out, int out_type, int rows, int d,
+                          float eps, int offset, int* nonfinite_flag, hipStream_t s);
+
+struct RopeArgs {
+  void* qkv;               // [T, ld] activations: q | k | v columns
+  int64_t ld;
+  void* knew;              // [B, KV, L, hd] post-RoPE keys of this call
+  void* vnew;              // [B, KV, L, hd] values of this call
+  void* kcache;            // [B, KV, cap, hd] or null
+  void* vcache;
+  const int* lengths;      // [B] start positions (null: zeros)
+  const float* cos_tab;    // [max_positions, hd/2]
+  const float* sin_tab;
+  const float* q_norm;     // [hd] or null
+  const float* k_norm;
+  int B, L, H, KV, hd, cap, window, offset;
+  int defer_append;        // 1: leave the cache to launch_kv_append (after attention)
+  float eps;
+};
+hipError_t launch_rope_append(const RopeArgs& a, int elem, hipStream_t s);
+hipError_t launch_kv_append(const RopeArgs& a, int elem, hipStream_t s);
+
+struct AttnArgs {
+  const void* q;           // [T, ldq] (query head h at column h*hd)
+  int64_t ldq;
+  const void* knew;        // [B, KV, L, hd]
+  const void* vnew;
+  const void* kcache;      // [B, KV, cap, hd] or null
+  const void* vcache;
+  const int* lengths;      // [B] start positions (null: zeros)
+  void* ctx;               // [T, H*hd]
+  int B, L, H, KV, hd, cap, window;
+  float softcap;           // 0 = off
+  float* part;             // decode split-K partials [B, H, max_chunks, hd + 2]
+  int chunk, max_chunks;
+};
+hipError_t launch_attention_generic(const AttnArgs& a, int elem, hipStream_t s);
+hipError_t launch_attention_prefill_bf16(const AttnArgs& a, hipStream_t s);
+bool attention_prefill_bf16_supported(int hd, int G);
+// Decode (L = 1): per-chunk partials into a.part, then the in-order combine into a.ctx.
+hipError_t launch_attention_decode_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention_decode_combine(const AttnArgs& a, hipStream_t s);
+bool attention_decode_bf16_supported(int hd, int G);
+int attention_decode_chunk();
+
+hipError_t launch_count_nonfinite(const void* p, int elem, int64_t n, int* flag, hipStream_t s);
+hipError_t launch_bump_lengths(int* lengths, int n, int by, hipStream_t s);
+
+}  // namespace gqa

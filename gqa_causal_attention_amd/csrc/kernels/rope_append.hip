@@ -1,0 +1,157 @@
+// Per-head q/k normalisation, RoPE and in-place KV-cache append.
+//
+// One wavefront per (token, head slot); head slots are the H query heads,
+// then the KV key heads, then the KV value heads of the q|k|v projection row.
+// For q and k: optional RMSNorm over head_dim (mojolearn ``qk_norm``: Qwen3
+// style, before RoPE), then RoPE (DantinoX "Core Layers" page, Positional
+// Encoding / RoPE: each pair rotated by p * theta_i, theta_i = base^(-2i/hd))
+// on Hugging Face's rotate-half pairs (i, i + hd/2), reading cos/sin from a
+// float32 table indexed by the absolute position p = lengths[b] + t.  Lane i
+// holds pairs i, i + 64, ... so a pair never crosses lanes.
+//
+// Outputs: q rotated in place; this call's keys (rotated) and values into
+// knew/vnew [B, KV, L, hd]; and, with a cache, the same keys/values into
+// slot p (full cache) or p mod W (sliding-window ring, mojolearn
+// TransformerState).  Under a window only the last W positions of the call
+// are stored, so the ring ends holding positions [start + L - W, start + L).
+// A windowed call with L > 1 defers the ring write (defer_append) to
+// kv_append, run after attention: its new positions reuse ring slots whose old
+// keys the call's earlier queries still read.
+#include "common.h"
+#include "launch.h"
+
+namespace gqa {
+namespace {
+
+template <typename T>
+__global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int slots = a.H + 2 * a.KV;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t T_ = (int64_t)a.B * a.L;
+  if (gw >= T_ * slots) return;
+  const int64_t tok = gw / slots;
+  const int slot = (int)(gw % slots);
+  const int b = (int)(tok / a.L), t = (int)(tok % a.L);
+  const int start = a.lengths ? a.lengths[b] : 0;
+  const int pos = start + t;
+  const int hd = a.hd, half = hd / 2;
+  const int QW = a.H * hd, KW = a.KV * hd;
+  T* row = static_cast<T*>(a.qkv) + tok * a.ld;
+
+  int kind, head;  // 0 = q, 1 = k, 2 = v
+  T* src;
+  if (slot < a.H) { kind = 0; head = slot; src = row + head * hd; }
+  else if (slot < a.H + a.KV) { kind = 1; head = slot - a.H; src = row + QW + head * hd; }
+  else { kind = 2; head = slot - a.H - a.KV; src = row + QW + KW + head * hd; }
+
+  const int64_t new_off = (((int64_t)b * a.KV + head) * a.L + t) * hd;
+  const bool to_cache = a.kcache && !a.defer_append && (a.window == 0 || t >= a.L - a.window);
+  const int cslot = a.window > 0 ? pos % a.window : pos;
+  const int64_t cache_off = (((int64_t)b * a.KV + head) * a.cap + cslot) * hd;
+
+  if (kind == 2) {
+    T* vn = static_cast<T*>(a.vnew) + new_off;
+    T* vc = static_cast<T*>(a.vcache) + cache_off;
+    for (int e = lane; e < hd; e += WAVE) {
+      const T v = src[e];
+      vn[e] = v;
+      if (to_cache) vc[e] = v;
+    }
+    return;
+  }
+
+  // q or k: load pairs (p, p + half) for p = lane, lane + 64, ...
+  constexpr int MAXP = 2;  // hd <= 256
+  float lo[MAXP], hi[MAXP];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXP; ++i) {
+    const int p = lane + i * WAVE;
+    lo[i] = hi[i] = 0.f;
+    if (p < half) {
+      lo[i] = to_f32(src[p]);
+      hi[i] = to_f32(src[p + half]);
+      ss += lo[i] * lo[i] + hi[i] * hi[i];
+    }
+  }
+  const float* nw = kind == 0 ? a.q_norm : a.k_norm;
+  float r = 1.f;
+  if (nw) r = 1.0f / sqrtf(wave_sum(ss) / (float)hd + a.eps);
+  const float* ct = a.cos_tab + (int64_t)pos * half;
+  const float* st = a.sin_tab + (int64_t)pos * half;
+  T* kn = kind == 1 ? static_cast<T*>(a.knew) + new_off : nullptr;
+  T* kc = (kind == 1 && to_cache) ? static_cast<T*>(a.kcache) + cache_off : nullptr;
+#pragma unroll
+  for (int i = 0; i < MAXP; ++i) {
+    const int p = lane + i * WAVE;
+    if (p >= half) continue;
+    float x1 = lo[i], x2 = hi[i];
+    if (nw) {
+      const float g1 = a.offset ? 1.0f + nw[p] : nw[p];
+      const float g2 = a.offset ? 1.0f + nw[p + half] : nw[p + half];
+      x1 = x1 * r * g1;
+      x2 = x2 * r * g2;
+    }
+    const float c = ct[p], s = st[p];
+    const T y1 = from_f32<T>(x1 * c - x2 * s);
+    const T y2 = from_f32<T>(x2 * c + x1 * s);
+    if (kind == 0) {
+      src[p] = y1;
+      src[p + half] = y2;
+    } else {
+      kn[p] = y1;
+      kn[p + half] = y2;
+      if (kc) {
+        kc[p] = y1;
+        kc[p + half] = y2;
+      }
+    }
+  }
+}
+
+// Ring write of the call's keys/values (the deferred form of the append):
+// one thread per element of the last min(L, W) positions of each (row, head).
+template <typename T>
+__global__ __launch_bounds__(256) void kv_append_kernel(RopeArgs a) {
+  const int keep = a.window > 0 ? min(a.L, a.window) : a.L;
+  const int64_t per = (int64_t)keep * a.hd;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)a.B * a.KV * per) return;
+  const int64_t bh = i / per;
+  const int b = (int)(bh / a.KV), head = (int)(bh % a.KV);
+  const int t = a.L - keep + (int)((i % per) / a.hd), e = (int)(i % a.hd);
+  const int pos = (a.lengths ? a.lengths[b] : 0) + t;
+  const int slot = a.window > 0 ? pos % a.window : pos;
+  const int64_t src = (((int64_t)b * a.KV + head) * a.L + t) * a.hd + e;
+  const int64_t dst = (((int64_t)b * a.KV + head) * a.cap + slot) * a.hd + e;
+  static_cast<T*>(a.kcache)[dst] = static_cast<const T*>(a.knew)[src];
+  static_cast<T*>(a.vcache)[dst] = static_cast<const T*>(a.vnew)[src];
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(const RopeArgs& a, int elem, hipStream_t s) {
+  const int keep = a.window > 0 ? (a.L < a.window ? a.L : a.window) : a.L;
+  const int64_t n = (int64_t)a.B * a.KV * keep * a.hd;
+  if (n == 0 || !a.kcache) return hipSuccess;
+  dim3 grid((unsigned)((n + 255) / 256));
+  if (elem == kBF16)
+    hipLaunchKernelGGL(kv_append_kernel<bf16>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(kv_append_kernel<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_append(const RopeArgs& a, int elem, hipStream_t s) {
+  const int64_t waves = (int64_t)a.B * a.L * (a.H + 2 * a.KV);
+  if (waves == 0) return hipSuccess;
+  dim3 grid((unsigned)((waves + 3) / 4));
+  if (elem == kBF16)
+    hipLaunchKernelGGL(rope_append_kernel<bf16>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(rope_append_kernel<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace gqa

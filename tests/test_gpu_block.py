@@ -1,0 +1,168 @@
+"""Parity of the HIP block against the CPU oracle on small shapes that still
+span several GEMM / attention tiles with ragged tails, every block option,
+carried state, chunked continuation and decode steps.
+
+Bar: max|gpu - oracle| / max|oracle| on y and on y - x, 1e-4 for float32
+blocks and 2e-2 for bf16-weight blocks (bf16 GEMM operands, activations and
+KV cache; float32 accumulation, softmax and residual stream)."""
+import numpy as np
+import pytest
+
+from gqa_causal_attention_amd.workloads import make_workload, random_block, round_bf16
+from tests.helpers import (OracleState, block_forward, block_step, check_close, fill_state_gpu,
+                           oracle_dtype, to_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _block(cfg, W):
+    from gqa_causal_attention_amd import Block
+    return Block(cfg, W)
+
+
+def test_tiny_llama_prefill_then_decode(torch_cuda):
+    """The tiny fp32 workload: prefill 16 tokens, then 8 single-token steps."""
+    wl = make_workload("tiny_llama_f32")
+    cfg, W, x, xs = wl["cfg"], wl["weights"], wl["x"], wl["x_steps"]
+    blk = _block(cfg, W)
+    st = blk.allocate_state(1, wl["capacity"])
+    ost = OracleState(cfg, 1, wl["capacity"], dtype=np.float64)
+    y = blk.forward(to_gpu(x), st).cpu().numpy()
+    yr = block_forward(cfg, W, x, ost, dtype=np.float64)
+    check_close(y, yr, x, "f32", "prefill")
+    for i in range(xs.shape[0]):
+        y = blk.step(to_gpu(xs[i]), st).cpu().numpy()
+        yr = block_step(cfg, W, xs[i], ost, dtype=np.float64)
+        check_close(y, yr, xs[i], "f32", f"step {i}")
+    np.testing.assert_array_equal(st.lengths.cpu().numpy(), [24])
+    np.testing.assert_array_equal(st.host_lengths(), [24])
+    # the cache holds post-RoPE keys and raw values at slot = position
+    np.testing.assert_allclose(st.k.cpu().numpy(), ost.k, rtol=1e-4, atol=1e-5)
+    np.testing.assert_allclose(st.v.cpu().numpy(), ost.v, rtol=1e-4, atol=1e-5)
+    # self-contained prefill (no state)
+    y0 = blk.forward(to_gpu(x)).cpu().numpy()
+    check_close(y0, block_forward(cfg, W, x, dtype=np.float64), x, "f32", "stateless")
+
+
+BF16_CASES = {
+    # name: (block overrides, B, prefill L, continuation L, decode steps)
+    "llama_g4_hd128": (dict(d_model=256, n_heads=8, n_kv_heads=2, head_dim=128, intermediate=512,
+                            rope_theta=5e5), 2, 150, 37, 3),
+    "hd64_g4": (dict(d_model=256, n_heads=8, n_kv_heads=2, head_dim=64, intermediate=320), 1, 200, 0, 2),
+    "gemma_window_softcap_hd256": (dict(d_model=256, n_heads=4, n_kv_heads=2, head_dim=256,
+                                        intermediate=384, window=64, attn_softcap=50.0,
+                                        mlp="geglu_tanh", norm="rmsnorm_offset"), 2, 150, 20, 3),
+    "qwen_bias_qknorm_g5": (dict(d_model=640, n_heads=10, n_kv_heads=2, head_dim=128,
+                                 intermediate=640, qkv_bias=True, qk_norm=True), 1, 130, 5, 2),
+    "mha_g1": (dict(d_model=256, n_heads=2, n_kv_heads=2, head_dim=128, intermediate=256), 1, 70, 0, 2),
+    "big_m_tiles": (dict(d_model=512, n_heads=4, n_kv_heads=1, head_dim=128, intermediate=768,
+                         rope_theta=5e5), 1, 1100, 0, 1),
+}
+
+
+@pytest.mark.parametrize("name", list(BF16_CASES))
+def test_bf16_block_variants(torch_cuda, name):
+    over, B, L0, L1, steps = BF16_CASES[name]
+    cfg, W = random_block(100 + list(BF16_CASES).index(name), dtype="bf16", **over)
+    rng = np.random.default_rng(7)
+    cap = L0 + L1 + steps
+    blk = _block(cfg, W)
+    st = blk.allocate_state(B, cap)
+    ost = OracleState(cfg, B, cap, dtype=np.float32)
+    x0 = rng.standard_normal((B, L0, cfg["d_model"]), dtype=np.float32)
+    check_close(blk.forward(to_gpu(x0), st).cpu().numpy(), block_forward(cfg, W, x0, ost), x0, "bf16",
+                f"{name} prefill")
+    if L1:
+        x1 = rng.standard_normal((B, L1, cfg["d_model"]), dtype=np.float32)
+        check_close(blk.forward(to_gpu(x1), st).cpu().numpy(), block_forward(cfg, W, x1, ost), x1, "bf16",
+                    f"{name} continuation")
+    for i in range(steps):
+        xt = rng.standard_normal((B, cfg["d_model"]), dtype=np.float32)
+        check_close(blk.step(to_gpu(xt), st).cpu().numpy(), block_step(cfg, W, xt, ost), xt, "bf16",
+                    f"{name} step {i}")
+    np.testing.assert_array_equal(st.lengths.cpu().numpy(), ost.lengths)
+
+
+def test_bf16_decode_ragged_rows_prefilled_cache(torch_cuda):
+    """Rows at different positions (one still empty), a cache pre-filled with
+    N(0, 1) keys/values, several chunks of the split-K decode per row."""
+    cfg, W = random_block(200, dtype="bf16", d_model=256, n_heads=8, n_kv_heads=2, head_dim=128,
+                          intermediate=256, max_positions=4096)
+    B, cap = 5, 2100
+    lengths = np.array([0, 1, 513, 2047, 700], dtype=np.int32)
+    rng = np.random.default_rng(8)
+    kf = round_bf16(rng.standard_normal((B, 2, cap, 128), dtype=np.float32))
+    vf = round_bf16(rng.standard_normal((B, 2, cap, 128), dtype=np.float32))
+    used = np.arange(cap)[None, None, :, None] < lengths[:, None, None, None]
+    kf, vf = np.where(used, kf, 0).astype(np.float32), np.where(used, vf, 0).astype(np.float32)
+    blk = _block(cfg, W)
+    st = blk.allocate_state(B, cap)
+    fill_state_gpu(st, kf, vf, lengths)
+    ost = OracleState.from_fill(cfg, kf, vf, lengths)
+    for i in range(3):
+        xt = rng.standard_normal((B, 1, 256), dtype=np.float32)
+        check_close(blk.step(to_gpu(xt), st).cpu().numpy(), block_step(cfg, W, xt, ost), xt, "bf16", f"step {i}")
+    np.testing.assert_array_equal(st.lengths.cpu().numpy(), lengths + 3)
+
+
+def test_bf16_window_ring_wraps(torch_cuda):
+    """Prefill longer than the window (in-call keys from the fresh K/V), then
+    decode steps through the ring's wrap-around."""
+    cfg, W = random_block(201, dtype="bf16", d_model=256, n_heads=4, n_kv_heads=2, head_dim=128,
+                          intermediate=256, window=48)
+    rng = np.random.default_rng(9)
+    blk = _block(cfg, W)
+    st = blk.allocate_state(2, 400)
+    ost = OracleState(cfg, 2, 400)
+    x = rng.standard_normal((2, 130, 256), dtype=np.float32)
+    check_close(blk.forward(to_gpu(x), st).cpu().numpy(), block_forward(cfg, W, x, ost), x, "bf16", "prefill")
+    for i in range(60):
+        xt = rng.standard_normal((2, 1, 256), dtype=np.float32)
+        y = blk.step(to_gpu(xt), st).cpu().numpy()
+        if i % 7 == 0 or i == 59:
+            check_close(y, block_step(cfg, W, xt, ost), xt, "bf16", f"step {i}")
+        else:
+            block_step(cfg, W, xt, ost)
+    got_k = st.k.float().cpu().numpy()
+    np.testing.assert_allclose(got_k, ost.k, rtol=2e-2, atol=2e-2 * np.abs(ost.k).max())
+
+
+F32_CASES = {
+    "window_softcap_geglu": (dict(window=7, attn_softcap=5.0, mlp="geglu_tanh", norm="rmsnorm_offset"),
+                             2, 19, 6, 10),
+    "bias_qknorm_g3": (dict(n_heads=6, n_kv_heads=2, head_dim=12, d_model=48, qkv_bias=True,
+                            qk_norm=True), 3, 9, 4, 3),
+    "odd_dims": (dict(d_model=50, n_heads=5, n_kv_heads=5, head_dim=10, intermediate=37), 1, 13, 0, 2),
+}
+
+
+@pytest.mark.parametrize("name", list(F32_CASES))
+def test_f32_block_variants(torch_cuda, name):
+    over, B, L0, L1, steps = F32_CASES[name]
+    cfg, W = random_block(300 + list(F32_CASES).index(name), **over)
+    rng = np.random.default_rng(10)
+    cap = L0 + L1 + steps
+    blk = _block(cfg, W)
+    st = blk.allocate_state(B, cap)
+    ost = OracleState(cfg, B, cap, dtype=np.float64)
+    d = cfg["d_model"]
+    x0 = rng.standard_normal((B, L0, d), dtype=np.float32)
+    check_close(blk.forward(to_gpu(x0), st).cpu().numpy(), block_forward(cfg, W, x0, ost, dtype=np.float64),
+                x0, "f32", f"{name} prefill")
+    if L1:
+        x1 = rng.standard_normal((B, L1, d), dtype=np.float32)
+        check_close(blk.forward(to_gpu(x1), st).cpu().numpy(), block_forward(cfg, W, x1, ost, dtype=np.float64),
+                    x1, "f32", f"{name} continuation")
+    for i in range(steps):
+        xt = rng.standard_normal((B, d), dtype=np.float32)
+        check_close(blk.step(to_gpu(xt), st).cpu().numpy(), block_step(cfg, W, xt, ost, dtype=np.float64),
+                    xt, "f32", f"{name} step {i}")
+    np.testing.assert_allclose(st.k.cpu().numpy(), ost.k, rtol=1e-4, atol=1e-4 * np.abs(ost.k).max())
