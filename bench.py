@@ -1,0 +1,245 @@
+"""Benchmark of the decoder block on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+
+A step is one pass of the whole block over one batch of seeded synthetic
+input (random-init weights, no checkpoints):
+
+  * headline: Llama-3-8B-shaped block prefill, B=1, L=4096, bf16 weights /
+    float32 accumulation (a self-contained prefill, mojolearn forward with no
+    state): whole-block tokens/s and the share of the bf16 MFMA peak;
+  * decode: the same block shape, 64 rows one token each, KV cache of 8192
+    slots pre-filled to per-row positions drawn from [1024, 8192): step time
+    and achieved HBM bandwidth.
+
+Inputs are resident in HBM before timing starts.  The timed region is K
+steps bracketed by device synchronisation; per-kernel durations come from
+HIP events recorded around each launch on the launch stream during the same
+region.  Prints ONE JSON line on stdout; details go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block prefill tokens/s (%MFMA peak) + decode step µs (%HBM BW), 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_flops(cfg, B, L):
+    """Algorithmic flops of one block prefill: GEMMs plus unmasked attention pairs."""
+    d, H, KV, hd, IT = cfg["d_model"], cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["intermediate"]
+    QW, KW = H * hd, KV * hd
+    T = B * L
+    gemm = 2 * T * (d * (QW + 2 * KW) + QW * d + 3 * d * IT)
+    W = cfg.get("window", 0)
+    pairs = 0
+    for t in range(L):
+        pairs += min(t + 1, W) if W else t + 1
+    attn = 4 * H * hd * B * pairs
+    return gemm, attn
+
+
+def decode_bytes(cfg, lengths, elem=2):
+    d, KV, hd, IT, H = cfg["d_model"], cfg["n_kv_heads"], cfg["head_dim"], cfg["intermediate"], cfg["n_heads"]
+    QW, KW = H * hd, KV * hd
+    B = len(lengths)
+    weights = (d * (QW + 2 * KW) + QW * d + 3 * d * IT) * elem
+    W = cfg.get("window", 0)
+    keys = sum(min(int(p) + 1, W) if W else int(p) + 1 for p in lengths)
+    kv_read = keys * KV * hd * 2 * elem          # every attended key and value once (incl. the new one)
+    append = B * KV * hd * 2 * elem
+    io = 2 * B * d * 4
+    return weights, kv_read, append, io
+
+
+def bench_prefill(args, torch):
+    from gqa_causal_attention_amd import Block
+    from gqa_causal_attention_amd.workloads import make_workload
+    t0 = time.time()
+    wl = make_workload("llama3_8b_prefill_4k")
+    cfg, B, L = wl["cfg"], wl["batch"], wl["seq_len"]
+    blk = Block(cfg, wl["weights"])
+    x = torch.from_numpy(wl["x"]).cuda()
+    y = torch.empty_like(x)
+    log(f"[prefill] inputs ready in {time.time() - t0:.1f}s")
+    for _ in range(args.warmup):
+        blk.forward(x, out=y)
+    torch.cuda.synchronize()
+    blk.set_timing(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        blk.forward(x, out=y)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t1
+    times = blk.kernel_times()
+    blk.set_timing(False)
+    ms = el * 1e3 / args.steps
+    gemm_f, attn_f = prefill_flops(cfg, B, L)
+    d, IT = cfg["d_model"], cfg["intermediate"]
+    T = B * L
+    per_kernel_flops = {
+        "gemm_qkv": 2 * T * d * (cfg["n_heads"] + 2 * cfg["n_kv_heads"]) * cfg["head_dim"],
+        "gemm_o": 2 * T * cfg["n_heads"] * cfg["head_dim"] * d,
+        "gemm_gate_up": 2 * T * d * 2 * IT,
+        "gemm_down": 2 * T * IT * d,
+        "attn_prefill": attn_f,
+    }
+    breakdown = {}
+    for name, (tot, cnt) in times.items():
+        avg = tot / max(cnt, 1)
+        f = per_kernel_flops.get(name)
+        breakdown[name] = {"avg_ms": round(avg, 4), "launches": cnt,
+                           "tflops": round(f / (avg * 1e-3) / 1e12, 1) if f else None}
+    log("[prefill] per-kernel (HIP events over the timed region):")
+    for k, v in breakdown.items():
+        log(f"   {k:16s} {v}")
+    gu = breakdown["gemm_gate_up"]
+    achieved = per_kernel_flops["gemm_gate_up"] / (gu["avg_ms"] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "gemm_gate_up", "achieved": round(achieved, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None,
+                "flops_per_launch": per_kernel_flops["gemm_gate_up"]}
+    total_f = gemm_f + attn_f
+    step_tflops = total_f / (ms * 1e-3) / 1e12
+    return dict(cfg=cfg, B=B, L=L, ms=ms, tokens_per_s=T / (ms * 1e-3), roofline=roofline,
+                step={"tflops": round(step_tflops, 1), "frac_of_peak": round(step_tflops / PEAK_BF16_TFLOPS, 4),
+                      "algorithmic_tflop": round(total_f / 1e12, 4)},
+                breakdown=breakdown, wl=wl)
+
+
+def bench_decode(args, torch):
+    from gqa_causal_attention_amd import Block
+    from gqa_causal_attention_amd.workloads import make_workload
+    t0 = time.time()
+    wl = make_workload("llama3_8b_decode_b64")
+    cfg, B, cap = wl["cfg"], wl["batch"], wl["capacity"]
+    lengths = wl["lengths"]
+    blk = Block(cfg, wl["weights"])
+    st = blk.allocate_state(B, cap)
+    st.k.copy_(torch.from_numpy(wl.pop("k_fill")).cuda().to(torch.bfloat16))
+    st.v.copy_(torch.from_numpy(wl.pop("v_fill")).cuda().to(torch.bfloat16))
+    x = torch.from_numpy(wl["x"]).cuda()
+    y = torch.empty_like(x)
+    log(f"[decode] inputs ready in {time.time() - t0:.1f}s")
+    for _ in range(args.warmup):
+        st.set_lengths(lengths)
+        blk.step(x, st, out=y)
+    torch.cuda.synchronize()
+    blk.set_timing(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        st.set_lengths(lengths)       # every step decodes at the same positions
+        blk.step(x, st, out=y)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t1
+    times = blk.kernel_times()
+    blk.set_timing(False)
+    us = el * 1e6 / args.steps
+    wb, kvb, apb, iob = decode_bytes(cfg, lengths)
+    total = wb + kvb + apb + iob
+    breakdown = {k: {"avg_us": round(t / max(c, 1) * 1e3, 2), "launches": c} for k, (t, c) in times.items()}
+    log("[decode] per-kernel (HIP events over the timed region):")
+    for k, v in breakdown.items():
+        log(f"   {k:22s} {v}")
+    att = breakdown.get("attn_decode")
+    kv_bytes_launch = kvb
+    achieved = kv_bytes_launch / (att["avg_us"] * 1e-6) / 1e9 if att else None
+    roofline = {"bound": "hbm", "kernel": "attn_decode", "achieved": round(achieved, 1) if achieved else None,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4) if achieved else None, "traffic": None,
+                "bytes_per_launch": kv_bytes_launch}
+    gbs = total / (us * 1e-6) / 1e9
+    return dict(us=us, tokens_per_s=B / (us * 1e-6), bytes=total, gbs=gbs, frac=gbs / PEAK_HBM_GBS,
+                roofline=roofline, breakdown=breakdown, B=B)
+
+
+def cpu_baseline(pre, budget_s=20.0):
+    """The CPU oracle (float32 numpy, as it stands) on the first 512 positions of
+    the same prefill workload (a causal prefix: those rows' outputs are exactly
+    the full run's), repeated until ~budget_s of work; reported in tokens/s."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import block_forward
+    wl = pre["wl"]
+    cfg, W, x = wl["cfg"], wl["weights"], wl["x"][:, :512]
+    n, t0 = 0, time.perf_counter()
+    while True:
+        block_forward(cfg, W, x)
+        n += 1
+        if time.perf_counter() - t0 > budget_s or n >= 20:
+            break
+    el = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": round(n * x.shape[1] / el, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} x prefill of the first 512 of 4096 positions (causal prefix), float32 numpy, "
+                      f"{el:.1f}s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the block runs on a single device); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    pre = bench_prefill(args, torch)
+    dec = None if args.no_decode else bench_decode(args, torch)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(pre)
+        log(f"[cpu] {cpu}")
+    out = {
+        "metric": METRIC,
+        "value": round(pre["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama3-8b-shaped block prefill (d=4096, 32/8 heads, hd=128, IT=14336)",
+                   "batch": pre["B"], "seq_len": pre["L"], "parallelism": "none"},
+        "prefill_mfma": pre["step"],
+        "roofline": pre["roofline"],
+        "cpu_baseline": cpu,
+    }
+    if dec:
+        out["decode"] = {"workload": "llama3-8b-shaped block decode, 64 rows, cache 8192, positions U[1024, 8192)",
+                         "step_us": round(dec["us"], 2), "tokens_per_s": round(dec["tokens_per_s"], 1),
+                         "algorithmic_bytes": dec["bytes"], "achieved_gbs": round(dec["gbs"], 1),
+                         "frac_of_hbm_peak": round(dec["frac"], 4), "roofline": dec["roofline"]}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -137,6 +137,17 @@ struct gqa_state {
   void* v;
   int* lengths_dev;
   std::vector<int> lengths;  // host mirror
+  // Pinned staging ring for gqa_state_set_lengths: the copy is asynchronous,
+  // and a slot is reused only after its previous copy has completed.
+  static constexpr int kRing = 4;
+  int* staging = nullptr;    // kRing * batch ints (pinned host memory)
+  hipEvent_t done[kRing] = {};
+  int next = 0;
+  ~gqa_state() {
+    for (auto& e : done)
+      if (e) hipEventDestroy(e);
+    if (staging) hipHostFree(staging);
+  }
 };
 
 namespace {
@@ -586,6 +597,20 @@ int gqa_block_allocate_state(const gqa_block* blk, int32_t batch, int32_t max_to
   st->v = v;
   st->lengths_dev = lengths_dev;
   st->lengths.assign(batch, 0);
+  hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&st->staging), (size_t)gqa_state::kRing * batch * 4,
+                               hipHostMallocDefault);
+  if (e != hipSuccess) {
+    st->staging = nullptr;
+    delete st;
+    return fail(GQA_ERR_HIP, "pinned staging allocation failed: %s", hipGetErrorString(e));
+  }
+  for (auto& ev : st->done) {
+    if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) {
+      ev = nullptr;
+      delete st;
+      return fail(GQA_ERR_HIP, "event creation failed: %s", hipGetErrorString(e));
+    }
+  }
   *out = st;
   return GQA_OK;
 }
@@ -598,8 +623,14 @@ int gqa_state_set_lengths(gqa_state* st, const int32_t* lengths_host, void* stre
     if (lengths_host[b] > st->blk->cfg.max_positions)
       return fail(GQA_ERR_POSITION, "row %d: length %d beyond max_positions", b, lengths_host[b]);
   }
-  HIP_TRY(hipMemcpyAsync(st->lengths_dev, lengths_host, (size_t)st->batch * 4, hipMemcpyHostToDevice,
+  const int slot = st->next;
+  st->next = (st->next + 1) % gqa_state::kRing;
+  HIP_TRY(hipEventSynchronize(st->done[slot]));  // the slot's previous copy has finished
+  int* stage = st->staging + (size_t)slot * st->batch;
+  std::copy(lengths_host, lengths_host + st->batch, stage);
+  HIP_TRY(hipMemcpyAsync(st->lengths_dev, stage, (size_t)st->batch * 4, hipMemcpyHostToDevice,
                          static_cast<hipStream_t>(stream)));
+  HIP_TRY(hipEventRecord(st->done[slot], static_cast<hipStream_t>(stream)));
   st->lengths.assign(lengths_host, lengths_host + st->batch);
   return GQA_OK;
 }

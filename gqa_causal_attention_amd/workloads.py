@@ -97,10 +97,10 @@ def round_bf16(a: np.ndarray) -> np.ndarray:
     Non-finite inputs are not expected here (all draws are finite normals).
     """
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16) << 16
-    return r.astype(np.uint32).view(np.float32)
+    u = a.view(np.uint32)
+    # finite values: u + 0x8000 never wraps a uint32
+    r = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
 
 
 def _is_norm_weight(name: str) -> bool:

@@ -121,16 +121,18 @@ int gqa_state_bytes(const gqa_block* blk, int32_t batch, int32_t max_tokens, siz
  * (slot = position, or position mod window), and lengths_dev: int32[batch],
  * the number of positions each row holds.  The buffers are BORROWED; this call
  * enqueues nothing and does not clear them (a new sequence needs lengths = 0,
- * see gqa_state_set_lengths).  The cache holds post-RoPE keys and raw values.
+ * see gqa_state_set_lengths).  It allocates a small pinned host staging buffer
+ * for gqa_state_set_lengths, freed by gqa_state_free.  The cache holds post-RoPE keys and raw values.
  * Departure from the page: one length per row instead of one cached_tokens. */
 int gqa_block_allocate_state(const gqa_block* blk, int32_t batch, int32_t max_tokens,
                              void* k_cache_dev, void* v_cache_dev, int32_t* lengths_dev,
                              gqa_state** out);
 
-/* Set every row's length (host values, copied to lengths_dev on `stream`,
- * also kept as the host mirror the argument checks use).  Used to start a
- * sequence (zeros) or to resume a pre-filled cache.  Errors: ARG, CAPACITY,
- * POSITION, HIP. */
+/* Set every row's length (host values, copied to lengths_dev on `stream`
+ * through a pinned staging buffer, so the call does not wait for the GPU; the
+ * values are also kept as the host mirror the argument checks use).  Used to
+ * start a sequence (zeros) or to resume a pre-filled cache.  Errors: ARG,
+ * CAPACITY, POSITION, HIP. */
 int gqa_state_set_lengths(gqa_state* st, const int32_t* lengths_host, void* hip_stream);
 /* Copy the host mirror of the lengths into lengths_host[batch]. */
 int gqa_state_get_lengths(const gqa_state* st, int32_t* lengths_host);
