@@ -15,6 +15,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstdarg>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -158,6 +159,14 @@ bool is_bf16(const gqa_block* b) { return b->cfg.weight_dtype == GQA_BF16; }
 // (N_b weight rows), K depth.  Large M: the wave tile count decides between
 // 256x256 and 256x192 (gfx950 has 256 CUs).  Small M (decode): 64x128 tiles,
 // K split until there are >= 2 workgroups per CU.
+int big_tile() {
+  static int t = [] {
+    const char* e = getenv("GQA_GEMM_BIG_TILE");  // tuning override: 0 = 8 waves, 4 = 4 waves
+    return e ? atoi(e) : (int)kTile256x256;
+  }();
+  return t;
+}
+
 GemmPlan plan_gemm(int M, int N, int K, bool gated) {
   if (M > 128) {
     if (M <= 512) return {kTile128x128, 1};
@@ -168,7 +177,7 @@ GemmPlan plan_gemm(int M, int N, int K, bool gated) {
       auto eff = [](long t) { return (double)t / (double)(((t + 255) / 256) * 256); };
       if (eff(t192) > eff(t256) + 0.05) return {kTile256x192, 1};
     }
-    return {kTile256x256, 1};
+    return {big_tile(), 1};
   }
   const int cols = gated ? 64 : 128;
   const long tiles = (long)((M + 63) / 64) * ((N + cols - 1) / cols);

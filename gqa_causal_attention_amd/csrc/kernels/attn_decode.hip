@@ -34,6 +34,17 @@ __device__ __forceinline__ const bf16* dec_row(const AttnArgs& a, const void* fr
   return static_cast<const bf16*>(cache) + (((int64_t)b * a.KV + j) * a.cap + slot) * a.hd;
 }
 
+// Sum over aligned groups of N lanes (N = 8, 16 or 32) with DPP row moves.
+template <int N>
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);  // row_half_mirror: the other quad of the 8
+  if (N >= 16) x += dpp<0x140>(x);  // row_mirror: the other 8 of the 16
+  if (N >= 32) x += __shfl_xor(x, 16, WAVE);
+  return x;
+}
+
 template <int HD, int G>
 __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs a) {
   constexpr int LPR = HD / 8;           // lanes per key row (8 bf16 each)
@@ -98,8 +109,7 @@ __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs a) {
         float s = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) s = fmaf(qv[g][e], kf[e], s);
-#pragma unroll
-        for (int o = LPR / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o, WAVE);
+        s = row_sum<LPR>(s);
         s *= scale;
         if (cap > 0.f) s = cap * tanh_exp(s / cap);
         if (rl == g % LPR) sc[g][kl] = kl < kcnt ? s : -INFINITY;

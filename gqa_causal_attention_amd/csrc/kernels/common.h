@@ -58,6 +58,27 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Value of lane (l ^ 32): the gfx950 swap of the upper half of one register
+// with the lower half of another (v_permlane32_swap), no LDS round trip.
+__device__ __forceinline__ float xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// All-reduce sum over each row of 16 lanes with DPP moves (no LDS):
+// quad_perm [1,0,3,2] and [2,3,0,1], then row_half_mirror and row_mirror.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  x += dpp<0x140>(x);
+  return x;
+}
+
 // Sum over a workgroup of NT threads (NT a multiple of 64, <= 1024).
 template <int NT>
 __device__ __forceinline__ float block_sum(float v, float* red) {

@@ -17,6 +17,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <cstdlib>
+
 namespace gqa {
 namespace {
 
@@ -28,13 +30,15 @@ __device__ __forceinline__ int seg_of(const GemmArgs& a, int64_t n) {
 }
 
 // Pointer to the start of B-tile row r (global K offset k0) for tile column tn.
-template <int MODE, int BN>
+// Gated mode: each wave's WTN B rows are WTN/2 gate rows then the WTN/2 up
+// rows of the same output columns, so one lane holds both accumulators.
+template <int MODE, int BN, int WTN>
 __device__ __forceinline__ const bf16* b_row(const GemmArgs& a, int tn, int r, int k0) {
   if (MODE == kModeGated) {
-    const int blk = r / 64, w = r % 64;
-    int col = tn * (BN / 2) + blk * 32 + (w % 32);
+    const int blk = r / WTN, w = r % WTN;
+    int col = tn * (BN / 2) + blk * (WTN / 2) + (w % (WTN / 2));
     col = min(col, a.N - 1);
-    const bf16* base = static_cast<const bf16*>(w < 32 ? a.B[0] : a.B[1]);
+    const bf16* base = static_cast<const bf16*>(w < WTN / 2 ? a.B[0] : a.B[1]);
     return base + (int64_t)col * a.K + k0;
   } else {
     int64_t n = min((int64_t)tn * BN + r, (int64_t)a.N - 1);
@@ -48,7 +52,7 @@ __device__ __forceinline__ float apply_act(int act, float g) {
   return act == kActGeluTanh ? gelu_tanh(g) : silu(g);
 }
 
-template <int BM, int BN, int WGM, int WGN, int MODE, int EPI>
+template <int BM, int BN, int WGM, int WGN, int MODE, int EPI, int WPOS>
 __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int NT = WGM * WGN * 64;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -57,8 +61,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_bf16_kernel(GemmArgs a)
   constexpr int CH_A = BM * CPR / NT, CH_B = BN * CPR / NT;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "tile loads must divide evenly");
-  static_assert(MODE != kModeGated || (EPI == kEpiPartial || WTN == 64), "gated needs 64-wide wave tiles");
-  static_assert(MODE != kModeGated || WTN == 64, "gated B rows are interleaved in blocks of 32");
+  static_assert(MODE != kModeGated || FN % 2 == 0, "gated wave tiles hold gate and up halves");
   constexpr int STAGE = (BM + BN) * LDK;
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * STAGE];
 
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_bf16_kernel(GemmArgs a)
 #pragma unroll
   for (int i = 0; i < CH_B; ++i) {
     const int row = tid / CPR + i * (NT / CPR);
-    bp[i] = b_row<MODE, BN>(a, tn, row, kbeg) + kc * 8;
+    bp[i] = b_row<MODE, BN, WTN>(a, tn, row, kbeg) + kc * 8;
   }
 
   u32x4 ra[CH_A], rb[CH_B];
@@ -134,34 +137,47 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_bf16_kernel(GemmArgs a)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+  // Fragment registers are double-buffered across the 16-deep k-steps of a
+  // tile (the reads for step ks+1 are in flight while step ks's MFMAs issue),
+  // and the next tile's LDS write is issued after step WPOS-1 so that only
+  // the barrier is left at the end of the tile.
+  constexpr int KS = BK / 16;
+  const int frag_row = lane & 31, frag_k = (lane >> 5) * 8;
+  bf16x8 fa[2][FM], fb[2][FN];
+  auto lfrag = [&](int buf, int ks, int slot) {
+    const bf16* sA = smem + buf * STAGE;
+    const bf16* sB = sA + BM * LDK;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      fa[slot][i] = *reinterpret_cast<const bf16x8*>(sA + (wm * WTM + i * 32 + frag_row) * LDK + ks * 16 + frag_k);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      fb[slot][j] = *reinterpret_cast<const bf16x8*>(sB + (wn * WTN + j * 32 + frag_row) * LDK + ks * 16 + frag_k);
+  };
+
   if (nk > 0) {
     gload(0);
     sstore(0);
   }
   __syncthreads();
-  const int frag_row = lane & 31, frag_k = (lane >> 5) * 8;
+  if (nk > 0) lfrag(0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const bf16* sA = smem + buf * STAGE;
-    const bf16* sB = sA + BM * LDK;
+    const bool more = kt + 1 < nk;
+    if (more) gload(kt + 1);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(sA + (wm * WTM + i * 32 + frag_row) * LDK + ks * 16 + frag_k);
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(sB + (wn * WTN + j * 32 + frag_row) * LDK + ks * 16 + frag_k);
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < KS) lfrag(buf, ks + 1, cur ^ 1);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+      if (ks == WPOS - 1 && more) sstore(buf ^ 1);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
     __syncthreads();
+    if (more) lfrag(buf ^ 1, 0, 0);
   }
 
   // ---- epilogue: accumulator (i, lane) holds row (i/4)*8 + (lane/32)*4 + i%4, column lane%32 ----
@@ -171,11 +187,14 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_bf16_kernel(GemmArgs a)
     for (int e = 0; e < 16; ++e) {
       const int m = m0 + wm * WTM + i * 32 + (e / 4) * 8 + (lane >> 5) * 4 + (e % 4);
       if (m >= a.M) continue;
-      if (EPI == kEpiGated) {
-        const int n = tn * (BN / 2) + wn * 32 + (lane & 31);
-        if (n < a.N) {
-          const float g = acc[i][0][e], u = acc[i][1][e];
-          static_cast<bf16*>(a.C)[(int64_t)m * a.ldc + n] = from_f32<bf16>(apply_act(a.act, g) * u);
+      if constexpr (EPI == kEpiGated) {
+#pragma unroll
+        for (int j = 0; j < FN / 2; ++j) {
+          const int n = tn * (BN / 2) + wn * (WTN / 2) + j * 32 + (lane & 31);
+          if (n < a.N) {
+            const float g = acc[i][j][e], u = acc[i][j + FN / 2][e];
+            static_cast<bf16*>(a.C)[(int64_t)m * a.ldc + n] = from_f32<bf16>(apply_act(a.act, g) * u);
+          }
         }
       } else {
 #pragma unroll
@@ -186,10 +205,10 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_bf16_kernel(GemmArgs a)
             int64_t nb;
             int64_t NB;
             if (MODE == kModeGated) {
-              const int blk = cb / 64, w = cb % 64;
-              const int col = tn * (BN / 2) + blk * 32 + (w % 32);
+              const int blk = cb / WTN, w = cb % WTN;
+              const int col = tn * (BN / 2) + blk * (WTN / 2) + (w % (WTN / 2));
               if (col >= a.N) continue;
-              nb = (w < 32 ? 0 : a.N) + col;
+              nb = (w < WTN / 2 ? 0 : a.N) + col;
               NB = 2 * (int64_t)a.N;
             } else {
               nb = (int64_t)tn * BN + cb;
@@ -250,12 +269,22 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a) {
   }
 }
 
+int g_wpos = -1;  // LDS write position override (tuning), read once from GQA_GEMM_WPOS
+
 template <int BM, int BN, int WGM, int WGN, int MODE, int EPI>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
   const int cols = MODE == kModeGated ? BN / 2 : BN;
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + cols - 1) / cols);
   dim3 grid(tiles, a.splits);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, MODE, EPI>), grid, dim3(WGM * WGN * 64), 0, s, a);
+  if (g_wpos < 0) {
+    const char* e = getenv("GQA_GEMM_WPOS");
+    g_wpos = e ? atoi(e) : 3;
+  }
+  switch (g_wpos) {
+    case 2: hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, MODE, EPI, 2>), grid, dim3(WGM * WGN * 64), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, MODE, EPI, 4>), grid, dim3(WGM * WGN * 64), 0, s, a); break;
+    default: hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, MODE, EPI, 3>), grid, dim3(WGM * WGN * 64), 0, s, a); break;
+  }
   return hipGetLastError();
 }
 
@@ -263,6 +292,7 @@ template <int MODE, int EPI>
 hipError_t dispatch_tile(const GemmArgs& a, int tile, hipStream_t s) {
   switch (tile) {
     case kTile256x256: return launch_tile<256, 256, 2, 4, MODE, EPI>(a, s);
+    case kTile256x256w4: return launch_tile<256, 256, 2, 2, MODE, EPI>(a, s);
     case kTile256x192:
       if constexpr (MODE == kModeGated) return hipErrorInvalidValue;
       else return launch_tile<256, 192, 4, 2, MODE, EPI>(a, s);

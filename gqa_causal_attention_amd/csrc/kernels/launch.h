@@ -42,7 +42,7 @@ struct GemmArgs {
 };
 
 // Tile shapes of the bf16 MFMA GEMM.
-enum GemmTile { kTile256x256 = 0, kTile256x192 = 1, kTile64x128 = 2, kTile128x128 = 3 };
+enum GemmTile { kTile256x256 = 0, kTile256x192 = 1, kTile64x128 = 2, kTile128x128 = 3, kTile256x256w4 = 4 };
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int mode, int epi, int tile, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& a, int mode, int epi, hipStream_t s);
