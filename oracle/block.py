@@ -53,7 +53,7 @@ import numpy as np
 
 __all__ = [
     "rms_norm", "rope_cos_sin", "apply_rope", "silu", "gelu_tanh", "attention_row",
-    "OracleState", "block_forward", "block_step",
+    "OracleState", "block_forward", "block_step", "block_forward_rows",
 ]
 
 
@@ -384,3 +384,60 @@ def block_step(cfg: dict, W: dict, x: np.ndarray, state: OracleState, **kw) -> n
     if x.ndim == 2:
         x = x[:, None, :]
     return block_forward(cfg, W, x, state, **kw)
+
+
+def block_forward_rows(cfg: dict, W: dict, x: np.ndarray, rows, state: OracleState | None = None,
+                       *, dtype=np.float32) -> np.ndarray:
+    """Outputs of ``block_forward`` at selected (b, t) positions only.
+
+    Same definition as ``block_forward`` restricted to output rows: keys and
+    values are formed for every position (any query may read them), queries,
+    attention, o_proj and the MLP only for the requested rows.  The state is
+    read, not updated.  Returns an array [len(rows), d].
+    """
+    dt = np.dtype(dtype)
+    x = np.asarray(x)
+    B, L, d = x.shape
+    H, KV, hd = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    window = int(cfg.get("window", 0))
+    offset = cfg.get("norm", "rmsnorm") == "rmsnorm_offset"
+    eps = cfg["norm_eps"]
+    w = {k: v.astype(dt) for k, v in W.items()}
+    start = np.zeros(B, dtype=np.int64) if state is None else state.lengths.astype(np.int64)
+    out = np.empty((len(rows), d), dtype=dt)
+    by_row = {}
+    for i, (b, t) in enumerate(rows):
+        by_row.setdefault(int(b), []).append((i, int(t)))
+    for b, items in by_row.items():
+        s0 = int(start[b])
+        xb = x[b].astype(dt)
+        h = rms_norm(xb, w["input_layernorm.weight"], eps, offset)              # [L, d]
+        k = _linear(h, w["k_proj.weight"], w.get("k_proj.bias")).reshape(L, KV, hd)
+        v = _linear(h, w["v_proj.weight"], w.get("v_proj.bias")).reshape(L, KV, hd)
+        if cfg.get("qk_norm"):
+            k = rms_norm(k, w["k_norm.weight"], eps, offset)
+        pos = s0 + np.arange(L)
+        cos, sin = rope_cos_sin(pos, hd, cfg["rope_theta"])
+        k = apply_rope(k, cos[:, None, :], sin[:, None, :])
+        lo = max(0, s0 - window) if window > 0 else 0
+        if state is not None and s0 > lo:
+            cpos = np.arange(lo, s0)
+            slots = state.slot(cpos)
+            kall = np.concatenate([np.transpose(state.k[b][:, slots, :], (1, 0, 2)).astype(dt), k], axis=0)
+            vall = np.concatenate([np.transpose(state.v[b][:, slots, :], (1, 0, 2)).astype(dt), v], axis=0)
+            kpos = np.concatenate([cpos, pos])
+        else:
+            kall, vall, kpos = k, v, pos
+        ts = np.array([t for _, t in items])
+        hq = h[ts]
+        q = _linear(hq, w["q_proj.weight"], w.get("q_proj.bias")).reshape(len(ts), H, hd)
+        if cfg.get("qk_norm"):
+            q = rms_norm(q, w["q_norm.weight"], eps, offset)
+        cq, sq = rope_cos_sin(s0 + ts, hd, cfg["rope_theta"])
+        q = apply_rope(q, cq[:, None, :], sq[:, None, :])
+        ctx = attention_row(q, kall, vall, s0 + ts, kpos, window, cfg.get("attn_softcap", 0.0))
+        x1 = xb[ts] + ctx.reshape(len(ts), H * hd) @ w["o_proj.weight"].T
+        y = _mlp(cfg, w, x1[None], "batched")[0]
+        for (i, _), yr in zip(items, y):
+            out[i] = yr
+    return out

@@ -23,6 +23,7 @@ def check_close(y_gpu, y_ref, x, dtype, what=""):
     assert np.all(np.isfinite(y_gpu)), f"{what}: non-finite GPU output"
     e1 = rel_err(y_gpu, y_ref)
     e2 = rel_err(y_gpu - x, y_ref - x)
+    print(f"[parity] {what}: err(y)={e1:.3e} err(y-x)={e2:.3e} tol={tol}")
     assert e1 <= tol and e2 <= tol, f"{what}: err(y)={e1:.3e} err(y-x)={e2:.3e} tol={tol}"
     return e1, e2
 

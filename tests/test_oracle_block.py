@@ -281,3 +281,23 @@ def test_ring_slot_layout():
         np.testing.assert_array_equal(ring.k[:, :, p % 4], full.k[:, :, p])
         np.testing.assert_array_equal(ring.v[:, :, p % 4], full.v[:, :, p])
     assert np.all(full.k[:, :, 10:] == 0)
+
+
+@pytest.mark.parametrize("over", [dict(), dict(window=5, attn_softcap=2.0, norm="rmsnorm_offset",
+                                               mlp="geglu_tanh"), dict(qkv_bias=True, qk_norm=True)])
+def test_rows_form_matches_full_form(over):
+    from oracle import block_forward_rows
+    cfg, W = random_block(50, **over)
+    rng = np.random.default_rng(51)
+    x = rng.standard_normal((2, 13, 64))
+    rows = [(0, 0), (1, 12), (0, 7), (1, 3)]
+    full = block_forward(cfg, W, x, dtype=np.float64)
+    got = block_forward_rows(cfg, W, x, rows, dtype=np.float64)
+    np.testing.assert_allclose(got, np.stack([full[b, t] for b, t in rows]), rtol=1e-12, atol=1e-12)
+    # continuation from a carried state (ring included)
+    st = OracleState(cfg, 2, 40, dtype=np.float64)
+    block_forward(cfg, W, rng.standard_normal((2, 9, 64)), st, dtype=np.float64)
+    x2 = rng.standard_normal((2, 6, 64))
+    ref = block_forward(cfg, W, x2, st.copy(), dtype=np.float64)
+    got = block_forward_rows(cfg, W, x2, [(0, 5), (1, 0)], st, dtype=np.float64)
+    np.testing.assert_allclose(got, np.stack([ref[0, 5], ref[1, 0]]), rtol=1e-12, atol=1e-12)
