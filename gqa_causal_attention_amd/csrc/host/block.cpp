@@ -229,7 +229,13 @@ WsLayout layout_for(const gqa_block* blk, int B, int L) {
     if (L == 1 && attention_decode_bf16_supported(c.head_dim, blk->G)) {
       w.decode_attn = true;
       const int span = c.window > 0 ? std::min(c.window, c.max_positions) : c.max_positions;
-      w.max_chunks = (span + attention_decode_chunk() - 1) / attention_decode_chunk();
+      w.max_chunks = (span + attention_decode_chunk(c.head_dim) - 1) / attention_decode_chunk(c.head_dim);
+      if (w.max_chunks > 1024) {  // the combine merges at most 1024 chunks; longer caches use the flash path
+        w.decode_attn = false;
+        w.max_chunks = 0;
+      }
+    }
+    if (w.decode_attn) {
       w.attn_part = take((size_t)B * c.n_heads * w.max_chunks * (c.head_dim + 2) * 4);
     }
   }
@@ -441,7 +447,7 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
     if (bf && lay.decode_attn) {
       a.part = reinterpret_cast<float*>(base + lay.attn_part);
       a.max_chunks = lay.max_chunks;
-      a.chunk = attention_decode_chunk();
+      a.chunk = attention_decode_chunk(hd);
       // launch only as many chunks as the longest row needs
       int maxlen = 0;
       for (int b = 0; b < B; ++b) maxlen = std::max(maxlen, st ? st->lengths[b] : 0);

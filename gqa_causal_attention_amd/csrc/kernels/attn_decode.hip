@@ -9,13 +9,21 @@
 // guide: 2 * H_kv * d_h bytes per token and layer), and this kernel reads each
 // cached key/value exactly once for all G query heads of its group.
 //
-// Work item = (row b, kv head j, chunk of CH keys).  A workgroup of 256
-// threads reads its chunk's key rows with 16-byte coalesced loads (hd/8 lanes
-// per row), forms the G scores of each key (lane-shuffle reduction), takes the
-// chunk's max and exponentials in float32, then reads the value rows once and
-// accumulates the G partial outputs.  It writes (max, sum, output[hd]) per
-// (b, query head, chunk); the combine kernel merges the chunks of a row in
-// chunk order (deterministic).  Work items past a row's last chunk exit at
+// Work item = (row b, kv head j, split of 1024 keys).  A workgroup of 4
+// waves streams its split in sub-tiles of 128 keys, 32 per wave; each wave
+// issues all of its K and V loads for a sub-tile at once (16 KB in flight per
+// wave), full sub-tiles taking a short address path:
+//  * scores on the matrix cores: S^T[16 keys][16 heads] = K Q^T with
+//    v_mfma_f32_16x16x32_bf16, K read straight from HBM in the operand layout
+//    (lane -> key lane%16, 16-byte dim pieces), Q^T resident in registers
+//    (heads past G are zero columns) — no conversions, no cross-lane sums;
+//  * per-wave online softmax in float32 (base 2; the reference max is raised
+//    lazily, beyond 2^8), the weights handed through a 16 x G slab of LDS;
+//  * values on the vector ALUs: each lane owns 8 dims of one value row and
+//    accumulates G outputs with float32 FMAs.
+// The four waves are merged once at the end.  It writes (output[hd], max,
+// sum) per (b, query head, split); the combine kernel merges a row's splits
+// in split order (deterministic).  Work items past a row's last split exit at
 // once (rows have different lengths).
 #include "common.h"
 #include "launch.h"
@@ -24,235 +32,255 @@ namespace gqa {
 namespace {
 
 constexpr int NT = 256;
-constexpr int CH = 512;  // keys per work item
-
-__device__ __forceinline__ const bf16* dec_row(const AttnArgs& a, const void* fresh, const void* cache, int b, int j,
-                                              int start, int kp) {
-  if (kp >= start)
-    return static_cast<const bf16*>(fresh) + (((int64_t)b * a.KV + j) * a.L + (kp - start)) * a.hd;
-  const int slot = a.window > 0 ? kp % a.window : kp;
-  return static_cast<const bf16*>(cache) + (((int64_t)b * a.KV + j) * a.cap + slot) * a.hd;
-}
-
-// Sum over aligned groups of N lanes (N = 8, 16 or 32) with DPP row moves.
-template <int N>
-__device__ __forceinline__ float row_sum(float x) {
-  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
-  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
-  x += dpp<0x141>(x);  // row_half_mirror: the other quad of the 8
-  if (N >= 16) x += dpp<0x140>(x);  // row_mirror: the other 8 of the 16
-  if (N >= 32) x += __shfl_xor(x, 16, WAVE);
-  return x;
-}
+constexpr int NWV = NT / WAVE;
+constexpr int KPW = 32;                 // keys per wave per sub-tile (two 16-key MFMA blocks)
+constexpr int SUBK = KPW * NWV;         // keys per sub-tile (128)
+constexpr int NSUB = 8;                 // sub-tiles per split (1024 keys)
+constexpr float kSlack = 8.0f;          // lazy rescale threshold (log2 units)
 
 template <int HD, int G>
 __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs a) {
-  constexpr int LPR = HD / 8;           // lanes per key row (8 bf16 each)
-  constexpr int RPI = NT / LPR;         // rows per workgroup iteration
-  constexpr int NIT = CH / RPI;         // iterations over the chunk
-  constexpr int UNR = NIT >= 8 ? 8 : NIT;
-  __shared__ float sc[G][CH];           // scores, then weights
-  __shared__ float red[NT / WAVE][G];
-  __shared__ float ored[NT / WAVE][G][HD];
+  constexpr int NK = HD / 32;           // 16-byte K pieces per lane per 16-key block (= MFMA k-steps)
+  constexpr int LPR = HD / 8;           // lanes per V row
+  constexpr int RPV = WAVE / LPR;       // V rows per wave load
+  constexpr int NV = KPW / RPV;         // V loads per lane per sub-tile
+  __shared__ float sp[NWV][KPW][G];     // this sub-tile's weights, per wave
+  __shared__ float wm[NWV][G], wl[NWV][G];
+  __shared__ float wo[NWV][G][HD];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int chunk = blockIdx.x % a.max_chunks;
+  const int split = blockIdx.x % a.max_chunks;
   const int bj = blockIdx.x / a.max_chunks;
   const int b = bj / a.KV, j = bj % a.KV;
   const int start = a.lengths ? a.lengths[b] : 0;
   const int p = start;                  // the new token's position (L = 1)
-  const int klo = a.window > 0 ? max(0, p - a.window + 1) : 0;
-  const int nkeys = p - klo + 1;
-  const int nchunks = (nkeys + CH - 1) / CH;
-  if (chunk >= nchunks) return;
-  const int kc0 = klo + chunk * CH;
-  const int kcnt = min(CH, p + 1 - kc0);
+  const int W = a.window;
+  const int klo = W > 0 ? max(0, p - W + 1) : 0;
+  const int nsplit = (p - klo + 1 + a.chunk - 1) / a.chunk;
+  if (split >= nsplit) return;
+  const int ks0 = klo + split * a.chunk;
+  const int kend = min(ks0 + a.chunk, p + 1);
+  const int nsub = (kend - ks0 + SUBK - 1) / SUBK;
 
-  const int rl = tid % LPR;             // lane within the row group: dims 8rl..8rl+7
-  const int rg = tid / LPR;             // row group
-  const float scale = 1.0f / sqrtf((float)HD);
+  const int64_t bjo = (int64_t)b * a.KV + j;
+  const bf16* kfresh = static_cast<const bf16*>(a.knew) + bjo * a.L * HD;
+  const bf16* vfresh = static_cast<const bf16*>(a.vnew) + bjo * a.L * HD;
+  const bf16* kbase = a.kcache ? static_cast<const bf16*>(a.kcache) + bjo * a.cap * HD : kfresh;
+  const bf16* vbase = a.vcache ? static_cast<const bf16*>(a.vcache) + bjo * a.cap * HD : vfresh;
+  // row of key position kp (clamped into the split): cache slot kp (or kp mod W), or the fresh row
+  auto row = [&](const bf16* fresh, const bf16* base, int kp) {
+    kp = min(kp, kend - 1);
+    return kp >= start ? fresh + (int64_t)(kp - start) * HD
+                       : base + (int64_t)(W > 0 ? kp % W : kp) * HD;
+  };
+
+  // K in the MFMA A layout: lane -> key (lane % 16) of each 16-key block, dims 32s + 8(lane / 16)
+  // V in rows: lane -> key t*RPV + lane / LPR, dims 8(lane % LPR)
+  const int kkey = lane % 16, kdim = 8 * (lane / 16);
+  const int vkey = lane / LPR, vdim = 8 * (lane % LPR);
+
+  // Q^T in the MFMA B layout: lane -> head (lane % 16) (zero past G), same dims as K
+  const int qh = lane % 16;
+  bf16x8 qf[NK];
+#pragma unroll
+  for (int s2 = 0; s2 < NK; ++s2) {
+    if (qh < G) {
+      const bf16* qr = static_cast<const bf16*>(a.q) + (int64_t)b * a.ldq + (int64_t)(j * G + qh) * HD + kdim;
+      qf[s2] = *reinterpret_cast<const bf16x8*>(qr + 32 * s2);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[s2][e] = from_f32<bf16>(0.f);
+    }
+  }
   const float cap = a.softcap;
+  const float scale = 1.0f / sqrtf((float)HD);
 
-  // q values of the G heads for this lane's 8 dims
-  float qv[G][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const bf16* qr = static_cast<const bf16*>(a.q) + (int64_t)b * a.ldq + (int64_t)(j * G + g) * HD + rl * 8;
-    const u32x4 u = *reinterpret_cast<const u32x4*>(qr);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      qv[g][2 * e] = bf16_lo(u[e]);
-      qv[g][2 * e + 1] = bf16_hi(u[e]);
-    }
-  }
-
-  // ---- phase 1: scores ----
-  for (int it0 = 0; it0 < NIT; it0 += UNR) {
-    u32x4 kr[UNR];
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int kl = (it0 + u) * RPI + rg;
-      const int kp = kc0 + min(kl, kcnt - 1);
-      kr[u] = *reinterpret_cast<const u32x4*>(dec_row(a, a.knew, a.kcache, b, j, start, kp) + rl * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int kl = (it0 + u) * RPI + rg;
-      float kf[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kf[2 * e] = bf16_lo(kr[u][e]);
-        kf[2 * e + 1] = bf16_hi(kr[u][e]);
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float s = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s = fmaf(qv[g][e], kf[e], s);
-        s = row_sum<LPR>(s);
-        s *= scale;
-        if (cap > 0.f) s = cap * tanh_exp(s / cap);
-        if (rl == g % LPR) sc[g][kl] = kl < kcnt ? s : -INFINITY;
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- phase 2: chunk max, weights, sum (per head) ----
-  float mloc[G], lloc[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float mx = -INFINITY;
-    for (int i = tid; i < CH; i += NT) mx = fmaxf(mx, sc[g][i]);
-    mx = wave_max(mx);
-    if (lane == 0) red[w][g] = mx;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float mx = red[0][g];
-#pragma unroll
-    for (int i = 1; i < NT / WAVE; ++i) mx = fmaxf(mx, red[i][g]);
-    mloc[g] = mx;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float ls = 0.f;
-    for (int i = tid; i < CH; i += NT) {
-      const float e = exp2_fast((sc[g][i] - mloc[g]) * kLog2e);
-      sc[g][i] = e;
-      ls += e;
-    }
-    ls = wave_sum(ls);
-    if (lane == 0) red[w][g] = ls;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float ls = 0.f;
-#pragma unroll
-    for (int i = 0; i < NT / WAVE; ++i) ls += red[i][g];
-    lloc[g] = ls;
-  }
-
-  // ---- phase 3: weighted values ----
-  float ov[G][8];
+  // per-wave online softmax: m (equal on all lanes of a head), l partial, o[g][8 dims]
+  float m_run = -INFINITY, l_run = 0.f;
+  float o[G][8];
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ov[g][e] = 0.f;
-  for (int it0 = 0; it0 < NIT; it0 += UNR) {
-    u32x4 vr[UNR];
+    for (int e = 0; e < 8; ++e) o[g][e] = 0.f;
+
+  for (int n = 0; n < nsub; ++n) {
+    const int k0 = ks0 + n * SUBK + w * KPW;
+    // ---- loads: all of this wave's K and V for the sub-tile at once ----
+    u32x4 kr[2][NK], vr[NV];
+    if (W == 0 && k0 + KPW <= min(start, kend)) {   // every row a cache slot = position
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int kl = (it0 + u) * RPI + rg;
-      const int kp = kc0 + min(kl, kcnt - 1);
-      vr[u] = *reinterpret_cast<const u32x4*>(dec_row(a, a.vnew, a.vcache, b, j, start, kp) + rl * 8);
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int s2 = 0; s2 < NK; ++s2)
+          kr[h2][s2] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)(k0 + 16 * h2 + kkey) * HD + kdim + 32 * s2);
+#pragma unroll
+      for (int t = 0; t < NV; ++t)
+        vr[t] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)(k0 + t * RPV + vkey) * HD + vdim);
+    } else {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const bf16* kp = row(kfresh, kbase, k0 + 16 * h2 + kkey) + kdim;
+#pragma unroll
+        for (int s2 = 0; s2 < NK; ++s2) kr[h2][s2] = *reinterpret_cast<const u32x4*>(kp + 32 * s2);
+      }
+#pragma unroll
+      for (int t = 0; t < NV; ++t)
+        vr[t] = *reinterpret_cast<const u32x4*>(row(vfresh, vbase, k0 + t * RPV + vkey) + vdim);
     }
+
+    // ---- scores: S^T[16 keys][16 heads] per block; lane holds keys 4(lane/16)+e ----
+    f32x4 sc[2];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int kl = (it0 + u) * RPI + rg;
+    for (int h2 = 0; h2 < 2; ++h2) {
+      sc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s2 = 0; s2 < NK; ++s2)
+        sc[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[h2][s2]), qf[s2], sc[h2], 0, 0, 0);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v = cap > 0.f ? cap * kLog2e * tanh_exp(sc[h2][e] * scale / cap) : sc[h2][e] * (scale * kLog2e);
+        v = (k0 + 16 * h2 + 4 * (lane / 16) + e < kend) ? v : -INFINITY;
+        sc[h2][e] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+    mx = fmaxf(mx, xor32(mx));
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kSlack)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float ag = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), g));  // head g's factor
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[g][e] *= ag;
+      }
+    }
+    const float mr = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float pw = exp2_fast(sc[h2][e] - mr);
+        l_run += pw;
+        if (qh < G) sp[w][16 * h2 + 4 * (lane / 16) + e][qh] = pw;
+      }
+    // the weights go to this wave's LDS slab and come back as per-key broadcasts
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the LDS writes have completed
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- values: o[g][dims] += w[key][g] * v[key][dims] ----
+#pragma unroll
+    for (int t = 0; t < NV; ++t) {
+      const int kk = t * RPV + vkey;
       float vf[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        vf[2 * e] = bf16_lo(vr[u][e]);
-        vf[2 * e + 1] = bf16_hi(vr[u][e]);
+        vf[2 * e] = bf16_lo(vr[t][e]);
+        vf[2 * e + 1] = bf16_hi(vr[t][e]);
       }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float pw = sc[g][kl];  // 0 for keys past the chunk's end
+        const float pw = sp[w][kk][g];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ov[g][e] = fmaf(pw, vf[e], ov[g][e]);
+        for (int e = 0; e < 8; ++e) o[g][e] = fmaf(pw, vf[e], o[g][e]);
       }
     }
+    __builtin_amdgcn_wave_barrier();
   }
-  // reduce over the row groups of a wave, then across waves through LDS
+
+  // wave totals: l over the 4 lanes of a head, o over the V row groups
+  l_run += __shfl_xor(l_run, 16, WAVE);
+  l_run += xor32(l_run);
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float v = ov[g][e];
+      float v = o[g][e];
 #pragma unroll
-      for (int o = LPR; o < WAVE; o <<= 1) v += __shfl_xor(v, o, WAVE);
-      ov[g][e] = v;
+      for (int off = LPR; off < WAVE; off <<= 1) v += __shfl_xor(v, off, WAVE);
+      o[g][e] = v;
     }
+  if (lane < G) {
+    wm[w][lane] = m_run;
+    wl[w][lane] = l_run;
+  }
   if (lane < LPR) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ored[w][g][rl * 8 + e] = ov[g][e];
+      for (int e = 0; e < 8; ++e) wo[w][g][vdim + e] = o[g][e];
   }
   __syncthreads();
-  // partial record: [B, H, max_chunks, HD + 2] = (out[HD], max, sum)
+  // partial record: [B, H, max_chunks, HD + 2] = (out[HD], max (base 2), sum)
   for (int i = tid; i < G * HD; i += NT) {
     const int g = i / HD, d = i % HD;
-    float s = 0.f;
+    float M = wm[0][g];
 #pragma unroll
-    for (int ww = 0; ww < NT / WAVE; ++ww) s += ored[ww][g][d];
-    float* rec = a.part + (((int64_t)b * a.H + j * G + g) * a.max_chunks + chunk) * (HD + 2);
-    rec[d] = s;
+    for (int ww = 1; ww < NWV; ++ww) M = fmaxf(M, wm[ww][g]);
+    float s2 = 0.f, ls = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NWV; ++ww) {
+      const float f = wm[ww][g] == -INFINITY ? 0.f : exp2_fast(wm[ww][g] - M);
+      s2 += wo[ww][g][d] * f;
+      ls += wl[ww][g] * f;
+    }
+    float* rec = a.part + (((int64_t)b * a.H + j * G + g) * a.max_chunks + split) * (HD + 2);
+    rec[d] = s2;
     if (d == 0) {
-      rec[HD] = mloc[g];
-      rec[HD + 1] = lloc[g];
+      rec[HD] = M;
+      rec[HD + 1] = ls;
     }
   }
 }
 
-// One wavefront per (row, query head): merge the row's chunks in order.
+// One workgroup per (row, query head): merge the row's chunks in chunk order.
 template <int HD>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (gw >= (int64_t)a.B * a.H) return;
-  const int b = (int)(gw / a.H), h = (int)(gw % a.H);
+  const int CH = a.chunk;
+  constexpr int DG = 256 / HD;          // chunk groups summed in parallel (2 for hd=128)
+  __shared__ float fw[1024];
+  __shared__ float red[8];
+  __shared__ float osum[DG][HD];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x / a.H, h = blockIdx.x % a.H;
   const int p = a.lengths ? a.lengths[b] : 0;
   const int klo = a.window > 0 ? max(0, p - a.window + 1) : 0;
-  const int nchunks = min((p - klo + 1 + CH - 1) / CH, a.max_chunks);
+  const int nchunks = min((p - klo + 1 + CH - 1) / CH, min(a.max_chunks, 1024));
   const float* rec = a.part + ((int64_t)b * a.H + h) * a.max_chunks * (HD + 2);
-  float M = -INFINITY;
-  for (int c = 0; c < nchunks; ++c) M = fmaxf(M, rec[c * (HD + 2) + HD]);
-  constexpr int PE = (HD + 63) / 64;
-  float o[PE];
-#pragma unroll
-  for (int i = 0; i < PE; ++i) o[i] = 0.f;
-  float lsum = 0.f;
-  for (int c = 0; c < nchunks; ++c) {
-    const float* r = rec + c * (HD + 2);
-    const float f = exp2_fast((r[HD] - M) * kLog2e);
-    lsum += f * r[HD + 1];
-#pragma unroll
-    for (int i = 0; i < PE; ++i) {
-      const int d = lane + i * 64;
-      if (d < HD) o[i] += f * r[d];
-    }
+  float m = -INFINITY;
+  for (int c = tid; c < nchunks; c += 256) m = fmaxf(m, rec[c * (HD + 2) + HD]);
+  m = wave_max(m);
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float l = 0.f;
+  for (int c = tid; c < nchunks; c += 256) {
+    const float f = exp2_fast(rec[c * (HD + 2) + HD] - M);
+    fw[c] = f;
+    l += f * rec[c * (HD + 2) + HD + 1];
   }
-  const float inv = 1.0f / lsum;
-  bf16* out = static_cast<bf16*>(a.ctx) + (int64_t)b * a.H * HD + (int64_t)h * HD;
+  l = wave_sum(l);
+  if ((tid & 63) == 0) red[4 + (tid >> 6)] = l;
+  __syncthreads();
+  const float lsum = red[4] + red[5] + red[6] + red[7];
+  const int d = tid % HD, cg = tid / HD;
+  float o = 0.f;
+#pragma unroll 8
+  for (int c = cg; c < nchunks; c += DG) o = fmaf(fw[c], rec[c * (HD + 2) + d], o);
+  osum[cg][d] = o;
+  __syncthreads();
+  if (tid < HD) {
+    float t = 0.f;
 #pragma unroll
-  for (int i = 0; i < PE; ++i) {
-    const int d = lane + i * 64;
-    if (d < HD) out[d] = from_f32<bf16>(o[i] * inv);
+    for (int g = 0; g < DG; ++g) t += osum[g][tid];
+    static_cast<bf16*>(a.ctx)[(int64_t)b * a.H * HD + (int64_t)h * HD + tid] = from_f32<bf16>(t / lsum);
   }
 }
 
@@ -278,10 +306,11 @@ hipError_t launch_h(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 bool attention_decode_bf16_supported(int hd, int G) {
-  return (hd == 64 || hd == 128 || hd == 256) && (G == 1 || G == 2 || G == 4 || G == 5 || G == 8);
+  return (hd == 64 || hd == 128 || hd == 256) && (G == 1 || G == 2 || G == 4 || G == 5 || G == 8);  // G <= 16
 }
 
-int attention_decode_chunk() { return CH; }
+// Keys per split-K work item: 8 sub-tiles of 128 keys.
+int attention_decode_chunk(int) { return NSUB * SUBK; }
 
 hipError_t launch_attention_decode_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
@@ -299,7 +328,7 @@ namespace gqa {
 
 hipError_t launch_attention_decode_combine(const AttnArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
-  dim3 g2((unsigned)(((int64_t)a.B * a.H + 3) / 4));
+  dim3 g2((unsigned)((int64_t)a.B * a.H));
   switch (a.hd) {
     case 64: hipLaunchKernelGGL(attn_combine_kernel<64>, g2, dim3(256), 0, s, a); break;
     case 128: hipLaunchKernelGGL(attn_combine_kernel<128>, g2, dim3(256), 0, s, a); break;

@@ -93,7 +93,7 @@ bool attention_prefill_bf16_supported(int hd, int G);
 hipError_t launch_attention_decode_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_decode_combine(const AttnArgs& a, hipStream_t s);
 bool attention_decode_bf16_supported(int hd, int G);
-int attention_decode_chunk();
+int attention_decode_chunk(int hd);  // keys per split-K work item
 
 hipError_t launch_count_nonfinite(const void* p, int elem, int64_t n, int* flag, hipStream_t s);
 hipError_t launch_bump_lengths(int* lengths, int n, int by, hipStream_t s);

@@ -177,3 +177,38 @@ def test_empty_inputs(torch_cuda):
     y = blk.forward(torch.zeros((2, 0, 512), dtype=torch.float32, device="cuda"), st)
     assert y.shape == (2, 0, 512)
     assert st.host_lengths().tolist() == [0, 0]
+
+
+def test_decode_step_graph_replays_match_eager(torch_cuda):
+    """The decode step captured in a HIP graph (positions restored on the device
+    inside the graph): every replay equals the eager step bit for bit, with
+    eager work and synchronisations between the replays."""
+    torch = torch_cuda
+    cfg, W = random_block(408, dtype="bf16", **LLAMA_SMALL)
+    blk = _blk(cfg, W)
+    rng = np.random.default_rng(11)
+    B = 4
+    st = blk.allocate_state(B, 600)
+    blk.forward(to_gpu(rng.standard_normal((B, 500, 512), dtype=np.float32)), st)
+    lengths = st.host_lengths().copy()
+    x = to_gpu(rng.standard_normal((B, 1, 512), dtype=np.float32))
+    y = torch.empty_like(x)
+    k0, v0 = st.k.clone(), st.v.clone()
+    ref = blk.step(x, st).clone()
+    st.set_lengths(lengths)
+    blk.step(x, st, out=y)
+    torch.cuda.synchronize()
+    lengths_dev = torch.from_numpy(lengths.astype(np.int32)).cuda()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        st.lengths.copy_(lengths_dev)
+        blk.step(x, st, out=y)
+    for i in range(4):
+        y.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(y.cpu().numpy(), ref.cpu().numpy())
+        assert st.lengths.cpu().tolist() == (lengths + 1).tolist()
+        _ = blk.forward(to_gpu(rng.standard_normal((1, 8, 512), dtype=np.float32)))  # unrelated eager work
+        torch.cuda.synchronize()
+    assert torch.equal(st.v[:, :, :500], v0[:, :, :500])
