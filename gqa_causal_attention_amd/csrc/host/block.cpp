@@ -155,18 +155,22 @@ namespace {
 
 bool is_bf16(const gqa_block* b) { return b->cfg.weight_dtype == GQA_BF16; }
 
-// Tile and K-split choice for a bf16 GEMM with M rows, N output columns
-// (N_b weight rows), K depth.  Large M: the wave tile count decides between
-// 256x256 and 256x192 (gfx950 has 256 CUs).  Small M (decode): 64x128 tiles,
-// K split until there are >= 2 workgroups per CU.
+// The large-M tile: 8 waves of 128x64 (default) or 4 waves of 128x128
+// (GQA_GEMM_BIG_TILE=4, a tuning override).
 int big_tile() {
   static int t = [] {
-    const char* e = getenv("GQA_GEMM_BIG_TILE");  // tuning override: 0 = 8 waves, 4 = 4 waves
+    const char* e = getenv("GQA_GEMM_BIG_TILE");
     return e ? atoi(e) : (int)kTile256x256;
   }();
   return t;
 }
 
+// Tile and K-split choice for a bf16 GEMM with M rows, N output columns, K
+// depth.  Large M: the wave count decides between 256x256 and 256x192 tiles
+// (gfx950 has 256 CUs).  Decode-sized M (<= 64): weight-streaming 64x64
+// tiles; K is split only while there are fewer than 256 tiles, and never
+// below 1024-deep splits, so the float32 partials stay a small fraction of
+// the weight bytes.
 GemmPlan plan_gemm(int M, int N, int K, bool gated) {
   if (M > 128) {
     if (M <= 512) return {kTile128x128, 1};
@@ -179,11 +183,37 @@ GemmPlan plan_gemm(int M, int N, int K, bool gated) {
     }
     return {big_tile(), 1};
   }
-  const int cols = gated ? 64 : 128;
-  const long tiles = (long)((M + 63) / 64) * ((N + cols - 1) / cols);
+  if (M > 64) {
+    const int cols = gated ? 64 : 128;
+    const long tiles = (long)((M + 63) / 64) * ((N + cols - 1) / cols);
+    int splits = 1;
+    while (tiles * splits < 512 && K / (splits * 2) >= 256 && (K / 64) % (splits * 2) == 0) splits *= 2;
+    return {kTile64x128, splits};
+  }
+  // M <= 64: the weight-streaming kernel (128 weight rows per workgroup).
+  // Split K (in halves, keeping 128-multiples) until there are about two
+  // workgroups per CU, but not below 512-deep splits: the float32 partials of
+  // a split cost M * 4 bytes per weight row against 2 * k_split weight bytes.
+  static const int target = [] {
+    const char* e = getenv("GQA_SKINNY_TARGET");  // tuning override
+    return e ? atoi(e) : 512;
+  }();
+  static const int kmin = [] {
+    const char* e = getenv("GQA_SKINNY_KMIN");  // tuning override
+    return e ? atoi(e) : 512;
+  }();
+  if (gemm_skinny_supported(M, N, K, K)) {
+    const long tiles = ((gated ? 2L * N : (long)N) + 127) / 128;
+    int splits = 1;
+    while (tiles * splits < target && K % (splits * 2 * 128) == 0 && K / (splits * 2) >= kmin) splits *= 2;
+    return {kTileSkinny, splits};
+  }
+  const int cols = gated ? 32 : 64;
+  const long tiles = (N + cols - 1) / cols;
   int splits = 1;
-  while (tiles * splits < 512 && K / (splits * 2) >= 256 && (K / 64) % (splits * 2) == 0) splits *= 2;
-  return {kTile64x128, splits};
+  if (tiles < 256)
+    while (tiles * splits < 512 && K / (splits * 2) >= 1024 && (K / 64) % (splits * 2) == 0) splits *= 2;
+  return {kTile64x64, splits};
 }
 
 struct WsLayout {

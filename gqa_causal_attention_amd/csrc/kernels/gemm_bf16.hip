@@ -298,6 +298,7 @@ hipError_t dispatch_tile(const GemmArgs& a, int tile, hipStream_t s) {
       else return launch_tile<256, 192, 4, 2, MODE, EPI>(a, s);
     case kTile128x128: return launch_tile<128, 128, 2, 2, MODE, EPI>(a, s);
     case kTile64x128: return launch_tile<64, 128, 1, 2, MODE, EPI>(a, s);
+    case kTile64x64: return launch_tile<64, 64, 2, 1, MODE, EPI>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -305,6 +306,7 @@ hipError_t dispatch_tile(const GemmArgs& a, int tile, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int mode, int epi, int tile, hipStream_t s) {
+  if (tile == kTileSkinny) return launch_gemm_skinny(a, mode, epi, s);
   if (mode == kModeGated) {
     if (epi == kEpiGated) return dispatch_tile<kModeGated, kEpiGated>(a, tile, s);
     if (epi == kEpiPartial) return dispatch_tile<kModeGated, kEpiPartial>(a, tile, s);

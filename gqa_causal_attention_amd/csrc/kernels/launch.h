@@ -42,9 +42,14 @@ struct GemmArgs {
 };
 
 // Tile shapes of the bf16 MFMA GEMM.
-enum GemmTile { kTile256x256 = 0, kTile256x192 = 1, kTile64x128 = 2, kTile128x128 = 3, kTile256x256w4 = 4 };
+enum GemmTile { kTile256x256 = 0, kTile256x192 = 1, kTile64x128 = 2, kTile128x128 = 3, kTile256x256w4 = 4,
+                kTile64x64 = 5, kTileSkinny = 6 };
 
+// kTileSkinny dispatches to launch_gemm_skinny.
 hipError_t launch_gemm_bf16(const GemmArgs& a, int mode, int epi, int tile, hipStream_t s);
+// Weight-streaming GEMM for M <= 64 (decode); K split in multiples of 128.
+bool gemm_skinny_supported(int M, int N, int K, int k_split);
+hipError_t launch_gemm_skinny(const GemmArgs& a, int mode, int epi, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& a, int mode, int epi, hipStream_t s);
 // Sum the K-split partials in split order, then apply `epi` (kEpiStore / kEpiResid /
 // kEpiGated) writing a.C; `out_type` is the element type of a.C for Store/Gated.

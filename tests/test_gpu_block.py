@@ -113,6 +113,33 @@ def test_bf16_decode_ragged_rows_prefilled_cache(torch_cuda):
     np.testing.assert_array_equal(st.lengths.cpu().numpy(), lengths + 3)
 
 
+DECODE_GEMM_BLOCKS = {
+    # every projection K-split (k_split 512 or 640: even and odd 128-deep chunk counts)
+    "split": dict(d_model=1024, n_heads=8, n_kv_heads=2, head_dim=128, intermediate=1280, qkv_bias=True),
+    # no split: the fused bias / residual / gated epilogues (3 and 5 chunks)
+    "fused": dict(d_model=384, n_heads=6, n_kv_heads=2, head_dim=64, intermediate=640, qkv_bias=True,
+                  mlp="geglu_tanh"),
+}
+
+
+@pytest.mark.parametrize("B", [1, 7, 20, 33, 64])
+@pytest.mark.parametrize("kind", list(DECODE_GEMM_BLOCKS))
+def test_bf16_decode_gemm_batch_sizes(torch_cuda, kind, B):
+    """Decode steps at every activation-row tiling of the decode GEMMs (1, 2
+    and 4 groups of 16 rows, ragged last group), split and unsplit K."""
+    cfg, W = random_block(210 + list(DECODE_GEMM_BLOCKS).index(kind), dtype="bf16", **DECODE_GEMM_BLOCKS[kind])
+    rng = np.random.default_rng(12 + B)
+    blk = _block(cfg, W)
+    st = blk.allocate_state(B, 8)
+    ost = OracleState(cfg, B, 8)
+    x = rng.standard_normal((B, 5, cfg["d_model"]), dtype=np.float32)
+    check_close(blk.forward(to_gpu(x), st).cpu().numpy(), block_forward(cfg, W, x, ost), x, "bf16", "prefill")
+    for i in range(2):
+        xt = rng.standard_normal((B, cfg["d_model"]), dtype=np.float32)
+        check_close(blk.step(to_gpu(xt), st).cpu().numpy(), block_step(cfg, W, xt, ost), xt, "bf16",
+                    f"{kind} B={B} step {i}")
+
+
 def test_bf16_window_ring_wraps(torch_cuda):
     """Prefill longer than the window (in-call keys from the fresh K/V), then
     decode steps through the ring's wrap-around."""
