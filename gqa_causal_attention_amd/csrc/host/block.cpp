@@ -155,14 +155,29 @@ namespace {
 
 bool is_bf16(const gqa_block* b) { return b->cfg.weight_dtype == GQA_BF16; }
 
-// The large-M tile: 8 waves of 128x64 (default) or 4 waves of 128x128
-// (GQA_GEMM_BIG_TILE=4, a tuning override).
+// The large-M tile: 256x256 on the direct-to-LDS pipelined kernel (8 waves of
+// 128x64, 64-deep slices, 2 stages).  GQA_GEMM_BIG_TILE (a GemmTile value)
+// overrides it for tuning.
 int big_tile() {
   static int t = [] {
     const char* e = getenv("GQA_GEMM_BIG_TILE");
-    return e ? atoi(e) : (int)kTile256x256;
+    return e ? atoi(e) : (int)kTileDma256x256;
   }();
   return t;
+}
+// Tile order of the pipelined GEMM (GQA_GEMM_ORDER overrides the XCD-aware
+// default for tuning).
+int gemm_tile_order() {
+  static int o = [] {
+    const char* e = getenv("GQA_GEMM_ORDER");
+    return e ? atoi(e) : 0;
+  }();
+  return o;
+}
+// The 256x192 tile that goes with big_tile() (same kernel family).
+int big_tile_192() {
+  const int t = big_tile();
+  return gemm_dma_tile(t) ? (int)kTileDma256x192 : (int)kTile256x192;
 }
 
 // Tile and K-split choice for a bf16 GEMM with M rows, N output columns, K
@@ -179,7 +194,7 @@ GemmPlan plan_gemm(int M, int N, int K, bool gated) {
     if (!gated && N % 192 == 0) {
       const long t192 = (long)((M + 255) / 256) * (N / 192);
       auto eff = [](long t) { return (double)t / (double)(((t + 255) / 256) * 256); };
-      if (eff(t192) > eff(t256) + 0.05) return {kTile256x192, 1};
+      if (eff(t192) > eff(t256) + 0.05) return {big_tile_192(), 1};
     }
     return {big_tile(), 1};
   }
@@ -398,6 +413,7 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
 
   // GEMM helper: fused epilogue, or K-split partials + ordered reduce.
   auto gemm = [&](const char* name, GemmArgs a, int mode, int epi, const GemmPlan& p) -> int {
+    a.order = gemm_tile_order();
     if (!bf) {
       Scope sc(tm, name, s);
       HIP_TRY(launch_gemm_f32(a, mode, epi, s));

@@ -307,6 +307,7 @@ hipError_t dispatch_tile(const GemmArgs& a, int tile, hipStream_t s) {
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int mode, int epi, int tile, hipStream_t s) {
   if (tile == kTileSkinny) return launch_gemm_skinny(a, mode, epi, s);
+  if (gemm_dma_tile(tile)) return launch_gemm_dma(a, mode, epi, tile, s);
   if (mode == kModeGated) {
     if (epi == kEpiGated) return dispatch_tile<kModeGated, kEpiGated>(a, tile, s);
     if (epi == kEpiPartial) return dispatch_tile<kModeGated, kEpiPartial>(a, tile, s);

@@ -1,0 +1,383 @@
+// bf16 "TN" GEMM for prefill-sized M on gfx950 matrix cores:
+//   C[m, n] = sum_k A[m, k] * W[n, k]
+// A = activations [M, K], W = a Hugging Face [out, in] weight (mojolearn
+// TransformerBlock weight table: q/k/v, o_proj, gate/up, down), both
+// K-contiguous.  Same epilogues as the register-staged kernel (q/k/v segments
+// + bias, residual add, act(gate) * up, split-K partials).
+//
+// Tiles stream from global memory straight into LDS with
+// global_load_lds_dwordx4 (no register round trip, no LDS write
+// instructions), through a ring of ST stages of BK-deep k-slices.  One
+// barrier per slice, placed after the last fragment reads of slice kt and
+// before that k-step's MFMAs: it publishes slice kt + 1 (every wave has waited
+// for its own loads of it) and frees slice kt's stage, which is refilled with
+// slice kt + ST at once; the MFMAs of the last k-step then overlap the first
+// fragment reads of slice kt + 1.
+//
+// A load instruction writes 64 lanes x 16 bytes contiguously into LDS, so the
+// LDS layout is chosen through the global address each lane reads: lane l of
+// load instruction i fetches row i * RPI + l / CPR (CPR = 16-byte chunks per
+// row), chunk (l % CPR) ^ swz(row).  Each instruction therefore reads whole
+// rows (full cache lines), and an MFMA fragment read (32 consecutive rows, one
+// chunk) hits 16 distinct 16-byte bank groups in every 16-lane phase: the XOR
+// key swz(row) = (row / RP) % CPR, with RP rows per 256 bytes of LDS, gives
+// each of 16 consecutive rows its own (row % RP, slot) pair.
+//
+// Each wave owns a (BM/WGM) x (BN/WGN) sub-tile of 32x32 accumulators fed by
+// v_mfma_f32_32x32x16_bf16; fragment registers are double-buffered across the
+// 16-deep k-steps of a slice.
+#include "common.h"
+#include "launch.h"
+
+namespace gqa {
+namespace {
+
+// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
+// (lds is wave-uniform).  The builtin only exists for the device pass.
+__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+#endif
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // s_waitcnt: vmcnt = N (bits 3:0 and 15:14), expcnt 7 and lgkmcnt 15 = no wait
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until at most `later` slices (NLD loads each) of this wave are pending.
+template <int NLD, int L>
+__device__ __forceinline__ void wait_slices(int later) {
+  if constexpr (L <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (later >= L) wait_vmcnt<L * NLD>();
+    else wait_slices<NLD, L - 1>(later);
+  }
+}
+
+// Workgroup barrier that orders LDS accesses only (global loads stay in flight).
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ int seg_of(const GemmArgs& a, int64_t n) {
+  return n < a.seg_end[0] ? 0 : (n < a.seg_end[1] ? 1 : 2);
+}
+
+__device__ __forceinline__ float act_fn(int act, float g) {
+  return act == kActGeluTanh ? gelu_tanh(g) : silu(g);
+}
+
+// Global row pointer of B-tile row r (K offset k0) for tile column tn.  Gated
+// mode: each wave's WTN B rows are WTN/2 gate rows then the WTN/2 up rows of
+// the same output columns, so one lane holds both accumulators of a column.
+template <int MODE, int BN, int WTN>
+__device__ __forceinline__ const bf16* b_row_ptr(const GemmArgs& a, int tn, int r, int64_t k0) {
+  if (MODE == kModeGated) {
+    const int blk = r / WTN, w = r % WTN;
+    int col = tn * (BN / 2) + blk * (WTN / 2) + (w % (WTN / 2));
+    col = min(col, a.N - 1);
+    const bf16* base = static_cast<const bf16*>(w < WTN / 2 ? a.B[0] : a.B[1]);
+    return base + (int64_t)col * a.K + k0;
+  } else {
+    const int64_t n = min((int64_t)tn * BN + r, (int64_t)a.N - 1);
+    const int s = seg_of(a, n);
+    const int64_t start = s == 0 ? 0 : a.seg_end[s - 1];
+    return static_cast<const bf16*>(a.B[s]) + (n - start) * a.K + k0;
+  }
+}
+
+// MFMA shapes: MF = 32 -> v_mfma_f32_32x32x16_bf16 (16 accumulators per lane),
+// MF = 16 -> v_mfma_f32_16x16x32_bf16 (4 per lane).  The A/B operand of lane l
+// is 8 consecutive k of row l % MF, at k offset 8 * (l / MF) within the step.
+template <int MF> struct Mfma;
+template <> struct Mfma<32> {
+  typedef f32x16 acc_t;
+  static constexpr int KD = 16;  // k per instruction
+  __device__ static acc_t run(bf16x8 a, bf16x8 b, acc_t c) { return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0); }
+  // accumulator element e of lane l: row (e / 4) * 8 + (l / 32) * 4 + e % 4, column l % 32
+  __device__ static int row(int e, int lane) { return (e / 4) * 8 + (lane >> 5) * 4 + (e % 4); }
+};
+template <> struct Mfma<16> {
+  typedef f32x4 acc_t;
+  static constexpr int KD = 32;
+  __device__ static acc_t run(bf16x8 a, bf16x8 b, acc_t c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
+  // accumulator element e of lane l: row (l / 16) * 4 + e, column l % 16
+  __device__ static int row(int e, int lane) { return (lane >> 4) * 4 + e; }
+};
+
+// SCHED 0: fragments double-buffered, two reads of the next k-step after each
+//          of the first MFMAs of a step;
+// SCHED 1: B fragments double-buffered (read one or two per A row), each A
+//          fragment re-read for the next k-step as soon as its row of MFMAs
+//          has issued (fewer live registers, reads spread over the step).
+template <int BM, int BN, int BK, int ST, int WGM, int WGN, int MF, int SCHED, int MODE, int EPI>
+__global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) {
+  typedef Mfma<MF> MM;
+  typedef typename MM::acc_t acc_t;
+  constexpr int NACC = sizeof(acc_t) / sizeof(float);
+  constexpr int NW = WGM * WGN, NT = NW * 64;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int FM = WTM / MF, FN = WTN / MF;
+  constexpr int CPR = BK / 8;            // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;          // rows per load instruction
+  constexpr int RP = 128 / BK;           // rows per 256 bytes of LDS
+  constexpr int IA = BM / RPI / NW, IB = BN / RPI / NW;  // load instructions per wave per slice
+  constexpr int NLD = IA + IB;
+  constexpr int A_BYTES = BM * BK * 2, STAGE_BYTES = (BM + BN) * BK * 2;
+  constexpr int KS = BK / MM::KD;        // MFMA k-steps per slice
+  constexpr int CPF = MM::KD / 8;        // 16-byte chunks per fragment row per k-step
+  constexpr int BPR = (FN + FM - 1) / FM;  // SCHED 1: B reads per A row
+  static_assert(BK == 32 || BK == 64 || BK == 128, "slice depth");
+  static_assert(RP * CPR == 16, "swizzle period is 16 rows");
+  static_assert((BM / RPI) % NW == 0 && (BN / RPI) % NW == 0, "load instructions split evenly over waves");
+  static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must be a multiple of the MFMA size");
+  static_assert(MODE != kModeGated || FN % 2 == 0, "gated wave tiles hold gate and up halves");
+  static_assert(ST >= 2 && ST <= 6 && (ST - 1) * NLD < 64, "pipeline depth");
+  static_assert(KS % 2 == 0 || SCHED == 1, "fragment slots alternate across slices");
+  __shared__ __attribute__((aligned(1024))) char smem[ST * STAGE_BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+
+  if (a.bump && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = tid; i < a.bump_n; i += NT) a.bump[i] += a.bump_by;
+
+  // ---- tile order (order 0, the default): consecutive workgroup ids go
+  // round-robin to the 8 XCDs, so give each XCD a contiguous run of the tile
+  // order, then walk groups of GM M-tiles across N so tiles running together
+  // on an XCD share A and B panels in its L2.  Orders 1 (row-major, no remap)
+  // and 2 (groups of 4, no XCD remap) are kept for tuning. ----
+  const int cols_per_tile = MODE == kModeGated ? BN / 2 : BN;
+  const int tiles_m = (a.M + BM - 1) / BM;
+  const int tiles_n = (a.N + cols_per_tile - 1) / cols_per_tile;
+  const int total = gridDim.x;
+  int pid = blockIdx.x, tm, tn;
+  if (a.order == 1) {
+    tm = pid / tiles_n;
+    tn = pid % tiles_n;
+  } else {
+    if (a.order == 0 && total % 8 == 0) pid = (pid % 8) * (total / 8) + pid / 8;
+    const int GM = a.order == 3 ? 8 : 4;
+    const int group = pid / (GM * tiles_n);
+    const int first_m = group * GM;
+    const int gsize = min(tiles_m - first_m, GM);
+    const int rem = pid % (GM * tiles_n);
+    tm = first_m + rem % gsize;
+    tn = rem / gsize;
+  }
+  const int m0 = tm * BM;
+
+  const int64_t kbeg = (int64_t)blockIdx.y * a.k_split;
+  const int nk = (int)((min((int64_t)a.K, kbeg + a.k_split) - kbeg) / BK);
+
+  // ---- this lane's global source of every load instruction it issues ----
+  const int lrow = lane / CPR, lslot = lane % CPR;
+  const bf16* gA[IA];
+  const bf16* gB[IB];
+  {
+    const bf16* A = static_cast<const bf16*>(a.A);
+#pragma unroll
+    for (int j = 0; j < IA; ++j) {
+      const int r = (wave + NW * j) * RPI + lrow;
+      const int chunk = lslot ^ ((r / RP) % CPR);
+      const int m = min(m0 + r, a.M - 1);
+      gA[j] = A + (int64_t)m * a.lda + kbeg + chunk * 8;
+    }
+#pragma unroll
+    for (int j = 0; j < IB; ++j) {
+      const int r = (wave + NW * j) * RPI + lrow;
+      const int chunk = lslot ^ ((r / RP) % CPR);
+      gB[j] = b_row_ptr<MODE, BN, WTN>(a, tn, r, kbeg) + chunk * 8;
+    }
+  }
+  auto issue = [&](int kt, int stage) {
+    char* sA = smem + stage * STAGE_BYTES;
+    char* sB = sA + A_BYTES;
+#pragma unroll
+    for (int j = 0; j < IA; ++j)
+      load_lds16(gA[j] + (int64_t)kt * BK, sA + (wave + NW * j) * 1024);
+#pragma unroll
+    for (int j = 0; j < IB; ++j)
+      load_lds16(gB[j] + (int64_t)kt * BK, sB + (wave + NW * j) * 1024);
+  };
+
+  // ---- fragment addressing: row lane % MF of an MF-row block, chunk CPF ks + lane / MF ----
+  // (MF-row blocks start at multiples of 16 rows, so the XOR key is a function of lane % MF)
+  const int frow = lane % MF, fhi = lane / MF;
+  const int fsw = (frow / RP) % CPR;
+  const int a_off = (wm * WTM + frow) * (BK * 2);
+  const int b_off = A_BYTES + (wn * WTN + frow) * (BK * 2);
+  int koff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = ((CPF * ks + fhi) ^ fsw) * 16;
+
+  acc_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < NACC; ++e) acc[i][j][e] = 0.f;
+
+  // Fragment registers: see SCHED.  `cur` is the slot the MFMAs of a k-step
+  // read; the reads of the next k-step (possibly of the next slice) go to the
+  // other slot (SCHED 0) or, for A under SCHED 1, to slot 0 after its row.
+  bf16x8 fa[2][FM], fb[2][FN];
+  auto rd = [&](int stage, int ks, int slot, int r) {
+    const char* s = smem + stage * STAGE_BYTES + koff[ks];
+    if (r < FM) fa[slot][r] = *reinterpret_cast<const bf16x8*>(s + a_off + r * MF * (BK * 2));
+    else fb[slot][r - FM] = *reinterpret_cast<const bf16x8*>(s + b_off + (r - FM) * MF * (BK * 2));
+  };
+  auto step = [&](int cur, int stage, int ks) {
+    if constexpr (SCHED == 1) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          acc[i][j] = MM::run(fa[0][i], fb[cur][j], acc[i][j]);
+          if (j < BPR && i * BPR + j < FN) rd(stage, ks, cur ^ 1, FM + i * BPR + j);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        rd(stage, ks, 0, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < FM * FN; ++t) {
+        acc[t / FN][t % FN] = MM::run(fa[cur][t / FN], fb[cur][t % FN], acc[t / FN][t % FN]);
+#pragma unroll
+        for (int r = 2 * t; r < 2 * t + 2; ++r)
+          if (r < FM + FN) rd(stage, ks, cur ^ 1, r);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // ---- pipeline: all ST stages in flight from the start; a stage is refilled
+  // (ST slices ahead) as soon as every wave has read its last fragments ----
+#pragma unroll
+  for (int s = 0; s < ST; ++s)
+    if (s < nk) issue(s, s);
+  if (nk > 0) {
+    wait_slices<NLD, ST - 1>(min(ST - 1, nk - 1));
+    lds_sync();
+#pragma unroll
+    for (int r = 0; r < FM + FN; ++r) rd(0, 0, 0, r);
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    const int stage = kt % ST;
+#pragma unroll
+    for (int ks = 0; ks + 1 < KS; ++ks) step(ks & 1, stage, ks + 1);
+    if (kt + 1 < nk) {
+      // slice kt + 1 has landed once at most min(ST - 2, nk - 2 - kt) later slices are pending
+      wait_slices<NLD, ST - 2>(min(ST - 2, nk - 2 - kt));
+      lds_sync();  // publishes slice kt + 1; every wave is done reading stage `stage`
+      if (kt + ST < nk) issue(kt + ST, stage);
+    }
+    // (after the last slice these reads fetch an unused stage: harmless, and it
+    // keeps a single copy of the MFMA sequence in the loop)
+    step((KS - 1) & 1, (kt + 1) % ST, 0);
+  }
+
+  // ---- epilogue: accumulator element e of block (i, j) is row i * MF + MM::row(e, lane),
+  // B row / column j * MF + lane % MF of the wave tile ----
+  const int lcol = lane % MF;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int e = 0; e < NACC; ++e) {
+      const int m = m0 + wm * WTM + i * MF + MM::row(e, lane);
+      if (m >= a.M) continue;
+      if constexpr (EPI == kEpiGated) {
+#pragma unroll
+        for (int j = 0; j < FN / 2; ++j) {
+          const int n = tn * (BN / 2) + wn * (WTN / 2) + j * MF + lcol;
+          if (n < a.N) {
+            const float g = acc[i][j][e], u = acc[i][j + FN / 2][e];
+            static_cast<bf16*>(a.C)[(int64_t)m * a.ldc + n] = from_f32<bf16>(act_fn(a.act, g) * u);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int cb = wn * WTN + j * MF + lcol;  // B row within the tile
+          const float v = acc[i][j][e];
+          if (EPI == kEpiPartial) {
+            int64_t nb, NB;
+            if (MODE == kModeGated) {
+              const int blk = cb / WTN, w = cb % WTN;
+              const int col = tn * (BN / 2) + blk * (WTN / 2) + (w % (WTN / 2));
+              if (col >= a.N) continue;
+              nb = (w < WTN / 2 ? 0 : a.N) + col;
+              NB = 2 * (int64_t)a.N;
+            } else {
+              nb = (int64_t)tn * BN + cb;
+              if (nb >= a.N) continue;
+              NB = a.N;
+            }
+            a.partial[((int64_t)blockIdx.y * a.M + m) * NB + nb] = v;
+          } else {
+            const int64_t n = (int64_t)tn * BN + cb;
+            if (n >= a.N) continue;
+            if (EPI == kEpiResid) {
+              static_cast<float*>(a.C)[(int64_t)m * a.ldc + n] = a.resid[(int64_t)m * a.ldr + n] + v;
+            } else {  // kEpiStore
+              const int s = seg_of(a, n);
+              const float b = a.bias[s] ? a.bias[s][n - (s == 0 ? 0 : a.seg_end[s - 1])] : 0.f;
+              static_cast<bf16*>(a.C)[(int64_t)m * a.ldc + n] = from_f32<bf16>(v + b);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int BK, int ST, int WGM, int WGN, int MF, int SCHED, int MODE, int EPI>
+hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
+  if (a.k_split % BK != 0) return hipErrorInvalidValue;
+  const int cols = MODE == kModeGated ? BN / 2 : BN;
+  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + cols - 1) / cols);
+  hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, BK, ST, WGM, WGN, MF, SCHED, MODE, EPI>), dim3(tiles, a.splits),
+                     dim3(WGM * WGN * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int MODE, int EPI>
+hipError_t dispatch(const GemmArgs& a, int tile, hipStream_t s) {
+  switch (tile) {
+    case kTileDma256x256: return launch_cfg<256, 256, 64, 2, 2, 4, 16, 1, MODE, EPI>(a, s);
+    case kTileDma256x256n: return launch_cfg<256, 256, 64, 2, 4, 2, 16, 0, MODE, EPI>(a, s);
+    case kTileDma256x256m32: return launch_cfg<256, 256, 64, 2, 2, 4, 32, 0, MODE, EPI>(a, s);
+    case kTileDma256x192:
+      if constexpr (MODE == kModeGated) return hipErrorInvalidValue;
+      else return launch_cfg<256, 192, 64, 2, 4, 2, 16, 1, MODE, EPI>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool gemm_dma_tile(int tile) { return tile >= kTileDma256x256 && tile <= kTileDma256x192; }
+
+hipError_t launch_gemm_dma(const GemmArgs& a, int mode, int epi, int tile, hipStream_t s) {
+  if (mode == kModeGated) {
+    if (epi == kEpiGated) return dispatch<kModeGated, kEpiGated>(a, tile, s);
+    if (epi == kEpiPartial) return dispatch<kModeGated, kEpiPartial>(a, tile, s);
+    return hipErrorInvalidValue;
+  }
+  switch (epi) {
+    case kEpiStore: return dispatch<kModeSeg, kEpiStore>(a, tile, s);
+    case kEpiResid: return dispatch<kModeSeg, kEpiResid>(a, tile, s);
+    case kEpiPartial: return dispatch<kModeSeg, kEpiPartial>(a, tile, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gqa

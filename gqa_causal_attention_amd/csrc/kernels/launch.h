@@ -39,14 +39,24 @@ struct GemmArgs {
   int k_split;             // K elements per split (multiple of 64)
   int* bump;               // if non-null: bump[i] += bump_by for i < bump_n (once)
   int bump_n, bump_by;
+  int order;               // tile order of the pipelined kernel (0 = XCD-aware groups; others for tuning)
 };
 
 // Tile shapes of the bf16 MFMA GEMM.
 enum GemmTile { kTile256x256 = 0, kTile256x192 = 1, kTile64x128 = 2, kTile128x128 = 3, kTile256x256w4 = 4,
-                kTile64x64 = 5, kTileSkinny = 6 };
+                kTile64x64 = 5, kTileSkinny = 6,
+                // direct-to-LDS pipelined tiles: 64-deep slices, 2 stages, 8 waves
+                kTileDma256x256 = 7,      // waves 128x64, 16x16x32 MFMA, A re-read per row
+                kTileDma256x256n = 8,     // waves 64x128, 16x16x32 MFMA, double-buffered fragments
+                kTileDma256x256m32 = 9,   // waves 128x64, 32x32x16 MFMA, double-buffered fragments
+                kTileDma256x192 = 10,     // waves 64x96, 16x16x32 MFMA, A re-read per row
+};
 
-// kTileSkinny dispatches to launch_gemm_skinny.
+// kTileSkinny dispatches to launch_gemm_skinny, kTileDma* to launch_gemm_dma.
 hipError_t launch_gemm_bf16(const GemmArgs& a, int mode, int epi, int tile, hipStream_t s);
+// Direct-to-LDS pipelined GEMM for prefill-sized M (k_split a multiple of the slice depth).
+bool gemm_dma_tile(int tile);
+hipError_t launch_gemm_dma(const GemmArgs& a, int mode, int epi, int tile, hipStream_t s);
 // Weight-streaming GEMM for M <= 64 (decode); K split in multiples of 128.
 bool gemm_skinny_supported(int M, int N, int K, int k_split);
 hipError_t launch_gemm_skinny(const GemmArgs& a, int mode, int epi, hipStream_t s);
