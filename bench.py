@@ -1,6 +1,8 @@
 """Benchmark of the decoder block on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+    python bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration   (under rocprofv3 --pmc)
+    python bench.py --ingest-pmc FETCH_DIR WRITE_DIR                          (no GPU: writes profiles/)
 
 A step is one pass of the whole block over one batch of seeded synthetic
 input (random-init weights, no checkpoints):
@@ -12,6 +14,13 @@ input (random-init weights, no checkpoints):
     slots pre-filled to per-row positions drawn from [1024, 8192): step time
     (the step captured in a HIP graph and replayed; the eagerly launched time
     is reported beside it) and achieved HBM bandwidth.
+
+HBM traffic of the dominant kernel: two rocprofv3 --pmc runs (FETCH_SIZE,
+then WRITE_SIZE) of this script with --copy-calibration, which adds a plain
+1 GiB device copy; --ingest-pmc scales each counter by what it read for that
+copy and stores bytes per launch under profiles/ together with a hash of the
+kernel sources.  A normal run reports that figure as roofline.traffic while
+the hash still matches, else null.
 
 Inputs are resident in HBM before timing starts.  The timed region is K
 steps bracketed by device synchronisation; per-kernel durations come from
@@ -67,6 +76,88 @@ def decode_bytes(cfg, lengths, elem=2):
     return weights, kv_read, append, io
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_llama3_8b_prefill_4k_traffic.json")
+# sources that define the prefill gate/up GEMM launch
+GEMM_SOURCES = ["gqa_causal_attention_amd/csrc/kernels/gemm_dma.hip", "gqa_causal_attention_amd/csrc/kernels/gemm_bf16.hip",
+                "gqa_causal_attention_amd/csrc/kernels/common.h", "gqa_causal_attention_amd/csrc/kernels/launch.h",
+                "gqa_causal_attention_amd/csrc/host/block.cpp"]
+COPY_BYTES = 1 << 30          # the calibration copy: 1 GiB read + 1 GiB written
+
+
+def sources_hash(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per launch of the prefill gate/up GEMM from the committed
+    counter runs, or None when the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_hash") != sources_hash(GEMM_SOURCES):
+        return None
+    return rec
+
+
+def ingest_pmc(fetch_dir, write_dir):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
+    of `bench.py --copy-calibration` into bytes per gate/up launch, each counter
+    scaled by its reading for the 1 GiB calibration copy."""
+    import csv
+    import glob
+    import re
+
+    def rows(d, counter):
+        out = []
+        for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(fn) as f:
+                for r in csv.DictReader(f):
+                    if r["Counter_Name"] == counter:
+                        out.append((r["Kernel_Name"], float(r["Counter_Value"]), int(r["Grid_Size"])))
+        if not out:
+            raise SystemExit(f"no {counter} records under {d}")
+        return out
+
+    gu = re.compile(r"gemm_dma_kernel<256, 256, 64, 2, 2, 4, 16, 1, 1, 2>")
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rr = rows(d, counter)
+        g = [v for n, v, _ in rr if gu.search(n)]
+        c = [v for n, v, grid in rr if "copyBuffer" in n and grid >= 65536]
+        if not g or not c:
+            raise SystemExit(f"{counter}: gate/up dispatches {len(g)}, copy dispatches {len(c)}")
+        copy_kib = max(c)
+        scale = COPY_BYTES / (copy_kib * 1024.0)
+        res[counter] = {"kernel_kib_avg": sum(g) / len(g), "dispatches": len(g), "copy_kib": copy_kib,
+                        "scale": scale, "bytes": sum(g) / len(g) * 1024.0 * scale}
+    rec = {"kernel": "gemm_gate_up", "workload": "llama3_8b_prefill_4k",
+           "sources_hash": sources_hash(GEMM_SOURCES),
+           "fetch_bytes": round(res["FETCH_SIZE"]["bytes"]), "write_bytes": round(res["WRITE_SIZE"]["bytes"]),
+           "traffic_bytes": round(res["FETCH_SIZE"]["bytes"] + res["WRITE_SIZE"]["bytes"]),
+           "counters": res}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+def copy_calibration(torch):
+    """A plain device copy of known size for the counter runs to scale by."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[calibration] copied {COPY_BYTES} bytes 3 times")
+
+
 def bench_prefill(args, torch):
     from gqa_causal_attention_amd import Block
     from gqa_causal_attention_amd.workloads import make_workload
@@ -111,9 +202,11 @@ def bench_prefill(args, torch):
         log(f"   {k:16s} {v}")
     gu = breakdown["gemm_gate_up"]
     achieved = per_kernel_flops["gemm_gate_up"] / (gu["avg_ms"] * 1e-3) / 1e12
+    tr = stored_traffic()
     roofline = {"bound": "mfma", "kernel": "gemm_gate_up", "achieved": round(achieved, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None,
+                "traffic": tr["traffic_bytes"] if tr else None,
+                "algorithmic_bytes": 2 * (T * d + 2 * IT * d + T * IT),
                 "flops_per_launch": per_kernel_flops["gemm_gate_up"]}
     total_f = gemm_f + attn_f
     step_tflops = total_f / (ms * 1e-3) / 1e12
@@ -221,7 +314,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="decode line only (profiling); no JSON headline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (scale for the --pmc byte counters)")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs into the stored gate/up traffic record (no GPU)")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(*args.ingest_pmc)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the block runs on a single device); got --gpus {args.gpus}",
               file=sys.stderr)
@@ -236,6 +336,8 @@ def main():
         log(json.dumps({"decode_step_us": round(dec["us"], 2), "achieved_gbs": round(dec["gbs"], 1)}))
         return
     pre = bench_prefill(args, torch)
+    if args.copy_calibration:
+        copy_calibration(torch)
     dec = None if args.no_decode else bench_decode(args, torch)
     cpu = None
     if not args.no_cpu_baseline:
