@@ -12,7 +12,9 @@
 //  * One workgroup per (row b, kv head j, block of BQ query positions); its
 //    waves cover all G query heads of the group, so every K/V tile staged in
 //    LDS is read from HBM once for the whole group.  Blocks are issued
-//    longest-first (the causal triangle's last query blocks first).
+//    longest-first (the causal triangle's last query blocks first); for a
+//    small causal grid a workgroup takes the pair of blocks p and nqb-1-p,
+//    so all workgroups have equal work.
 //  * Each wave owns 32 query positions of one head.  Transposed products
 //    S^T = K Q^T and O^T += V^T P^T with v_mfma_f32_32x32x16_bf16: each lane
 //    then owns one query column, so softmax statistics are per-lane scalars,
@@ -33,6 +35,8 @@
 //    wave cannot see are skipped.
 #include "common.h"
 #include "launch.h"
+
+#include <cstdlib>
 
 namespace gqa {
 namespace {
@@ -65,7 +69,7 @@ __device__ __forceinline__ int vt_key(int g, int e) {
 }
 
 template <int HD, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void attn_prefill_kernel(AttnArgs a, int nqb) {
+__global__ __launch_bounds__(NW * 64, 1) void attn_prefill_kernel(AttnArgs a, int nqb, int paired) {
   using C = PrefillCfg<HD>;
   constexpr int NT = NW * 64, BKV = C::BKV, KS = C::KS, RT = C::RT;
   constexpr int KCH = (BKV * HD / 8 + NT - 1) / NT;    // 16-byte K chunks per thread
@@ -77,14 +81,20 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_kernel(AttnArgs a, in
   const int wph = NW / G;          // waves per head
   const int BQ = 32 * wph;         // query positions per workgroup
 
-  // longest query blocks first
+  // Query blocks: unpaired, one per workgroup, longest first; paired (causal,
+  // no window), workgroup p takes blocks nqb-1-p and p in turn, so every
+  // workgroup has the same number of key tiles.
   const int bkv = a.B * a.KV;
-  const int qb = nqb - 1 - (int)(blockIdx.x / bkv);
+  const int slot = (int)(blockIdx.x / bkv);
   const int bj = blockIdx.x % bkv;
   const int b = bj / a.KV, j = bj % a.KV;
   const int start = a.lengths ? a.lengths[b] : 0;
   const int L = a.L, W = a.window;
+  const int npass = paired && slot < nqb - 1 - slot ? 2 : 1;
 
+  for (int pass = 0; pass < npass; ++pass) {
+  if (pass > 0) __syncthreads();  // the previous block's last LDS reads are done
+  const int qb = pass == 0 ? nqb - 1 - slot : slot;
   const int q0 = qb * BQ;
   const int hh = w / wph, sub = w % wph;
   const int h = j * G + hh;
@@ -283,22 +293,23 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_kernel(AttnArgs a, in
   }
 
   // ---- normalise and write ctx[token, h*HD + d] ----
-  if (!wave_valid) return;
   const int tok = qt0 + (lane & 31);
   const float lt = l_run + xor32(l_run);
-  if (tok >= L) return;
-  const float inv = 1.0f / lt;
-  bf16* out = static_cast<bf16*>(a.ctx) + ((int64_t)b * L + tok) * ((int64_t)a.H * HD) + (int64_t)h * HD;
+  if (wave_valid && tok < L) {
+    const float inv = 1.0f / lt;
+    bf16* out = static_cast<bf16*>(a.ctx) + ((int64_t)b * L + tok) * ((int64_t)a.H * HD) + (int64_t)h * HD;
 #pragma unroll
-  for (int r = 0; r < RT; ++r)
+    for (int r = 0; r < RT; ++r)
 #pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      const int d = r * 32 + e4 * 8 + (lane >> 5) * 4;
-      bf16x4 v;
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int d = r * 32 + e4 * 8 + (lane >> 5) * 4;
+        bf16x4 v;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = from_f32<bf16>(o[r][e4 * 4 + e] * inv);
-      *reinterpret_cast<bf16x4*>(out + d) = v;
-    }
+        for (int e = 0; e < 4; ++e) v[e] = from_f32<bf16>(o[r][e4 * 4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(out + d) = v;
+      }
+  }
+  }  // pass
 }
 
 // Waves per workgroup for group size G: G heads x floor(8 / G) waves of 32
@@ -309,13 +320,27 @@ int waves_for(int hd, int G) {
   return G * (G >= 5 ? 1 : 8 / G);
 }
 
+// Pairing evens out the causal triangle when the grid is small; with many
+// workgroups (or a window, whose blocks have near-equal work) longest-first
+// ordering balances well by itself.  GQA_ATTN_PAIR=0/1 overrides (tuning).
+bool pair_blocks(const AttnArgs& a, int nqb) {
+  static const int forced = [] {
+    const char* e = getenv("GQA_ATTN_PAIR");
+    return e ? atoi(e) : -1;
+  }();
+  if (forced >= 0) return forced != 0 && a.window == 0;
+  return a.window == 0 && (int64_t)nqb * a.B * a.KV <= 4096;
+}
+
 template <int HD, int NW>
 hipError_t launch_hd_nw(const AttnArgs& a, hipStream_t s) {
   const int G = a.H / a.KV;
   const int BQ = 32 * (NW / G);
   const int nqb = (a.L + BQ - 1) / BQ;
-  dim3 grid((unsigned)(nqb * a.B * a.KV));
-  hipLaunchKernelGGL((attn_prefill_kernel<HD, NW>), grid, dim3(NW * 64), 0, s, a, nqb);
+  const int paired = pair_blocks(a, nqb) ? 1 : 0;
+  const int slots = paired ? (nqb + 1) / 2 : nqb;
+  dim3 grid((unsigned)(slots * a.B * a.KV));
+  hipLaunchKernelGGL((attn_prefill_kernel<HD, NW>), grid, dim3(NW * 64), 0, s, a, nqb, paired);
   return hipGetLastError();
 }
 
