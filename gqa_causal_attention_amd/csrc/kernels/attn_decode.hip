@@ -9,7 +9,7 @@
 // guide: 2 * H_kv * d_h bytes per token and layer), and this kernel reads each
 // cached key/value exactly once for all G query heads of its group.
 //
-// Work item = (row b, kv head j, split of 1024 keys).  A workgroup of 4
+// Work item = (row b, kv head j, split of 2048 keys).  A workgroup of 4
 // waves streams its split in sub-tiles of 128 keys, 32 per wave; each wave
 // issues all of its K and V loads for a sub-tile at once (16 KB in flight per
 // wave), full sub-tiles taking a short address path:
@@ -24,7 +24,8 @@
 // The four waves are merged once at the end.  It writes (output[hd], max,
 // sum) per (b, query head, split); the combine kernel merges a row's splits
 // in split order (deterministic).  Work items past a row's last split exit at
-// once (rows have different lengths).
+// once (rows have different lengths); the grid is split-major so that every
+// XCD gets its share of the long rows.
 #include "common.h"
 #include "launch.h"
 
@@ -35,8 +36,14 @@ constexpr int NT = 256;
 constexpr int NWV = NT / WAVE;
 constexpr int KPW = 32;                 // keys per wave per sub-tile (two 16-key MFMA blocks)
 constexpr int SUBK = KPW * NWV;         // keys per sub-tile (128)
-constexpr int NSUB = 8;                 // sub-tiles per split (1024 keys)
+constexpr int NSUB = 16;                // sub-tiles per split (2048 keys)
 constexpr float kSlack = 8.0f;          // lazy rescale threshold (log2 units)
+
+// 16 bytes of the cache, read once per step: a non-temporal load, so the
+// stream does not evict reused lines from L2 / Infinity Cache.
+__device__ __forceinline__ u32x4 stream_load(const bf16* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 
 template <int HD, int G>
 __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs a) {
@@ -49,8 +56,12 @@ __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs a) {
   __shared__ float wo[NWV][G][HD];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int split = blockIdx.x % a.max_chunks;
-  const int bj = blockIdx.x / a.max_chunks;
+  // Split-major order: consecutive workgroups are dispatched round-robin over
+  // the 8 XCDs, so a (row, kv head)-major order would pin split s to XCD
+  // s % 8 and leave the XCDs of the late (often empty) splits idle.
+  const int bkv = a.B * a.KV;
+  const int split = (int)(blockIdx.x / bkv);
+  const int bj = (int)(blockIdx.x % bkv);
   const int b = bj / a.KV, j = bj % a.KV;
   const int start = a.lengths ? a.lengths[b] : 0;
   const int p = start;                  // the new token's position (L = 1)
@@ -112,20 +123,20 @@ __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs a) {
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int s2 = 0; s2 < NK; ++s2)
-          kr[h2][s2] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)(k0 + 16 * h2 + kkey) * HD + kdim + 32 * s2);
+          kr[h2][s2] = stream_load(kbase + (int64_t)(k0 + 16 * h2 + kkey) * HD + kdim + 32 * s2);
 #pragma unroll
       for (int t = 0; t < NV; ++t)
-        vr[t] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)(k0 + t * RPV + vkey) * HD + vdim);
+        vr[t] = stream_load(vbase + (int64_t)(k0 + t * RPV + vkey) * HD + vdim);
     } else {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const bf16* kp = row(kfresh, kbase, k0 + 16 * h2 + kkey) + kdim;
 #pragma unroll
-        for (int s2 = 0; s2 < NK; ++s2) kr[h2][s2] = *reinterpret_cast<const u32x4*>(kp + 32 * s2);
+        for (int s2 = 0; s2 < NK; ++s2) kr[h2][s2] = stream_load(kp + 32 * s2);
       }
 #pragma unroll
       for (int t = 0; t < NV; ++t)
-        vr[t] = *reinterpret_cast<const u32x4*>(row(vfresh, vbase, k0 + t * RPV + vkey) + vdim);
+        vr[t] = stream_load(row(vfresh, vbase, k0 + t * RPV + vkey) + vdim);
     }
 
     // ---- scores: S^T[16 keys][16 heads] per block; lane holds keys 4(lane/16)+e ----
@@ -309,7 +320,7 @@ bool attention_decode_bf16_supported(int hd, int G) {
   return (hd == 64 || hd == 128 || hd == 256) && (G == 1 || G == 2 || G == 4 || G == 5 || G == 8);  // G <= 16
 }
 
-// Keys per split-K work item: 8 sub-tiles of 128 keys.
+// Keys per split-K work item: 16 sub-tiles of 128 keys.
 int attention_decode_chunk(int) { return NSUB * SUBK; }
 
 hipError_t launch_attention_decode_bf16(const AttnArgs& a, hipStream_t s) {

@@ -95,9 +95,11 @@ def test_bf16_decode_ragged_rows_prefilled_cache(torch_cuda):
     """Rows at different positions (one still empty), a cache pre-filled with
     N(0, 1) keys/values, several chunks of the split-K decode per row."""
     cfg, W = random_block(200, dtype="bf16", d_model=256, n_heads=8, n_kv_heads=2, head_dim=128,
-                          intermediate=256, max_positions=4096)
-    B, cap = 5, 2100
-    lengths = np.array([0, 1, 513, 2047, 700], dtype=np.int32)
+                          intermediate=256, max_positions=8192)
+    # 0 and 1 cached keys, a split boundary crossed during the steps (2047),
+    # three splits (4097) and one split with a ragged end (700)
+    B, cap = 5, 4400
+    lengths = np.array([0, 1, 2047, 4097, 700], dtype=np.int32)
     rng = np.random.default_rng(8)
     kf = round_bf16(rng.standard_normal((B, 2, cap, 128), dtype=np.float32))
     vf = round_bf16(rng.standard_normal((B, 2, cap, 128), dtype=np.float32))
