@@ -181,11 +181,10 @@ int big_tile_192() {
 }
 
 // Tile and K-split choice for a bf16 GEMM with M rows, N output columns, K
-// depth.  Large M: the wave count decides between 256x256 and 256x192 tiles
-// (gfx950 has 256 CUs).  Decode-sized M (<= 64): weight-streaming 64x64
-// tiles; K is split only while there are fewer than 256 tiles, and never
-// below 1024-deep splits, so the float32 partials stay a small fraction of
-// the weight bytes.
+// depth.  M > 512: the pipelined direct-to-LDS kernel, 256x256 or (when it
+// fills the 256 CUs better) 256x192 tiles.  129..512: 128x128 tiles.  65..128:
+// 64x128 tiles with a K split.  M <= 64 (decode): the weight-streaming kernel
+// (below), else 64x64 tiles split while there are fewer than 256 tiles.
 GemmPlan plan_gemm(int M, int N, int K, bool gated) {
   if (M > 128) {
     if (M <= 512) return {kTile128x128, 1};
@@ -206,12 +205,14 @@ GemmPlan plan_gemm(int M, int N, int K, bool gated) {
     return {kTile64x128, splits};
   }
   // M <= 64: the weight-streaming kernel (128 weight rows per workgroup).
-  // Split K (in halves, keeping 128-multiples) until there are about two
-  // workgroups per CU, but not below 512-deep splits: the float32 partials of
-  // a split cost M * 4 bytes per weight row against 2 * k_split weight bytes.
+  // Split K (in halves, keeping 128-multiples) only until there are about
+  // 192 workgroups (three quarters of the CUs), and not below 512-deep splits:
+  // a split's float32 partials cost M * 4 bytes per weight row (written and
+  // read back) against 2 * k_split weight bytes, and measured on the 8B decode
+  // shapes fewer, longer-running workgroups stream the weights faster.
   static const int target = [] {
     const char* e = getenv("GQA_SKINNY_TARGET");  // tuning override
-    return e ? atoi(e) : 512;
+    return e ? atoi(e) : 192;
   }();
   static const int kmin = [] {
     const char* e = getenv("GQA_SKINNY_KMIN");  // tuning override

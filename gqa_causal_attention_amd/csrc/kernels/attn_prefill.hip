@@ -19,20 +19,27 @@
 //    S^T = K Q^T and O^T += V^T P^T with v_mfma_f32_32x32x16_bf16: each lane
 //    then owns one query column, so softmax statistics are per-lane scalars,
 //    and the P^T operand of the second product is the lane's own S^T
-//    accumulator converted to bf16 — provided V^T's keys are stored in the
-//    same order, which the transposing LDS write arranges.
-//  * Q^T fragments live in registers; K tiles are [key][hd] and V^T tiles
-//    [hd][key] in LDS, padded rows, double-buffered (global -> registers ->
-//    LDS, one barrier per tile).  A tile is two 32-key sub-tiles whose score
-//    products are both issued before the first softmax, so the exponentials
-//    of one overlap the matrix work of the other.
+//    accumulator converted to bf16.  The MFMA's inner (key) index may be
+//    permuted freely as long as both operands agree, so V^T is fetched in the
+//    key order in which a lane's accumulator holds P^T.
+//  * K and V tiles of 64 keys stream from global memory straight into LDS
+//    (global_load_lds_dwordx4, no register staging), row-major as stored,
+//    double-buffered with one barrier per tile.  K fragments are plain
+//    16-byte reads; V^T fragments come from the transposing read
+//    ds_read_b64_tr_b16 (within a 16-lane group, lane i receives element i % 4
+//    of the 8-byte pieces addressed by lanes 4e + i / 4), 4 keys x 1 dim per
+//    lane per read.  Both tiles are XOR-swizzled on 16-byte chunks (chosen
+//    through the global address each lane fetches) so that the fragment reads
+//    of 16 consecutive rows, or the 8 rows x 64 bytes of a transposing read,
+//    spread over all LDS banks.
 //  * Softmax in float32 (dew CausalTransformer force_fp32_for_softmax) with
-//    base-2 exponentials; the scale is folded into one FMA.  The running
+//    base-2 exponentials; the scale is folded into one multiply.  The running
 //    reference max is raised lazily: the output is rescaled only when a
 //    column's max exceeds its reference by more than 2^8 (the weights stay
 //    <= 256, harmless in float32/bf16), which after the first tiles is rare.
-//  * Masks only on tiles that cross the diagonal or the window edge; tiles a
-//    wave cannot see are skipped.
+//    The softcap variant is a separate instantiation; masks are selects on
+//    tiles that cross the diagonal or the window edge only (wave-uniform
+//    tests), and tiles a wave cannot see are skipped.
 #include "common.h"
 #include "launch.h"
 
@@ -43,15 +50,53 @@ namespace {
 
 template <int HD>
 struct PrefillCfg {
-  static constexpr int BKV = 64;                    // keys per LDS tile (two 32-key sub-tiles)
-  static constexpr int KS = HD / 16;                // 16-deep MFMA steps over hd
-  static constexpr int RT = HD / 32;                // 32-row tiles of O^T
-  static constexpr int KLD = HD + 8;                // K tile row (bf16)
-  static constexpr int VLD = BKV + 8;               // V^T tile row (bf16)
-  static constexpr int STAGE = BKV * KLD + HD * VLD;
+  static constexpr int BKV = 64;                      // keys per LDS tile (two 32-key sub-tiles)
+  static constexpr int RB = HD * 2;                   // bytes per K / V row
+  static constexpr int CR = HD / 8;                   // 16-byte chunks per row
+  static constexpr int RP = RB >= 256 ? 1 : 256 / RB; // rows per 256 bytes of LDS
+  static constexpr int RPI = 1024 / RB;               // rows per load instruction (64 lanes x 16 B)
+  static constexpr int TILE = BKV * RB;               // bytes of a K (or V) tile
+  static constexpr int NI = TILE / 1024;              // load instructions per K (or V) tile
+  static constexpr int STAGE = 2 * TILE;              // K tile + V tile
+  static constexpr int KS = HD / 16;                  // 16-deep MFMA steps over hd
+  static constexpr int RT = HD / 32;                  // 32-row tiles of O^T
+  static constexpr int XK = CR < 16 ? CR : 16;        // XOR range of the swizzles
+  // K: 16 consecutive rows read one chunk each -> distinct bank groups
+  static __device__ __forceinline__ int kkey(int r) { return (r / RP) % XK; }
+  // V: a transposing read covers 8 rows x 4 chunks -> each bank group twice
+  static __device__ __forceinline__ int vkey(int r) { return 4 * ((r / RP) % (XK / 4)); }
 };
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units: lazily rescale beyond 2^8
+
+// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
+// (lds is wave-uniform).  The builtin only exists for the device pass.
+__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+#endif
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+#else
+  return s16x4{};
+#endif
+}
+
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// tanh(x) = 1 - 2 / (e^{2x} + 1) with the hardware reciprocal.
+__device__ __forceinline__ float tanh_rcp(float x) {
+  const float e = exp2_fast(2.0f * kLog2e * x);
+  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+}
 
 __device__ __forceinline__ const bf16* kv_row(const AttnArgs& a, const void* fresh, const void* cache, int b, int j,
                                              int start, int kp) {
@@ -61,22 +106,14 @@ __device__ __forceinline__ const bf16* kv_row(const AttnArgs& a, const void* fre
   return static_cast<const bf16*>(cache) + (((int64_t)b * a.KV + j) * a.cap + slot) * a.hd;
 }
 
-// Logical key (within a tile) of physical V^T slot e of 8-key chunk g: each
-// 16-key group is stored as keys [0..3, 8..11, 4..7, 12..15], the order in
-// which one lane's S^T accumulator holds them.
-__device__ __forceinline__ int vt_key(int g, int e) {
-  return (g >> 1) * 16 + (e < 4 ? (g & 1) * 4 + e : 8 + (g & 1) * 4 + (e - 4));
-}
-
-template <int HD, int NW>
+template <int HD, int NW, bool CAP>
 __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_kernel(AttnArgs a, int nqb, int paired) {
   using C = PrefillCfg<HD>;
-  constexpr int NT = NW * 64, BKV = C::BKV, KS = C::KS, RT = C::RT;
-  constexpr int KCH = (BKV * HD / 8 + NT - 1) / NT;    // 16-byte K chunks per thread
-  constexpr int VUN = (BKV * HD / 32 + NT - 1) / NT;   // (8 keys x 4 dims) V units per thread
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::STAGE];
+  constexpr int BKV = C::BKV, KS = C::KS, RT = C::RT, RB = C::RB;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index (scalar)
   const int G = a.H / a.KV;
   const int wph = NW / G;          // waves per head
   const int BQ = 32 * wph;         // query positions per workgroup
@@ -92,6 +129,20 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_kernel(AttnArgs a, in
   const int L = a.L, W = a.window;
   const int npass = paired && slot < nqb - 1 - slot ? 2 : 1;
 
+  // per-lane constants of the fragment reads
+  const int kfrag = (lane & 31) * RB + 16 * 0;                   // K row lane % 32 of a 32-key sub-tile
+  const int khi = lane >> 5;                                     // K chunk within a 16-deep step
+  const int kkey = C::kkey(lane & 31);
+  const int g16 = lane >> 4, i16 = lane & 15;                    // transposing reads: group, lane in group
+  const int vrow = 4 * (g16 >> 1) + (i16 >> 2);                  // V row (key) offset of this lane's piece
+  const int vdim = 16 * (g16 & 1) + 4 * (i16 & 3);               // V dim offset of this lane's piece
+  const int vkey = C::vkey(vrow);                                // (rows +8, +16, ... share the key)
+
+  const float scale = 1.0f / sqrtf((float)HD);
+  const float s_log2 = scale * kLog2e;           // no softcap: t = s * scale * log2e
+  const float cap_log2 = a.softcap * kLog2e;     // softcap: t = cap * log2e * tanh(s * scale / cap)
+  const float inv_cap = CAP ? scale / a.softcap : 0.f;
+
   for (int pass = 0; pass < npass; ++pass) {
   if (pass > 0) __syncthreads();  // the previous block's last LDS reads are done
   const int qb = pass == 0 ? nqb - 1 - slot : slot;
@@ -102,80 +153,33 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_kernel(AttnArgs a, in
   const int qp_lo = start + qt0;                     // its position
   const int qp_hi = start + min(qt0 + 32, L) - 1;    // last valid position of this wave
   const int my_qp = start + qt0 + (lane & 31);       // this lane's query position
+  const bool wave_valid = qt0 < L;
 
   const int blk_lo = start + q0, blk_hi = start + min(q0 + BQ, L) - 1;
   int klo = W > 0 ? max(0, blk_lo - W + 1) : 0;
   klo = klo / BKV * BKV;
-  const int khi = blk_hi + 1;
-  const int ntiles = (khi - klo + BKV - 1) / BKV;
+  const int kend = blk_hi + 1;
+  const int ntiles = (kend - klo + BKV - 1) / BKV;
 
   // ---- Q^T fragments: column = query token, 8 consecutive dims per lane ----
   bf16x8 qf[KS];
   {
     const int tok = min(qt0 + (lane & 31), L - 1);
-    const bf16* qr = static_cast<const bf16*>(a.q) + ((int64_t)b * L + tok) * a.ldq + (int64_t)h * HD +
-                     (lane >> 5) * 8;
+    const bf16* qr = static_cast<const bf16*>(a.q) + ((int64_t)b * L + tok) * a.ldq + (int64_t)h * HD + khi * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qr + ks * 16);
   }
 
-  // ---- staging of one K/V tile ----
-  u32x4 kreg[KCH];
-  u32x2 vreg[VUN][8];
-  auto gload = [&](int t) {
+  // ---- one K/V tile: C::NI load instructions each, spread over the waves ----
+  auto issue = [&](int t, int stage) {
     const int kb = klo + t * BKV;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * NT;
-      if (c < BKV * HD / 8) {
-        const int r = c / (HD / 8), ch = c % (HD / 8);
-        const int kp = min(kb + r, khi - 1);
-        kreg[i] = *reinterpret_cast<const u32x4*>(kv_row(a, a.knew, a.kcache, b, j, start, kp) + ch * 8);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VUN; ++i) {
-      const int u = tid + i * NT;
-      if (u < BKV * HD / 32) {
-        const int g = u % (BKV / 8), dg = u / (BKV / 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int kp = min(kb + vt_key(g, e), khi - 1);
-          vreg[i][e] = *reinterpret_cast<const u32x2*>(kv_row(a, a.vnew, a.vcache, b, j, start, kp) + dg * 4);
-        }
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
-    bf16* sK = smem + buf * C::STAGE;
-    bf16* sV = sK + BKV * C::KLD;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * NT;
-      if (c < BKV * HD / 8) {
-        const int r = c / (HD / 8), ch = c % (HD / 8);
-        *reinterpret_cast<u32x4*>(sK + r * C::KLD + ch * 8) = kreg[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VUN; ++i) {
-      const int u = tid + i * NT;
-      if (u < BKV * HD / 32) {
-        const int g = u % (BKV / 8), dg = u / (BKV / 8);
-        // vreg[i][e] holds dims 4dg..4dg+3 of key vt_key(g, e): transpose into 4 rows of V^T
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          u32x4 row;
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const uint32_t x0 = vreg[i][2 * e2][r / 2], x1 = vreg[i][2 * e2 + 1][r / 2];
-            const uint32_t h0 = (r & 1) ? (x0 >> 16) : (x0 & 0xffffu);
-            const uint32_t h1 = (r & 1) ? (x1 >> 16) : (x1 & 0xffffu);
-            row[e2] = h0 | (h1 << 16);
-          }
-          *reinterpret_cast<u32x4*>(sV + (dg * 4 + r) * C::VLD + g * 8) = row;
-        }
-      }
+    char* sK = smem + stage * C::STAGE;
+    char* sV = sK + C::TILE;
+    for (int i = w; i < C::NI; i += NW) {
+      const int r = i * C::RPI + lane / C::CR, sl = lane % C::CR;
+      const int kp = min(kb + r, kend - 1);
+      load_lds16(kv_row(a, a.knew, a.kcache, b, j, start, kp) + (sl ^ C::kkey(r)) * 8, sK + i * 1024);
+      load_lds16(kv_row(a, a.vnew, a.vcache, b, j, start, kp) + (sl ^ C::vkey(r)) * 8, sV + i * 1024);
     }
   };
 
@@ -188,33 +192,26 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_kernel(AttnArgs a, in
   float m_ref = -INFINITY;   // reference max (log2 units) the weights are taken against
   float l_run = 0.f;         // this lane's share of the softmax denominator
 
-  const float scale = 1.0f / sqrtf((float)HD);
-  const float cap = a.softcap;
-  const float s_log2 = scale * kLog2e;           // no softcap: t = s * scale * log2e
-  const float cap_log2 = cap * kLog2e;           // softcap: t = cap * log2e * tanh(s * scale / cap)
-  const float inv_cap = cap > 0.f ? scale / cap : 0.f;
-  const bool wave_valid = qt0 < L;
-
   // scores of one 32-key sub-tile: S^T[32 keys][32 queries]
-  auto qk = [&](const bf16* sK, int sb) {
+  auto qk = [&](const char* sK, int sb) {
     f32x16 s;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.f;
+    const char* base = sK + sb * 32 * RB + kfrag;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + (sb * 32 + (lane & 31)) * C::KLD + ks * 16 +
-                                                        (lane >> 5) * 8);
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(base + (((2 * ks + khi) ^ kkey) * 16));
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
     }
     return s;
   };
-  // softmax update for a sub-tile starting at key position k32; returns P^T (bf16) in s
+  // softmax update for a sub-tile starting at key position k32; leaves P^T in s
   auto softmax = [&](f32x16& s, int k32) {
     const bool need_mask = (k32 + 31 > qp_lo) || (W > 0 && k32 < qp_hi - W + 1);
     float mx = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      float v = cap > 0.f ? cap_log2 * tanh_exp(s[e] * inv_cap) : s[e] * s_log2;
+      float v = CAP ? cap_log2 * tanh_rcp(s[e] * inv_cap) : s[e] * s_log2;
       if (need_mask) {
         const int kp = k32 + (e / 4) * 8 + (lane >> 5) * 4 + (e % 4);
         const bool ok = kp <= my_qp && (W == 0 || kp > my_qp - W);
@@ -244,33 +241,39 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_kernel(AttnArgs a, in
     }
     l_run += ls;
   };
-  auto pv = [&](const bf16* sV, const f32x16& p, int sb) {
+  // O^T += V^T P^T for a sub-tile: 16-key step k16 uses the lane's P^T values
+  // 8 k16 .. 8 k16 + 7 (keys 16 k16 + {0..3, 8..11} + 4 (lane / 32)), so the
+  // V^T fragment takes the same keys: two transposing reads of 4 keys each.
+  auto pv = [&](const char* sV, const f32x16& p, int sb) {
 #pragma unroll
     for (int k16 = 0; k16 < 2; ++k16) {
       bf16x8 pf;
 #pragma unroll
       for (int e = 0; e < 8; ++e) pf[e] = from_f32<bf16>(p[k16 * 8 + e]);
+      const int row = sb * 32 + k16 * 16 + vrow;
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(sV + (r * 32 + (lane & 31)) * C::VLD + sb * 32 +
-                                                          k16 * 16 + (lane >> 5) * 8);
+        const int d = r * 32 + vdim;
+        const int off = ((d >> 3) ^ vkey) * 16 + (d & 7) * 2;
+        const s16x4 lo = lds_read_tr16(sV + row * RB + off);
+        const s16x4 hi = lds_read_tr16(sV + (row + 8) * RB + off);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[r], 0, 0, 0);
       }
     }
   };
 
-  if (ntiles > 0) {
-    gload(0);
-    sstore(0);
-  }
-  __syncthreads();
+  // ---- pipeline: tile t + 1 is in flight while tile t is multiplied ----
+  if (ntiles > 0) issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of tile 0 (and Q) are done
+  lds_sync();
+  if (ntiles > 1) issue(1, 1);
   for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) gload(t + 1);
-    const bf16* sK = smem + buf * C::STAGE;
-    const bf16* sV = sK + BKV * C::KLD;
+    const int stage = t & 1;
+    const char* sK = smem + stage * C::STAGE;
+    const char* sV = sK + C::TILE;
     const int kb = klo + t * BKV;
-    // which of the two sub-tiles this wave can see
+    // which of the two sub-tiles this wave can see (wave-uniform)
     bool use[2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
@@ -288,8 +291,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_kernel(AttnArgs a, in
       softmax(s1, kb + 32);
       pv(sV, s1, 1);
     }
-    if (t + 1 < ntiles) sstore(buf ^ 1);
-    __syncthreads();
+    if (t + 1 < ntiles) {
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of tile t + 1 are done
+      lds_sync();                          // ... everyone's; and stage t & 1 is free
+      if (t + 2 < ntiles) issue(t + 2, stage);
+    }
   }
 
   // ---- normalise and write ctx[token, h*HD + d] ----
@@ -340,7 +346,10 @@ hipError_t launch_hd_nw(const AttnArgs& a, hipStream_t s) {
   const int paired = pair_blocks(a, nqb) ? 1 : 0;
   const int slots = paired ? (nqb + 1) / 2 : nqb;
   dim3 grid((unsigned)(slots * a.B * a.KV));
-  hipLaunchKernelGGL((attn_prefill_kernel<HD, NW>), grid, dim3(NW * 64), 0, s, a, nqb, paired);
+  if (a.softcap > 0.f)
+    hipLaunchKernelGGL((attn_prefill_kernel<HD, NW, true>), grid, dim3(NW * 64), 0, s, a, nqb, paired);
+  else
+    hipLaunchKernelGGL((attn_prefill_kernel<HD, NW, false>), grid, dim3(NW * 64), 0, s, a, nqb, paired);
   return hipGetLastError();
 }
 
