@@ -9,6 +9,9 @@
 // float32 table indexed by the absolute position p = lengths[b] + t.  Lane i
 // holds pairs i, i + 64, ... so a pair never crosses lanes.
 //
+// bf16 blocks with head_dim 64 / 128 / 256 use the vector form (a thread per
+// 4 pairs); other shapes the wave-per-head form.
+//
 // Outputs: q rotated in place; this call's keys (rotated) and values into
 // knew/vnew [B, KV, L, hd]; and, with a cache, the same keys/values into
 // slot p (full cache) or p mod W (sliding-window ring, mojolearn
@@ -110,6 +113,88 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
   }
 }
 
+// Vector form for bf16 activations and head_dim 64 / 128 / 256: a thread
+// owns 4 consecutive pairs (p .. p+3, p+half .. p+half+3) of one head slot, so
+// every access is an 8-byte vector and a head is handled by half/4 adjacent
+// lanes (the qk-norm sum of squares is reduced across them with shuffles).
+template <int HD>
+__global__ __launch_bounds__(256) void rope_append_vec_kernel(RopeArgs a) {
+  constexpr int HALF = HD / 2, GH = HALF / 4;  // lanes per head slot
+  const int slots = a.H + 2 * a.KV;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t T_ = (int64_t)a.B * a.L;
+  const bool live = idx < T_ * slots * GH;
+  const int64_t hs = live ? idx / GH : 0;     // (token, slot)
+  const int g = (int)(idx % GH);
+  const int64_t tok = hs / slots;
+  const int slot = (int)(hs % slots);
+  const int b = (int)(tok / a.L), t = (int)(tok % a.L);
+  const int pos = (a.lengths ? a.lengths[b] : 0) + t;
+  const int QW = a.H * HD, KW = a.KV * HD;
+  bf16* row = static_cast<bf16*>(a.qkv) + tok * a.ld;
+  int kind, head;  // 0 = q, 1 = k, 2 = v
+  bf16* src;
+  if (slot < a.H) { kind = 0; head = slot; src = row + head * HD; }
+  else if (slot < a.H + a.KV) { kind = 1; head = slot - a.H; src = row + QW + head * HD; }
+  else { kind = 2; head = slot - a.H - a.KV; src = row + QW + KW + head * HD; }
+  const int p = 4 * g;
+
+  bf16x4 lo = bf16x4{}, hi = bf16x4{};
+  if (live) {
+    lo = *reinterpret_cast<const bf16x4*>(src + p);
+    hi = *reinterpret_cast<const bf16x4*>(src + p + HALF);
+  }
+  const int64_t new_off = (((int64_t)b * a.KV + head) * a.L + t) * HD;
+  const bool to_cache = a.kcache && !a.defer_append && (a.window == 0 || t >= a.L - a.window);
+  const int cslot = a.window > 0 ? pos % a.window : pos;
+  const int64_t cache_off = (((int64_t)b * a.KV + head) * a.cap + cslot) * HD;
+
+  if (kind != 2) {
+    float x1[4], x2[4];
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x1[e] = to_f32(lo[e]);
+      x2[e] = to_f32(hi[e]);
+      ss += x1[e] * x1[e] + x2[e] * x2[e];
+    }
+    const float* nw = kind == 0 ? a.q_norm : a.k_norm;
+    if (nw) {  // a head's GH lanes are adjacent and aligned: reduce within them
+#pragma unroll
+      for (int o = 1; o < GH; o <<= 1) ss += __shfl_xor(ss, o, WAVE);
+      const float r = 1.0f / sqrtf(ss / (float)HD + a.eps);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float g1 = a.offset ? 1.0f + nw[p + e] : nw[p + e];
+        const float g2 = a.offset ? 1.0f + nw[p + HALF + e] : nw[p + HALF + e];
+        x1[e] *= r * g1;
+        x2[e] *= r * g2;
+      }
+    }
+    const f32x4 c = *reinterpret_cast<const f32x4*>(a.cos_tab + (int64_t)pos * HALF + p);
+    const f32x4 s = *reinterpret_cast<const f32x4*>(a.sin_tab + (int64_t)pos * HALF + p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lo[e] = from_f32<bf16>(x1[e] * c[e] - x2[e] * s[e]);
+      hi[e] = from_f32<bf16>(x2[e] * c[e] + x1[e] * s[e]);
+    }
+  }
+  if (!live) return;
+  if (kind == 0) {
+    *reinterpret_cast<bf16x4*>(src + p) = lo;
+    *reinterpret_cast<bf16x4*>(src + p + HALF) = hi;
+    return;
+  }
+  bf16* dn = static_cast<bf16*>(kind == 1 ? a.knew : a.vnew) + new_off;
+  *reinterpret_cast<bf16x4*>(dn + p) = lo;
+  *reinterpret_cast<bf16x4*>(dn + p + HALF) = hi;
+  if (to_cache) {
+    bf16* dc = static_cast<bf16*>(kind == 1 ? a.kcache : a.vcache) + cache_off;
+    *reinterpret_cast<bf16x4*>(dc + p) = lo;
+    *reinterpret_cast<bf16x4*>(dc + p + HALF) = hi;
+  }
+}
+
 // Ring write of the call's keys/values (the deferred form of the append):
 // one thread per element of the last min(L, W) positions of each (row, head).
 template <typename T>
@@ -143,9 +228,21 @@ hipError_t launch_kv_append(const RopeArgs& a, int elem, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int HD>
+hipError_t launch_vec(const RopeArgs& a, hipStream_t s) {
+  const int64_t n = (int64_t)a.B * a.L * (a.H + 2 * a.KV) * (HD / 8);
+  hipLaunchKernelGGL(rope_append_vec_kernel<HD>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_rope_append(const RopeArgs& a, int elem, hipStream_t s) {
   const int64_t waves = (int64_t)a.B * a.L * (a.H + 2 * a.KV);
   if (waves == 0) return hipSuccess;
+  if (elem == kBF16 && a.ld % 4 == 0) {
+    if (a.hd == 64) return launch_vec<64>(a, s);
+    if (a.hd == 128) return launch_vec<128>(a, s);
+    if (a.hd == 256) return launch_vec<256>(a, s);
+  }
   dim3 grid((unsigned)((waves + 3) / 4));
   if (elem == kBF16)
     hipLaunchKernelGGL(rope_append_kernel<bf16>, grid, dim3(256), 0, s, a);
