@@ -285,7 +285,71 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
     step((KS - 1) & 1, (kt + 1) % ST, 0);
   }
 
-  // ---- epilogue: accumulator element e of block (i, j) is row i * MF + MM::row(e, lane),
+  // ---- epilogue through LDS (16x16 MFMA; residual and q/k/v epilogues): 64
+  // rows at a time the owning waves write their accumulators into a float32
+  // staging tile, then all threads read it back row-major and apply the
+  // epilogue with 16-byte loads and stores, whole rows per wave.  (The gated
+  // gate/up epilogue stays direct: its tiles are many per CU, so their
+  // stores overlap other tiles' main loops, and measured slower staged.) ----
+  if constexpr (MF == 16 && (EPI == kEpiResid || EPI == kEpiStore)) {
+    constexpr int COLS = MODE == kModeGated ? BN / 2 : BN;  // output columns of the tile
+    constexpr int SW = COLS + 4;                            // staging row stride (floats): 4 rows per
+                                                            // write land 16 banks apart
+    constexpr int PR = 64;                                  // rows per pass
+    static_assert(PR * SW * 4 <= ST * STAGE_BYTES, "staging tile fits in the pipeline's LDS");
+    static_assert(COLS % 4 == 0 && WTM % PR == 0 || PR % WTM == 0, "pass rows cover whole wave rows");
+    float* stg = reinterpret_cast<float*>(smem);
+    const int col0 = tn * COLS;
+#pragma unroll 1
+    for (int pass = 0; pass < BM / PR; ++pass) {
+      __syncthreads();  // the previous pass's reads (or the main loop's) are done
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int rb = wm * WTM + i * 16;  // first tile row of block i
+        if (rb / PR != pass) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = rb - pass * PR + MM::row(e, lane);
+          if constexpr (MODE == kModeGated) {
+#pragma unroll
+            for (int jj = 0; jj < FN / 2; ++jj)
+              stg[r * SW + wn * (WTN / 2) + jj * 16 + (lane & 15)] =
+                  act_fn(a.act, acc[i][jj][e]) * acc[i][jj + FN / 2][e];
+          } else {
+#pragma unroll
+            for (int jj = 0; jj < FN; ++jj) stg[r * SW + wn * WTN + jj * 16 + (lane & 15)] = acc[i][jj][e];
+          }
+        }
+      }
+      __syncthreads();
+      for (int idx = tid; idx < PR * (COLS / 4); idx += NT) {
+        const int r = idx / (COLS / 4), c = (idx % (COLS / 4)) * 4;
+        const int m = m0 + pass * PR + r;
+        const int n = col0 + c;
+        if (m >= a.M || n >= a.N) continue;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(stg + r * SW + c);
+        if constexpr (EPI == kEpiResid) {
+          const f32x4 rv = *reinterpret_cast<const f32x4*>(a.resid + (int64_t)m * a.ldr + n);
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.C) + (int64_t)m * a.ldc + n) = rv + v;
+        } else {
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float x = v[e];
+            if constexpr (EPI == kEpiStore) {
+              const int sg = seg_of(a, n + e);
+              if (a.bias[sg]) x += a.bias[sg][n + e - (sg == 0 ? 0 : a.seg_end[sg - 1])];
+            }
+            o[e] = from_f32<bf16>(x);
+          }
+          *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.C) + (int64_t)m * a.ldc + n) = o;
+        }
+      }
+    }
+    return;
+  }
+
+  // ---- direct epilogue: accumulator element e of block (i, j) is row i * MF + MM::row(e, lane),
   // B row / column j * MF + lane % MF of the wave tile ----
   const int lcol = lane % MF;
 #pragma unroll
