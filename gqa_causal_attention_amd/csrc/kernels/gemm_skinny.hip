@@ -4,26 +4,28 @@
 // TransformerBlock: q/k/v, o_proj, gate/up, down), where every weight byte is
 // used by at most 64 rows and the kernel is bound by streaming W from HBM.
 //
-// What bounds it is bytes in flight, not arithmetic: a CU must keep tens of KB
-// of weight loads outstanding to cover HBM latency.  So W never goes through
-// LDS: each lane loads its 16-byte weight chunks straight into registers in
-// the A-operand layout of v_mfma_f32_16x16x32_bf16 (lane l: weight row l%16,
-// k-slots 8*(l/16)..+7 of a 32-deep k-step), a whole 128-deep chunk ahead of
-// the MFMAs that consume it.  The activations are the part reused across
-// weight rows; a workgroup stages each 128-deep chunk of them once in LDS, in
-// B-operand fragment order (1 KB per 16 rows x 32 k, lane l at byte 16*l), so
-// every fragment read is one conflict-free ds_read_b128.
-//
-// Workgroup: 4 waves x 2 row groups x 16 weight rows = 128 weight rows (gated
-// mode: 64 output columns, each wave holding 16 gate rows and the 16 up rows
-// of the same columns so act(gate) * up is formed in-lane), over one K split.
+// What bounds it is streaming W at full HBM bandwidth, and two things hold
+// that back: partial-line loads, and waves waiting on each other (a
+// workgroup barrier per chunk holds every wave to the slowest one's HBM
+// latency).  So each wave streams its own 32 weight rows into a private ring
+// of 3 LDS stages with global_load_lds_dwordx4, two chunks ahead: one
+// instruction moves 4 rows x 256 bytes (a 128-deep chunk of each row, whole
+// lines), XOR-swizzled on 16-byte chunks (chunk c of row r at slot
+// c ^ (r % 16)) so the MFMA operand reads of 16 rows hit distinct banks.  A
+// wave waits only on its own weight loads.  The activations (at most 64 rows,
+// reused by every weight row) are shared: fetched the same way in B-operand
+// fragment order (1 KB per 16 rows x 32 k) a 256-deep super-chunk at a time,
+// double-buffered, with one barrier per super-chunk that waits only on
+// activation loads issued a chunk before the weights in flight.
 #include "common.h"
 #include "launch.h"
 
 namespace gqa {
 namespace {
 
-constexpr int SK_KX = 128;           // k per chunk (one LDS buffer)
+constexpr int SK_KX = 128;           // k per chunk
+constexpr int SK_SC = 2;             // chunks per super-chunk (one LDS activation buffer)
+constexpr int SK_WST = 3;            // weight ring stages per wave (two chunks in flight)
 constexpr int SK_KS = SK_KX / 32;    // MFMA k-steps per chunk
 constexpr int SK_NW = 4;             // waves per workgroup
 constexpr int SK_RG = 2;             // 16-row weight groups per wave
@@ -46,45 +48,83 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
+// (lds is wave-uniform).  The builtin only exists for the device pass.
+__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+#endif
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 template <int MT, int MODE, int EPI>
-__global__ __launch_bounds__(SK_NW * 64, 2) void gemm_skinny_kernel(GemmArgs a) {
-  constexpr int XF = MT * SK_KS;     // activation fragments per chunk
-  constexpr int XPW = XF / SK_NW;    // fragments each wave stages per chunk
-  static_assert(XF % SK_NW == 0, "activation fragments split evenly over the waves");
-  __shared__ bf16x8 xs[2][XF][64];
+__global__ __launch_bounds__(SK_NW * 64, 1) void gemm_skinny_kernel(GemmArgs a) {
+  constexpr int RB = SK_KX * 2;                  // bytes of a row's chunk (256)
+  constexpr int WROWS = SK_RG * 16;              // weight rows per wave (32)
+  constexpr int W_WAVE = WROWS * RB;             // a wave's weight chunk (8 KB)
+  constexpr int WI = W_WAVE / 1024;              // its load instructions per chunk (8)
+  constexpr int XF = MT * SK_KS;                 // activation fragments per chunk
+  constexpr int XS = SK_SC * XF;                 // per super-chunk
+  constexpr int XI = XS / SK_NW;                 // fragments each wave loads per super-chunk
+  static_assert(XS % SK_NW == 0, "activation fragments split evenly over the waves");
+  static_assert(SK_SC == 2 && SK_WST == 3, "the wait counts below assume these depths");
+  constexpr int W_RING = SK_NW * SK_WST * W_WAVE;
+  __shared__ __attribute__((aligned(1024))) char smem[W_RING + 2 * XS * 1024];
+  bf16x8 (*xs)[XS][64] = reinterpret_cast<bf16x8 (*)[XS][64]>(smem + W_RING);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int z = blockIdx.y;
   const int64_t kb = (int64_t)z * a.k_split;
   const int nchunks = a.k_split / SK_KX;
+  const int nsc = (nchunks + SK_SC - 1) / SK_SC;
+  char* ring = smem + wave * (SK_WST * W_WAVE);
 
   if (a.bump && blockIdx.x == 0 && blockIdx.y == 0)
     for (int i = threadIdx.x; i < a.bump_n; i += SK_NW * 64) a.bump[i] += a.bump_by;
 
-  // This lane's weight rows (one per row group), advanced to its k-slots.
-  const bf16* wp[SK_RG];
+  // ---- weights: load instruction jj moves the wave's rows 4jj .. 4jj+3 (lane l:
+  // row 4jj + l/16, 16-byte chunk (l % 16) ^ (row % 16)) ----
+  const bf16* gW[WI];
 #pragma unroll
-  for (int r = 0; r < SK_RG; ++r) {
-    if (MODE == kModeGated) {
-      const int col = min(blockIdx.x * (SK_ROWS / 2) + wave * 16 + lr, a.N - 1);
-      wp[r] = static_cast<const bf16*>(a.B[r]) + (int64_t)col * a.K;
+  for (int jj = 0; jj < WI; ++jj) {
+    const int wr = 4 * jj + (lane >> 4);         // row within the wave's 32
+    const bf16* row;
+    if (MODE == kModeGated) {                    // rows 0-15 gate, 16-31 up, same 16 columns
+      const int col = min(blockIdx.x * (SK_ROWS / 2) + wave * 16 + (wr & 15), a.N - 1);
+      row = static_cast<const bf16*>(a.B[wr >> 4]) + (int64_t)col * a.K;
     } else {
-      const int64_t n = min((int64_t)blockIdx.x * SK_ROWS + wave * (SK_RG * 16) + r * 16 + lr, (int64_t)a.N - 1);
-      const int s = seg_index(a, n);
-      wp[r] = static_cast<const bf16*>(a.B[s]) + (n - (s == 0 ? 0 : a.seg_end[s - 1])) * a.K;
+      const int64_t n = min((int64_t)blockIdx.x * SK_ROWS + wave * WROWS + wr, (int64_t)a.N - 1);
+      const int sg = seg_index(a, n);
+      row = static_cast<const bf16*>(a.B[sg]) + (n - (sg == 0 ? 0 : a.seg_end[sg - 1])) * a.K;
     }
-    wp[r] += kb + 8 * lg;
+    gW[jj] = row + kb + 8 * ((lane & 15) ^ (wr & 15));
   }
-  // The activation fragments this wave stages: f = wave * XPW + j holds k-step
-  // f / MT and rows 16 * (f % MT) + (0..15); rows past M repeat row M-1.
-  const bf16* xp[XPW];
+  auto issue_w = [&](int c) {
+    char* dst = ring + (c % SK_WST) * W_WAVE;
 #pragma unroll
-  for (int j = 0; j < XPW; ++j) {
-    const int f = wave * XPW + j;
-    const int m = min(16 * (f % MT) + lr, a.M - 1);
-    xp[j] = static_cast<const bf16*>(a.A) + (int64_t)m * a.lda + kb + 32 * (f / MT) + 8 * lg;
-  }
+    for (int jj = 0; jj < WI; ++jj) load_lds16(gW[jj] + (int64_t)c * SK_KX, dst + jj * 1024);
+  };
+  // ---- activations: fragment f of a super-chunk (k-step f / MT, rows 16 (f % MT)
+  // + (0..15), rows past M repeating row M-1) is one load instruction into a 1 KB
+  // slot in B-operand order; wave w loads fragments w XI .. w XI + XI - 1 ----
+  const bf16* xrow[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+    xrow[t] = static_cast<const bf16*>(a.A) + (int64_t)min(16 * t + lr, a.M - 1) * a.lda + kb + 8 * lg;
+  auto issue_x = [&](int sc) {
+#pragma unroll
+    for (int j = 0; j < XI; ++j) {
+      const int f = wave * XI + j;
+      const int kstep = min(sc * SK_SC * SK_KS + f / MT, nchunks * SK_KS - 1);  // past the end: never read
+      load_lds16(xrow[f % MT] + 32 * kstep, &xs[sc & 1][f][0]);
+    }
+  };
 
   f32x4 acc[SK_RG][MT];
 #pragma unroll
@@ -92,68 +132,54 @@ __global__ __launch_bounds__(SK_NW * 64, 2) void gemm_skinny_kernel(GemmArgs a) 
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  bf16x8 wb0[SK_KS][SK_RG], wb1[SK_KS][SK_RG], xst[XPW];
-  auto load_w = [&](bf16x8 (&w)[SK_KS][SK_RG], int c) {
+  // chunk c: weights from the wave's ring (row lr of each 16-row group, chunk
+  // 4 ks + lg, swizzled by lr), activations from super-chunk buffer (c / 2) & 1
+  auto compute = [&](int c) {
+    const char* sW = ring + (c % SK_WST) * W_WAVE + lr * RB;
+    const int buf = (c / SK_SC) & 1, cl = c % SK_SC;
 #pragma unroll
-    for (int s = 0; s < SK_KS; ++s)
+    for (int ks = 0; ks < SK_KS; ++ks) {
+      const int off = ((4 * ks + lg) ^ lr) * 16;
+      bf16x8 wf[SK_RG], xf[MT];
 #pragma unroll
-      for (int r = 0; r < SK_RG; ++r)
-        w[s][r] = *reinterpret_cast<const bf16x8*>(wp[r] + c * SK_KX + 32 * s);
-    // keep the prefetch ahead of the MFMAs that follow (the scheduler would
-    // otherwise sink the loads next to their first use)
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  auto load_x = [&](int c) {
+      for (int r = 0; r < SK_RG; ++r) wf[r] = *reinterpret_cast<const bf16x8*>(sW + r * 16 * RB + off);
 #pragma unroll
-    for (int j = 0; j < XPW; ++j) xst[j] = *reinterpret_cast<const bf16x8*>(xp[j] + c * SK_KX);
-  };
-  auto store_x = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < XPW; ++j) xs[buf][wave * XPW + j][lane] = xst[j];
-  };
-  auto compute = [&](const bf16x8 (&w)[SK_KS][SK_RG], int buf) {
-#pragma unroll
-    for (int s = 0; s < SK_KS; ++s) {
-      bf16x8 xf[MT];
-#pragma unroll
-      for (int t = 0; t < MT; ++t) xf[t] = xs[buf][s * MT + t][lane];
+      for (int t = 0; t < MT; ++t) xf[t] = xs[buf][(cl * SK_KS + ks) * MT + t][lane];
 #pragma unroll
       for (int r = 0; r < SK_RG; ++r)
 #pragma unroll
         for (int t = 0; t < MT; ++t)
-          acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[s][r], xf[t], acc[r][t], 0, 0, 0);
+          acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[r], xf[t], acc[r][t], 0, 0, 0);
     }
   };
 
-  // Two chunks per trip (registers wb0 / wb1, LDS buffers 0 / 1); every load
-  // in the loop body is unconditional so the wait before each compute only
-  // covers the chunk it consumes.
-  load_x(0);
-  load_w(wb0, 0);
-  store_x(0);
-  lds_barrier();
-  int c = 0;
-  for (; c + 2 < nchunks; c += 2) {
-    load_x(c + 1);
-    load_w(wb1, c + 1);
-    compute(wb0, 0);
-    store_x(1);
-    lds_barrier();
-    load_x(c + 2);
-    load_w(wb0, c + 2);
-    compute(wb1, 1);
-    store_x(0);
-    lds_barrier();
-  }
-  if (nchunks - c == 2) {
-    load_x(c + 1);
-    load_w(wb1, c + 1);
-    compute(wb0, 0);
-    store_x(1);
-    lds_barrier();
-    compute(wb1, 1);
-  } else {
-    compute(wb0, 0);
+  // ---- pipeline.  Issue order: x0 w0 w1 | x1 w2 | w3 | x2 w4 | w5 | ... (iteration
+  // c issues super-chunk c/2 + 1's activations when c is even, then chunk c + 2's
+  // weights).  Chunk c is ready once at most the later issues are pending:
+  // w(c+1), w(c+2) and x(c/2 + 1), whichever exist.  The one barrier per
+  // super-chunk waits only on activations issued before w(c), i.e. on loads
+  // that are normally long complete; the weight stream stays in flight. ----
+  issue_x(0);
+  issue_w(0);
+  if (nchunks > 1) issue_w(1);
+  for (int c = 0; c < nchunks; ++c) {
+    if (c % SK_SC == 0) {
+      // this super-chunk's activations: issued before w(c) (and w(c+1))
+      if (c + 1 < nchunks) wait_vmcnt<2 * WI>();
+      else wait_vmcnt<WI>();
+      lds_barrier();  // published; and every wave is done with the other buffer
+      if (c / SK_SC + 1 < nsc) issue_x(c / SK_SC + 1);
+    }
+    if (c + 2 < nchunks) issue_w(c + 2);  // into the slot chunk c - 1 used
+    // chunk c's weights
+    const int later = (c + 1 < nchunks ? WI : 0) + (c + 2 < nchunks ? WI : 0) + (c / SK_SC + 1 < nsc ? XI : 0);
+    if (later == 2 * WI + XI) wait_vmcnt<2 * WI + XI>();
+    else if (later == 2 * WI) wait_vmcnt<2 * WI>();
+    else if (later == WI + XI) wait_vmcnt<WI + XI>();
+    else if (later == WI) wait_vmcnt<WI>();
+    else if (later == XI) wait_vmcnt<XI>();
+    else wait_vmcnt<0>();
+    compute(c);
   }
 
   // Epilogue: acc[r][t] element e is weight row 4*lg + e of row group r and
