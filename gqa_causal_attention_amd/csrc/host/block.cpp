@@ -165,6 +165,14 @@ int big_tile() {
   }();
   return t;
 }
+// Keys per decode-attention segment (GQA_DECODE_SEG_KEYS overrides, tuning).
+int decode_keys_per_segment() {
+  static int k = [] {
+    const char* e = getenv("GQA_DECODE_SEG_KEYS");
+    return e && atoi(e) > 0 ? atoi(e) : 768;
+  }();
+  return k;
+}
 // Tile order of the pipelined GEMM (GQA_GEMM_ORDER overrides the XCD-aware
 // default for tuning).
 int gemm_tile_order() {
@@ -234,7 +242,6 @@ GemmPlan plan_gemm(int M, int N, int K, bool gated) {
 
 struct WsLayout {
   size_t h, qkv, knew, vnew, ctx, x1, h2, act, part, attn_part, total;
-  int max_chunks;
   GemmPlan p_qkv, p_o, p_gu, p_down;
   bool decode_attn;
 };
@@ -255,7 +262,6 @@ WsLayout layout_for(const gqa_block* blk, int B, int L) {
   w.h2 = take(T * d * es);
   w.act = take(T * IT * es);
   w.part = w.attn_part = 0;
-  w.max_chunks = 0;
   w.decode_attn = false;
   if (is_bf16(blk)) {
     const int M = (int)T;
@@ -272,17 +278,11 @@ WsLayout layout_for(const gqa_block* blk, int B, int L) {
     need(w.p_gu, 2 * (size_t)IT);
     need(w.p_down, d);
     if (part) w.part = take(part);
-    if (L == 1 && attention_decode_bf16_supported(c.head_dim, blk->G)) {
+    if (L == 1 && attention_decode_bf16_supported(c.head_dim, blk->G) && B <= attention_decode_max_rows()) {
       w.decode_attn = true;
-      const int span = c.window > 0 ? std::min(c.window, c.max_positions) : c.max_positions;
-      w.max_chunks = (span + attention_decode_chunk(c.head_dim) - 1) / attention_decode_chunk(c.head_dim);
-      if (w.max_chunks > 1024) {  // the combine merges at most 1024 chunks; longer caches use the flash path
-        w.decode_attn = false;
-        w.max_chunks = 0;
-      }
-    }
-    if (w.decode_attn) {
-      w.attn_part = take((size_t)B * c.n_heads * w.max_chunks * (c.head_dim + 2) * 4);
+      // records [H, max segments + B, hd + 2] floats, then the row table (2 ints per row)
+      w.attn_part = take((size_t)c.n_heads * (attention_decode_max_segments() + B) * (c.head_dim + 2) * 4 +
+                         (size_t)B * 2 * 4);
     }
   }
   w.total = off;
@@ -493,14 +493,15 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
     a.cap = st ? st->capacity : 0; a.window = c.window; a.softcap = c.attn_softcap;
     if (bf && lay.decode_attn) {
       a.part = reinterpret_cast<float*>(base + lay.attn_part);
-      a.max_chunks = lay.max_chunks;
-      a.chunk = attention_decode_chunk(hd);
-      // launch only as many chunks as the longest row needs
-      int maxlen = 0;
-      for (int b = 0; b < B; ++b) maxlen = std::max(maxlen, st ? st->lengths[b] : 0);
-      const int lo = c.window > 0 ? std::max(0, maxlen - c.window + 1) : 0;
-      const int need = (maxlen - lo + 1 + a.chunk - 1) / a.chunk;
-      a.max_chunks = std::min(lay.max_chunks, need);
+      // equal key segments over the rows' attended keys (host mirror of the
+      // lengths; the device recomputes the same split from its own copy)
+      int64_t total = 0;
+      for (int b = 0; b < B; ++b) {
+        const int p = st ? st->lengths[b] : 0;
+        total += p + 1 - (c.window > 0 ? std::max(0, p - c.window + 1) : 0);
+      }
+      a.nseg = attention_decode_segments(total, decode_keys_per_segment());
+      a.rec_stride = attention_decode_max_segments() + B;
       {
         Scope sc(tm, "attn_decode", s);
         HIP_TRY(launch_attention_decode_bf16(a, s));

@@ -9,8 +9,12 @@
 // guide: 2 * H_kv * d_h bytes per token and layer), and this kernel reads each
 // cached key/value exactly once for all G query heads of its group.
 //
-// Work item = (row b, kv head j, split of 2048 keys).  A workgroup of 4
-// waves streams its split in sub-tiles of 128 keys, 32 per wave; each wave
+// Work item = (segment s, kv head j).  The keys all rows attend are laid end
+// to end (row b's [klo_b, p_b] after row b-1's) and cut into nseg equal
+// contiguous segments, so every workgroup streams the same number of keys
+// whatever the mix of row lengths; a segment that spans a row boundary is
+// processed as one piece per row, each writing its own partial.  A workgroup
+// of 4 waves streams a piece in sub-tiles of 128 keys, 32 per wave; each wave
 // issues all of its K and V loads for a sub-tile at once (16 KB in flight per
 // wave), full sub-tiles taking a short address path:
 //  * scores on the matrix cores: S^T[16 keys][16 heads] = K Q^T with
@@ -21,11 +25,11 @@
 //    lazily, beyond 2^8), the weights handed through a 16 x G slab of LDS;
 //  * values on the vector ALUs: each lane owns 8 dims of one value row and
 //    accumulates G outputs with float32 FMAs.
-// The four waves are merged once at the end.  It writes (output[hd], max,
-// sum) per (b, query head, split); the combine kernel merges a row's splits
-// in split order (deterministic).  Work items past a row's last split exit at
-// once (rows have different lengths); the grid is split-major so that every
-// XCD gets its share of the long rows.
+// The four waves are merged once per piece.  A piece of row b in segment s
+// writes (output[hd], max, sum) per query head to record s + b (row b's
+// segments are consecutive, so rows never share a record); the combine kernel
+// merges a row's records in segment order (deterministic).  Cache loads are
+// non-temporal: the stream is read once per step.
 #include "common.h"
 #include "launch.h"
 
@@ -36,7 +40,8 @@ constexpr int NT = 256;
 constexpr int NWV = NT / WAVE;
 constexpr int KPW = 32;                 // keys per wave per sub-tile (two 16-key MFMA blocks)
 constexpr int SUBK = KPW * NWV;         // keys per sub-tile (128)
-constexpr int NSUB = 16;                // sub-tiles per split (2048 keys)
+constexpr int kMaxRows = 2048;          // rows whose key-count prefix fits the workgroup's LDS
+constexpr int kMaxSeg = 1024;           // segments per kv head (records per row the combine merges)
 constexpr float kSlack = 8.0f;          // lazy rescale threshold (log2 units)
 
 // 16 bytes of the cache, read once per step: a non-temporal load, so the
@@ -56,21 +61,64 @@ __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs a) {
   __shared__ float wo[NWV][G][HD];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  // Split-major order: consecutive workgroups are dispatched round-robin over
-  // the 8 XCDs, so a (row, kv head)-major order would pin split s to XCD
-  // s % 8 and leave the XCDs of the late (often empty) splits idle.
-  const int bkv = a.B * a.KV;
-  const int split = (int)(blockIdx.x / bkv);
-  const int bj = (int)(blockIdx.x % bkv);
-  const int b = bj / a.KV, j = bj % a.KV;
+  // ---- prefix of the key counts n_b = p_b + 1 - klo_b: pre[b] = sum over rows < b ----
+  __shared__ int pre[kMaxRows + 1];
+  const int W = a.window;
+  if (w == 0) {
+    int carry = 0;
+    if (lane == 0) pre[0] = 0;
+    for (int base = 0; base < a.B; base += WAVE) {
+      const int bb = base + lane;
+      int v = 0;
+      if (bb < a.B) {
+        const int pb = a.lengths ? a.lengths[bb] : 0;
+        v = pb + 1 - (W > 0 ? max(0, pb - W + 1) : 0);
+      }
+#pragma unroll
+      for (int o = 1; o < WAVE; o <<= 1) {
+        const int t = __shfl_up(v, o, WAVE);
+        if (lane >= o) v += t;
+      }
+      if (bb < a.B) pre[bb + 1] = carry + v;
+      carry += __shfl(v, WAVE - 1, WAVE);
+    }
+  }
+  __syncthreads();
+  const int j = (int)(blockIdx.x % a.KV), sgm = (int)(blockIdx.x / a.KV);
+  const int64_t total = pre[a.B];
+  // never more segments than keys (so none is empty): the combine uses the same count
+  const int nseg = (int)min((int64_t)a.nseg, total);
+  if (blockIdx.x == 0) {
+    // row table for the combine: row b's records are fs .. fs + n - 1 (+ b), where
+    // fs / ls are the segments of its first / last key (segment of key g: the
+    // last s with s * total / nseg <= g)
+    int* tab = reinterpret_cast<int*>(a.part + (int64_t)a.H * a.rec_stride * (HD + 2));
+    for (int bb = tid; bb < a.B; bb += NT) {
+      const int fs = (int)((((int64_t)pre[bb] + 1) * nseg - 1) / total);
+      const int ls = (int)((((int64_t)pre[bb + 1]) * nseg - 1) / total);
+      tab[2 * bb] = fs;
+      tab[2 * bb + 1] = ls - fs + 1;
+    }
+  }
+  if (sgm >= nseg) return;
+  const int64_t seg_lo = (int64_t)sgm * total / nseg, seg_hi = (int64_t)(sgm + 1) * total / nseg;
+  int b = 0;  // the row holding key seg_lo: the last b with pre[b] <= seg_lo
+  {
+    int lo = 0, hi = a.B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if (pre[mid] <= seg_lo) lo = mid;
+      else hi = mid - 1;
+    }
+    b = lo;
+  }
+  for (bool first_piece = true; b < a.B && pre[b] < seg_hi; ++b, first_piece = false) {
+  if (!first_piece) __syncthreads();  // the previous piece's LDS slabs have been read
   const int start = a.lengths ? a.lengths[b] : 0;
   const int p = start;                  // the new token's position (L = 1)
-  const int W = a.window;
   const int klo = W > 0 ? max(0, p - W + 1) : 0;
-  const int nsplit = (p - klo + 1 + a.chunk - 1) / a.chunk;
-  if (split >= nsplit) return;
-  const int ks0 = klo + split * a.chunk;
-  const int kend = min(ks0 + a.chunk, p + 1);
+  const int ks0 = klo + (int)(max(seg_lo, (int64_t)pre[b]) - pre[b]);
+  const int kend = klo + (int)(min(seg_hi, (int64_t)pre[b + 1]) - pre[b]);
   const int nsub = (kend - ks0 + SUBK - 1) / SUBK;
 
   const int64_t bjo = (int64_t)b * a.KV + j;
@@ -228,7 +276,7 @@ __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs a) {
       for (int e = 0; e < 8; ++e) wo[w][g][vdim + e] = o[g][e];
   }
   __syncthreads();
-  // partial record: [B, H, max_chunks, HD + 2] = (out[HD], max (base 2), sum)
+  // partial record of this piece: (out[HD], max (base 2), sum) per query head
   for (int i = tid; i < G * HD; i += NT) {
     const int g = i / HD, d = i % HD;
     float M = wm[0][g];
@@ -241,38 +289,37 @@ __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs a) {
       s2 += wo[ww][g][d] * f;
       ls += wl[ww][g] * f;
     }
-    float* rec = a.part + (((int64_t)b * a.H + j * G + g) * a.max_chunks + split) * (HD + 2);
+    float* rec = a.part + ((int64_t)(j * G + g) * a.rec_stride + sgm + b) * (HD + 2);
     rec[d] = s2;
     if (d == 0) {
       rec[HD] = M;
       rec[HD + 1] = ls;
     }
   }
+  }  // piece
 }
 
-// One workgroup per (row, query head): merge the row's chunks in chunk order.
+// One workgroup per (row, query head): merge the row's records in segment order.
 template <int HD>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  const int CH = a.chunk;
-  constexpr int DG = 256 / HD;          // chunk groups summed in parallel (2 for hd=128)
-  __shared__ float fw[1024];
+  constexpr int DG = 256 / HD;          // record groups summed in parallel (2 for hd=128)
+  __shared__ float fw[kMaxSeg];
   __shared__ float red[8];
   __shared__ float osum[DG][HD];
   const int tid = threadIdx.x;
   const int b = blockIdx.x / a.H, h = blockIdx.x % a.H;
-  const int p = a.lengths ? a.lengths[b] : 0;
-  const int klo = a.window > 0 ? max(0, p - a.window + 1) : 0;
-  const int nchunks = min((p - klo + 1 + CH - 1) / CH, min(a.max_chunks, 1024));
-  const float* rec = a.part + ((int64_t)b * a.H + h) * a.max_chunks * (HD + 2);
+  const int* tab = reinterpret_cast<const int*>(a.part + (int64_t)a.H * a.rec_stride * (HD + 2));
+  const int fs = tab[2 * b], nrec = tab[2 * b + 1];
+  const float* rec = a.part + ((int64_t)h * a.rec_stride + fs + b) * (HD + 2);
   float m = -INFINITY;
-  for (int c = tid; c < nchunks; c += 256) m = fmaxf(m, rec[c * (HD + 2) + HD]);
+  for (int c = tid; c < nrec; c += 256) m = fmaxf(m, rec[c * (HD + 2) + HD]);
   m = wave_max(m);
   if ((tid & 63) == 0) red[tid >> 6] = m;
   __syncthreads();
   const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
   float l = 0.f;
-  for (int c = tid; c < nchunks; c += 256) {
+  for (int c = tid; c < nrec; c += 256) {
     const float f = exp2_fast(rec[c * (HD + 2) + HD] - M);
     fw[c] = f;
     l += f * rec[c * (HD + 2) + HD + 1];
@@ -283,8 +330,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const float lsum = red[4] + red[5] + red[6] + red[7];
   const int d = tid % HD, cg = tid / HD;
   float o = 0.f;
-#pragma unroll 8
-  for (int c = cg; c < nchunks; c += DG) o = fmaf(fw[c], rec[c * (HD + 2) + d], o);
+#pragma unroll 4
+  for (int c = cg; c < nrec; c += DG) o = fmaf(fw[c], rec[c * (HD + 2) + d], o);
   osum[cg][d] = o;
   __syncthreads();
   if (tid < HD) {
@@ -297,7 +344,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 
 template <int HD, int G>
 hipError_t launch_hg(const AttnArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)((int64_t)a.B * a.KV * a.max_chunks));
+  dim3 grid((unsigned)((int64_t)a.nseg * a.KV));
   hipLaunchKernelGGL((attn_decode_kernel<HD, G>), grid, dim3(NT), 0, s, a);
   return hipGetLastError();
 }
@@ -320,11 +367,21 @@ bool attention_decode_bf16_supported(int hd, int G) {
   return (hd == 64 || hd == 128 || hd == 256) && (G == 1 || G == 2 || G == 4 || G == 5 || G == 8);  // G <= 16
 }
 
-// Keys per split-K work item: 16 sub-tiles of 128 keys.
-int attention_decode_chunk(int) { return NSUB * SUBK; }
+int attention_decode_max_rows() { return kMaxRows; }
+
+// Segments per kv head for `total` attended keys: about `keys_per_seg` keys
+// each, at most kMaxSeg, never more than the keys.
+int attention_decode_segments(int64_t total, int keys_per_seg) {
+  int64_t s = (total + keys_per_seg / 2) / keys_per_seg;
+  if (s > kMaxSeg) s = kMaxSeg;
+  if (s > total) s = total;
+  return s < 1 ? 1 : (int)s;
+}
+int attention_decode_max_segments() { return kMaxSeg; }
 
 hipError_t launch_attention_decode_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
+  if (a.B > kMaxRows || a.nseg < 1 || a.nseg > kMaxSeg || a.rec_stride < a.nseg + a.B) return hipErrorInvalidValue;
   switch (a.hd) {
     case 64: return launch_h<64>(a, s);
     case 128: return launch_h<128>(a, s);

@@ -98,8 +98,8 @@ struct AttnArgs {
   void* ctx;               // [T, H*hd]
   int B, L, H, KV, hd, cap, window;
   float softcap;           // 0 = off
-  float* part;             // decode split-K partials [B, H, max_chunks, hd + 2]
-  int chunk, max_chunks;
+  float* part;             // decode partials [H, rec_stride, hd + 2]: record s + b = row b's piece of segment s
+  int nseg, rec_stride;    // decode: key segments per kv head; records per head (>= nseg + B)
 };
 hipError_t launch_attention_generic(const AttnArgs& a, int elem, hipStream_t s);
 hipError_t launch_attention_prefill_bf16(const AttnArgs& a, hipStream_t s);
@@ -108,7 +108,9 @@ bool attention_prefill_bf16_supported(int hd, int G);
 hipError_t launch_attention_decode_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_decode_combine(const AttnArgs& a, hipStream_t s);
 bool attention_decode_bf16_supported(int hd, int G);
-int attention_decode_chunk(int hd);  // keys per split-K work item
+int attention_decode_max_rows();
+int attention_decode_max_segments();
+int attention_decode_segments(int64_t total_keys, int keys_per_seg);
 
 hipError_t launch_count_nonfinite(const void* p, int elem, int64_t n, int* flag, hipStream_t s);
 hipError_t launch_bump_lengths(int* lengths, int n, int by, hipStream_t s);
