@@ -9,7 +9,9 @@ input (random-init weights, no checkpoints):
 
   * headline: Llama-3-8B-shaped block prefill, B=1, L=4096, bf16 weights /
     float32 accumulation (a self-contained prefill, mojolearn forward with no
-    state): whole-block tokens/s and the share of the bf16 MFMA peak;
+    state): whole-block tokens/s and the share of the bf16 MFMA peak (the
+    prefill captured in a HIP graph and replayed; the eagerly launched time is
+    reported beside it);
   * decode: the same block shape, 64 rows one token each, KV cache of 8192
     slots pre-filled to per-row positions drawn from [1024, 8192): step time
     (the step captured in a HIP graph and replayed; the eagerly launched time
@@ -77,19 +79,26 @@ def decode_bytes(cfg, lengths, elem=2):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_llama3_8b_prefill_4k_traffic.json")
-# sources that define the prefill gate/up GEMM launch
-GEMM_SOURCES = ["gqa_causal_attention_amd/csrc/kernels/gemm_dma.hip", "gqa_causal_attention_amd/csrc/kernels/gemm_bf16.hip",
-                "gqa_causal_attention_amd/csrc/kernels/common.h", "gqa_causal_attention_amd/csrc/kernels/launch.h",
-                "gqa_causal_attention_amd/csrc/host/block.cpp"]
+# What defines the prefill gate/up GEMM launch: its kernel source, the device
+# helpers, the GemmArgs struct and the host's tile planning.
+GEMM_SOURCES = [("gqa_causal_attention_amd/csrc/kernels/gemm_dma.hip", None, None),
+                ("gqa_causal_attention_amd/csrc/kernels/common.h", None, None),
+                ("gqa_causal_attention_amd/csrc/kernels/launch.h", "struct GemmArgs {", "};"),
+                ("gqa_causal_attention_amd/csrc/host/block.cpp", "int big_tile() {", "struct WsLayout {")]
 COPY_BYTES = 1 << 30          # the calibration copy: 1 GiB read + 1 GiB written
 
 
-def sources_hash(paths):
+def sources_hash(parts):
+    """Hash of the listed files (or of the text between two markers in them)."""
     import hashlib
     h = hashlib.sha256()
-    for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+    for path, begin, end in parts:
+        with open(os.path.join(ROOT, path), "rb") as f:
+            data = f.read()
+        if begin is not None:
+            i = data.index(begin.encode())
+            data = data[i:data.index(end.encode(), i)]
+        h.update(data)
     return h.hexdigest()[:16]
 
 
@@ -180,7 +189,22 @@ def bench_prefill(args, torch):
     el = time.perf_counter() - t1
     times = blk.kernel_times()
     blk.set_timing(False)
-    ms = el * 1e3 / args.steps
+    ms_eager = el * 1e3 / args.steps
+    # The same prefill captured once in a HIP graph and replayed: the step
+    # without per-launch host overhead (workspace already allocated above).
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        blk.forward(x, out=y)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t1) * 1e3 / args.steps
+    log(f"[prefill] step {ms:.4f} ms replayed from a HIP graph, {ms_eager:.4f} ms launched eagerly")
     gemm_f, attn_f = prefill_flops(cfg, B, L)
     d, IT = cfg["d_model"], cfg["intermediate"]
     T = B * L
@@ -210,7 +234,7 @@ def bench_prefill(args, torch):
                 "flops_per_launch": per_kernel_flops["gemm_gate_up"]}
     total_f = gemm_f + attn_f
     step_tflops = total_f / (ms * 1e-3) / 1e12
-    return dict(cfg=cfg, B=B, L=L, ms=ms, tokens_per_s=T / (ms * 1e-3), roofline=roofline,
+    return dict(cfg=cfg, B=B, L=L, ms=ms, ms_eager=ms_eager, tokens_per_s=T / (ms * 1e-3), roofline=roofline,
                 step={"tflops": round(step_tflops, 1), "frac_of_peak": round(step_tflops / PEAK_BF16_TFLOPS, 4),
                       "algorithmic_tflop": round(total_f / 1e12, 4)},
                 breakdown=breakdown, wl=wl)
@@ -351,6 +375,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(pre["ms"], 4),
+        "ms_per_step_eager": round(pre["ms_eager"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

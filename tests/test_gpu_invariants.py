@@ -203,12 +203,39 @@ def test_decode_step_graph_replays_match_eager(torch_cuda):
     with torch.cuda.graph(graph):
         st.lengths.copy_(lengths_dev)
         blk.step(x, st, out=y)
+    other = _blk(cfg, W)  # unrelated eager work on its own workspace (the graph holds blk's)
     for i in range(4):
         y.zero_()
         graph.replay()
         torch.cuda.synchronize()
         np.testing.assert_array_equal(y.cpu().numpy(), ref.cpu().numpy())
         assert st.lengths.cpu().tolist() == (lengths + 1).tolist()
-        _ = blk.forward(to_gpu(rng.standard_normal((1, 8, 512), dtype=np.float32)))  # unrelated eager work
+        _ = other.forward(to_gpu(rng.standard_normal((1, 8, 512), dtype=np.float32)))
         torch.cuda.synchronize()
     assert torch.equal(st.v[:, :, :500], v0[:, :, :500])
+
+
+def test_prefill_graph_replays_match_eager(torch_cuda):
+    """A self-contained prefill on the large-M GEMM and flash paths (M > 512),
+    captured in a HIP graph: every replay equals the eager forward bit for bit,
+    with eager work and synchronisations between the replays."""
+    torch = torch_cuda
+    cfg, W = random_block(409, dtype="bf16", **LLAMA_SMALL)
+    blk = _blk(cfg, W)
+    rng = np.random.default_rng(12)
+    x = to_gpu(rng.standard_normal((1, 700, 512), dtype=np.float32))
+    y = torch.empty_like(x)
+    ref = blk.forward(x).clone()
+    blk.forward(x, out=y)  # workspace allocated before the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        blk.forward(x, out=y)
+    for i in range(3):
+        y.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(y.cpu().numpy(), ref.cpu().numpy())
+        # unrelated eager work (a smaller call: blk's captured workspace is kept)
+        _ = blk.forward(to_gpu(rng.standard_normal((2, 9, 512), dtype=np.float32)))
+        torch.cuda.synchronize()
