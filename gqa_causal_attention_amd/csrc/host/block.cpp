@@ -213,8 +213,8 @@ GemmPlan plan_gemm(int M, int N, int K, bool gated) {
     return {kTile64x128, splits};
   }
   // M <= 64: the weight-streaming kernel (128 weight rows per workgroup).
-  // Split K (in halves, keeping 128-multiples) only until there are about
-  // 192 workgroups (three quarters of the CUs), and not below 512-deep splits:
+  // Split K only until there are about 192 workgroups (three quarters of the
+  // CUs), and not below 512-deep splits:
   // a split's float32 partials cost M * 4 bytes per weight row (written and
   // read back) against 2 * k_split weight bytes, and measured on the 8B decode
   // shapes fewer, longer-running workgroups stream the weights faster.
@@ -227,10 +227,21 @@ GemmPlan plan_gemm(int M, int N, int K, bool gated) {
     return e ? atoi(e) : 512;
   }();
   if (gemm_skinny_supported(M, N, K, K)) {
+    // splits: the smallest divisor s of K / 256 (whole 256-deep super-chunks
+    // per split, at least kmin deep) that reaches the target, among depths
+    // that are multiples of 512 (the kernel's deeper weight ring) if any
     const long tiles = ((gated ? 2L * N : (long)N) + 127) / 128;
-    int splits = 1;
-    while (tiles * splits < target && K % (splits * 2 * 128) == 0 && K / (splits * 2) >= kmin) splits *= 2;
-    return {kTileSkinny, splits};
+    if (tiles >= target) return {kTileSkinny, 1};
+    const int units = K / 256;
+    int best = 1;
+    for (int pass = 0; pass < 2 && best == 1; ++pass)
+      for (int s = 2; s <= units; ++s) {
+        if (units % s != 0 || K / s < kmin) continue;
+        if (pass == 0 && (K / s) % 512 != 0) continue;
+        best = s;
+        if (tiles * s >= target) break;
+      }
+    return {kTileSkinny, best};
   }
   const int cols = gated ? 32 : 64;
   const long tiles = (N + cols - 1) / cols;

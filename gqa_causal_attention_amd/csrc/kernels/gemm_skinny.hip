@@ -4,32 +4,37 @@
 // TransformerBlock: q/k/v, o_proj, gate/up, down), where every weight byte is
 // used by at most 64 rows and the kernel is bound by streaming W from HBM.
 //
-// What bounds it is streaming W at full HBM bandwidth, and two things hold
-// that back: partial-line loads, and waves waiting on each other (a
-// workgroup barrier per chunk holds every wave to the slowest one's HBM
-// latency).  So each wave streams its own 32 weight rows into a private ring
-// of 3 LDS stages with global_load_lds_dwordx4, two chunks ahead: one
-// instruction moves 4 rows x 256 bytes (a 128-deep chunk of each row, whole
-// lines), XOR-swizzled on 16-byte chunks (chunk c of row r at slot
-// c ^ (r % 16)) so the MFMA operand reads of 16 rows hit distinct banks.  A
-// wave waits only on its own weight loads.  The activations (at most 64 rows,
-// reused by every weight row) are shared: fetched the same way in B-operand
-// fragment order (1 KB per 16 rows x 32 k) a 256-deep super-chunk at a time,
-// double-buffered, with one barrier per super-chunk that waits only on
-// activation loads issued a chunk before the weights in flight.
+// Streaming W at full HBM bandwidth is a question of how the loads are shaped
+// (measured on gfx950 with this kernel's geometry, 4 waves x 32 rows per
+// workgroup, M = 64): loads straight into LDS (global_load_lds) top out near
+// 3.5 TB/s; register loads in MFMA operand layout (each instruction 64 bytes of
+// 16 rows) near 4.3 TB/s; register loads that cover whole 256-byte row pieces
+// (each instruction 4 rows x 256 bytes) near 5.3 TB/s.  So each wave streams
+// its 32 weight rows in that whole-piece shape into a register ring of SK_D
+// 128-deep chunks, and when a chunk comes due writes it to a private LDS slab
+// (XOR-swizzled on 16-byte pieces) and reads it back in A-operand layout (lane
+// l: row l % 16 of a 16-row group, 8 consecutive k at 8 (l / 16) of each
+// 32-deep step); only the wave itself touches its slab, so no barrier is
+// involved.  The activations (at most 64 rows, reused by every weight row) are
+// shared through LDS in B-operand fragment order a 256-deep super-chunk at a
+// time, double-buffered: each thread loads its share of super-chunk s + 1
+// (whole row pieces again) into registers while super-chunk s is multiplied
+// and writes it to LDS before the one barrier per super-chunk.  That barrier
+// has no memory fence, so the weight loads stay in flight across it.
 #include "common.h"
 #include "launch.h"
 
 namespace gqa {
 namespace {
 
-constexpr int SK_KX = 128;           // k per chunk
+constexpr int SK_KX = 128;           // k per chunk (256 bytes of a row)
 constexpr int SK_SC = 2;             // chunks per super-chunk (one LDS activation buffer)
-constexpr int SK_WST = 3;            // weight ring stages per wave (two chunks in flight)
+constexpr int SK_D = 2;              // weight chunks in flight per wave (register ring)
 constexpr int SK_KS = SK_KX / 32;    // MFMA k-steps per chunk
 constexpr int SK_NW = 4;             // waves per workgroup
 constexpr int SK_RG = 2;             // 16-row weight groups per wave
 constexpr int SK_ROWS = SK_NW * SK_RG * 16;
+constexpr int SK_WI = SK_RG * 4;     // weight load instructions per wave per chunk (4 rows each)
 
 __device__ __forceinline__ float act_of(int act, float g) {
   return act == kActGeluTanh ? gelu_tanh(g) : silu(g);
@@ -39,63 +44,52 @@ __device__ __forceinline__ int seg_index(const GemmArgs& a, int64_t n) {
   return n < a.seg_end[0] ? 0 : (n < a.seg_end[1] ? 1 : 2);
 }
 
-// Workgroup-wide barrier for the LDS staging: the LDS writes are complete
-// (lgkmcnt 0) before the barrier; outstanding global loads stay in flight.
+// Workgroup-wide barrier that publishes this wave's LDS writes (lgkmcnt 0).  No
+// memory fence: a workgroup-scope release fence would also wait for every
+// outstanding global load (vmcnt 0) and drain the weight stream at each
+// barrier.  The empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(0xc07f);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  asm volatile("" ::: "memory");
 }
 
-// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
-// (lds is wave-uniform).  The builtin only exists for the device pass.
-__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-#endif
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+// 16-byte load through the global address space: a generic (flat) load would
+// count on both wait counters, and the compiler then waits for every
+// outstanding load (vmcnt 0) before using its result.
+__device__ __forceinline__ bf16x8 load_global16(const bf16* p) {
+  return *(const __attribute__((address_space(1))) bf16x8*)p;
 }
 
 template <int MT, int MODE, int EPI>
 __global__ __launch_bounds__(SK_NW * 64, 1) void gemm_skinny_kernel(GemmArgs a) {
-  constexpr int RB = SK_KX * 2;                  // bytes of a row's chunk (256)
   constexpr int WROWS = SK_RG * 16;              // weight rows per wave (32)
-  constexpr int W_WAVE = WROWS * RB;             // a wave's weight chunk (8 KB)
-  constexpr int WI = W_WAVE / 1024;              // its load instructions per chunk (8)
-  constexpr int XF = MT * SK_KS;                 // activation fragments per chunk
-  constexpr int XS = SK_SC * XF;                 // per super-chunk
-  constexpr int XI = XS / SK_NW;                 // fragments each wave loads per super-chunk
-  static_assert(XS % SK_NW == 0, "activation fragments split evenly over the waves");
-  static_assert(SK_SC == 2 && SK_WST == 3, "the wait counts below assume these depths");
-  constexpr int W_RING = SK_NW * SK_WST * W_WAVE;
-  __shared__ __attribute__((aligned(1024))) char smem[W_RING + 2 * XS * 1024];
-  bf16x8 (*xs)[XS][64] = reinterpret_cast<bf16x8 (*)[XS][64]>(smem + W_RING);
+  constexpr int XF = SK_SC * SK_KS * MT;         // activation fragments (1 KB each) per super-chunk
+  constexpr int XT = XF / SK_NW;                 // 16-byte activation pieces per thread per super-chunk
+  static_assert(XF % SK_NW == 0, "activation pieces split evenly over the threads");
+  __shared__ __attribute__((aligned(1024))) bf16x8 xs[2][XF][64];
+  __shared__ __attribute__((aligned(1024))) bf16x8 wslab[SK_NW][WROWS * 16];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int z = blockIdx.y;
   const int64_t kb = (int64_t)z * a.k_split;
   const int nchunks = a.k_split / SK_KX;
-  const int nsc = (nchunks + SK_SC - 1) / SK_SC;
-  char* ring = smem + wave * (SK_WST * W_WAVE);
 
   if (a.bump && blockIdx.x == 0 && blockIdx.y == 0)
     for (int i = threadIdx.x; i < a.bump_n; i += SK_NW * 64) a.bump[i] += a.bump_by;
 
-  // ---- weights: load instruction jj moves the wave's rows 4jj .. 4jj+3 (lane l:
-  // row 4jj + l/16, 16-byte chunk (l % 16) ^ (row % 16)) ----
-  const bf16* gW[WI];
+  // ---- weights: load instruction q moves rows 4 q .. 4 q + 3 of the wave's 32
+  // (rows 0-15 row group 0, 16-31 group 1), lane l: row 4 q + l / 16, 16-byte
+  // piece l % 16 of the chunk's 256 bytes ----
+  const bf16* wp[SK_WI];
 #pragma unroll
-  for (int jj = 0; jj < WI; ++jj) {
-    const int wr = 4 * jj + (lane >> 4);         // row within the wave's 32
+  for (int q = 0; q < SK_WI; ++q) {
+    const int wr = 4 * q + (lane >> 4);          // row within the wave's 32
     const bf16* row;
-    if (MODE == kModeGated) {                    // rows 0-15 gate, 16-31 up, same 16 columns
+    if (MODE == kModeGated) {                    // group 0 gate, group 1 up, same 16 columns
       const int col = min(blockIdx.x * (SK_ROWS / 2) + wave * 16 + (wr & 15), a.N - 1);
       row = static_cast<const bf16*>(a.B[wr >> 4]) + (int64_t)col * a.K;
     } else {
@@ -103,26 +97,38 @@ __global__ __launch_bounds__(SK_NW * 64, 1) void gemm_skinny_kernel(GemmArgs a) 
       const int sg = seg_index(a, n);
       row = static_cast<const bf16*>(a.B[sg]) + (n - (sg == 0 ? 0 : a.seg_end[sg - 1])) * a.K;
     }
-    gW[jj] = row + kb + 8 * ((lane & 15) ^ (wr & 15));
+    wp[q] = row + kb + 8 * (lane & 15);
   }
-  auto issue_w = [&](int c) {
-    char* dst = ring + (c % SK_WST) * W_WAVE;
+  bf16x8 wr[SK_D][SK_WI];
+  auto load_w = [&](int c, bf16x8 (&dst)[SK_WI]) {
 #pragma unroll
-    for (int jj = 0; jj < WI; ++jj) load_lds16(gW[jj] + (int64_t)c * SK_KX, dst + jj * 1024);
+    for (int q = 0; q < SK_WI; ++q)
+      dst[q] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(wp[q] + c * SK_KX));
   };
-  // ---- activations: fragment f of a super-chunk (k-step f / MT, rows 16 (f % MT)
-  // + (0..15), rows past M repeating row M-1) is one load instruction into a 1 KB
-  // slot in B-operand order; wave w loads fragments w XI .. w XI + XI - 1 ----
-  const bf16* xrow[MT];
+  // slab slot of (row r of the wave's 32, 16-byte piece p): r * 16 + (p ^ (r % 16))
+  bf16x8* slab = wslab[wave];
+
+  // ---- activations: a super-chunk is MT*16 rows x 256 k = 32 pieces of 16 bytes
+  // per row; this thread loads pieces tid + 256 i (row p / 32, piece p % 32;
+  // rows past M repeat row M-1) and stores piece kp of row m at fragment
+  // (kp / 4) * MT + m / 16, lane m % 16 + 16 (kp % 4) (B-operand order) ----
+  const bf16* xbase = static_cast<const bf16*>(a.A) + kb;
+  bf16x8 xr[XT];
+  auto load_x = [&](int sc) {
 #pragma unroll
-  for (int t = 0; t < MT; ++t)
-    xrow[t] = static_cast<const bf16*>(a.A) + (int64_t)min(16 * t + lr, a.M - 1) * a.lda + kb + 8 * lg;
-  auto issue_x = [&](int sc) {
+    for (int i = 0; i < XT; ++i) {
+      const int p = threadIdx.x + SK_NW * 64 * i;
+      const int m = min(p / 32, a.M - 1);
+      const int k = min(sc * (SK_SC * SK_KX) + (p % 32) * 8, a.k_split - 8);  // past the end: never read
+      xr[i] = load_global16(xbase + (int64_t)m * a.lda + k);
+    }
+  };
+  auto store_x = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < XI; ++j) {
-      const int f = wave * XI + j;
-      const int kstep = min(sc * SK_SC * SK_KS + f / MT, nchunks * SK_KS - 1);  // past the end: never read
-      load_lds16(xrow[f % MT] + 32 * kstep, &xs[sc & 1][f][0]);
+    for (int i = 0; i < XT; ++i) {
+      const int p = threadIdx.x + SK_NW * 64 * i;
+      const int m = p / 32, kp = p % 32;
+      xs[buf][(kp / 4) * MT + m / 16][(m % 16) + 16 * (kp % 4)] = xr[i];
     }
   };
 
@@ -132,17 +138,22 @@ __global__ __launch_bounds__(SK_NW * 64, 1) void gemm_skinny_kernel(GemmArgs a) 
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // chunk c: weights from the wave's ring (row lr of each 16-row group, chunk
-  // 4 ks + lg, swizzled by lr), activations from super-chunk buffer (c / 2) & 1
-  auto compute = [&](int c) {
-    const char* sW = ring + (c % SK_WST) * W_WAVE + lr * RB;
+  auto compute = [&](int c, const bf16x8 (&w)[SK_WI]) {
+    // the chunk through the wave's slab, from whole row pieces to A-operand layout
+#pragma unroll
+    for (int q = 0; q < SK_WI; ++q) {
+      const int r = 4 * q + (lane >> 4), p = lane & 15;
+      slab[r * 16 + (p ^ (r & 15))] = w[q];
+    }
     const int buf = (c / SK_SC) & 1, cl = c % SK_SC;
 #pragma unroll
     for (int ks = 0; ks < SK_KS; ++ks) {
-      const int off = ((4 * ks + lg) ^ lr) * 16;
       bf16x8 wf[SK_RG], xf[MT];
 #pragma unroll
-      for (int r = 0; r < SK_RG; ++r) wf[r] = *reinterpret_cast<const bf16x8*>(sW + r * 16 * RB + off);
+      for (int r = 0; r < SK_RG; ++r) {
+        const int row = 16 * r + lr;
+        wf[r] = slab[row * 16 + ((4 * ks + lg) ^ lr)];
+      }
 #pragma unroll
       for (int t = 0; t < MT; ++t) xf[t] = xs[buf][(cl * SK_KS + ks) * MT + t][lane];
 #pragma unroll
@@ -153,33 +164,41 @@ __global__ __launch_bounds__(SK_NW * 64, 1) void gemm_skinny_kernel(GemmArgs a) 
     }
   };
 
-  // ---- pipeline.  Issue order: x0 w0 w1 | x1 w2 | w3 | x2 w4 | w5 | ... (iteration
-  // c issues super-chunk c/2 + 1's activations when c is even, then chunk c + 2's
-  // weights).  Chunk c is ready once at most the later issues are pending:
-  // w(c+1), w(c+2) and x(c/2 + 1), whichever exist.  The one barrier per
-  // super-chunk waits only on activations issued before w(c), i.e. on loads
-  // that are normally long complete; the weight stream stays in flight. ----
-  issue_x(0);
-  issue_w(0);
-  if (nchunks > 1) issue_w(1);
-  for (int c = 0; c < nchunks; ++c) {
-    if (c % SK_SC == 0) {
-      // this super-chunk's activations: issued before w(c) (and w(c+1))
-      if (c + 1 < nchunks) wait_vmcnt<2 * WI>();
-      else wait_vmcnt<WI>();
-      lds_barrier();  // published; and every wave is done with the other buffer
-      if (c / SK_SC + 1 < nsc) issue_x(c / SK_SC + 1);
+  // ---- pipeline (nchunks is a multiple of SK_D = SK_SC).  Chunk c's weights
+  // are loaded SK_D chunks ahead into ring slot c % SK_D (the loop is unrolled
+  // by SK_D so the slots are registers).  Super-chunk s + 1's activations are
+  // loaded into registers while super-chunk s is multiplied and written to LDS
+  // buffer (s + 1) & 1 after it: that buffer was last read in super-chunk
+  // s - 1, which every wave finished before the barrier that closed it.  Every
+  // load is unconditional (indices clamp to the last chunk), and loads and
+  // stores of one activation super-chunk fall in one loop iteration, so the
+  // compiler's waits stay exact and never drain the weight stream. ----
+  static_assert(SK_D == SK_SC, "one activation super-chunk per loop iteration");
+  // (sched_barrier pins the issue order: the waits the compiler derives for
+  // the loop must hold for the prologue's order as well)
+  load_x(0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < SK_D; ++u) {
+    load_w(u, wr[u]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  store_x(0);
+  lds_barrier();
+  for (int c0 = 0; c0 < nchunks; c0 += SK_D) {
+    load_x(c0 / SK_SC + 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < SK_D; ++u) {
+      const int c = c0 + u;
+      compute(c, wr[u]);
+      load_w(min(c + SK_D, nchunks - 1), wr[u]);
+      // keep the issue order: the scheduler would otherwise sink these loads
+      // below the activation stores and the waits would cover them
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (c + 2 < nchunks) issue_w(c + 2);  // into the slot chunk c - 1 used
-    // chunk c's weights
-    const int later = (c + 1 < nchunks ? WI : 0) + (c + 2 < nchunks ? WI : 0) + (c / SK_SC + 1 < nsc ? XI : 0);
-    if (later == 2 * WI + XI) wait_vmcnt<2 * WI + XI>();
-    else if (later == 2 * WI) wait_vmcnt<2 * WI>();
-    else if (later == WI + XI) wait_vmcnt<WI + XI>();
-    else if (later == WI) wait_vmcnt<WI>();
-    else if (later == XI) wait_vmcnt<XI>();
-    else wait_vmcnt<0>();
-    compute(c);
+    store_x((c0 / SK_SC + 1) & 1);
+    lds_barrier();
   }
 
   // Epilogue: acc[r][t] element e is weight row 4*lg + e of row group r and
@@ -242,7 +261,8 @@ hipError_t launch_mt(const GemmArgs& a, hipStream_t s) {
 }  // namespace
 
 bool gemm_skinny_supported(int M, int N, int K, int k_split) {
-  return M >= 1 && M <= 64 && N % 4 == 0 && K % 8 == 0 && k_split >= SK_KX && k_split % SK_KX == 0;
+  // whole super-chunks (an even number of 128-deep chunks) per split
+  return M >= 1 && M <= 64 && N % 4 == 0 && K % 8 == 0 && k_split >= SK_SC * SK_KX && k_split % (SK_SC * SK_KX) == 0;
 }
 
 hipError_t launch_gemm_skinny(const GemmArgs& a, int mode, int epi, hipStream_t s) {

@@ -57,7 +57,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, int mode, int epi, int tile, hipS
 // Direct-to-LDS pipelined GEMM for prefill-sized M (k_split a multiple of the slice depth).
 bool gemm_dma_tile(int tile);
 hipError_t launch_gemm_dma(const GemmArgs& a, int mode, int epi, int tile, hipStream_t s);
-// Weight-streaming GEMM for M <= 64 (decode); K split in multiples of 128.
+// Weight-streaming GEMM for M <= 64 (decode); K split in multiples of 256.
 bool gemm_skinny_supported(int M, int N, int K, int k_split);
 hipError_t launch_gemm_skinny(const GemmArgs& a, int mode, int epi, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& a, int mode, int epi, hipStream_t s);

@@ -116,10 +116,11 @@ def test_bf16_decode_ragged_rows_prefilled_cache(torch_cuda):
 
 
 DECODE_GEMM_BLOCKS = {
-    # every projection K-split (k_split 512 or 640: even and odd 128-deep chunk counts)
+    # q/k/v, o_proj and gate/up K-split in two (512 deep: 4-chunk weight ring);
+    # down unsplit, 1280 deep (10 chunks: 2-chunk ring), fused residual
     "split": dict(d_model=1024, n_heads=8, n_kv_heads=2, head_dim=128, intermediate=1280, qkv_bias=True),
-    # no split: the fused bias / residual / gated epilogues (3 and 5 chunks)
-    "fused": dict(d_model=384, n_heads=6, n_kv_heads=2, head_dim=64, intermediate=640, qkv_bias=True,
+    # no split: the fused bias / residual / gated epilogues (4- and 6-chunk depths)
+    "fused": dict(d_model=512, n_heads=8, n_kv_heads=2, head_dim=64, intermediate=768, qkv_bias=True,
                   mlp="geglu_tanh"),
 }
 
