@@ -424,7 +424,10 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
   KernelTimer* tm = &blk->timer;
 
   // GEMM helper: fused epilogue, or K-split partials + ordered reduce.
-  auto gemm = [&](const char* name, GemmArgs a, int mode, int epi, const GemmPlan& p) -> int {
+  // (defer_reduce: leave the K-split partials in `part` for the next kernel,
+  // which sums them itself)
+  auto gemm = [&](const char* name, GemmArgs a, int mode, int epi, const GemmPlan& p,
+                  bool defer_reduce = false) -> int {
     a.order = gemm_tile_order();
     if (!bf) {
       Scope sc(tm, name, s);
@@ -447,6 +450,7 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
       Scope sc(tm, name, s);
       HIP_TRY(launch_gemm_bf16(pa, mode, kEpiPartial, p.tile, s));
     }
+    if (defer_reduce) return GQA_OK;
     a.splits = p.splits;
     a.partial = part;
     {
@@ -463,7 +467,9 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
     HIP_TRY(launch_rmsnorm(x, static_cast<const float*>(blk->w[W_IN_NORM]), h, et, T, d, c.norm_eps, offset,
                            blk->status, s));
   }
-  // 2. q/k/v projections (+ bias) in one GEMM over three weight segments
+  // 2. q/k/v projections (+ bias) in one GEMM over three weight segments (a
+  // K-split GEMM leaves its partials to the RoPE/append kernel when it can sum them)
+  const bool fuse_qkv = bf && lay.p_qkv.splits > 1 && rope_append_fuses_reduce(hd, QW + 2 * KW, et);
   {
     GemmArgs a{};
     a.A = h; a.lda = d;
@@ -474,7 +480,7 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
     a.bias[2] = static_cast<const float*>(blk->w[W_VB]);
     a.M = T; a.N = QW + 2 * KW; a.K = d;
     a.C = qkv; a.ldc = QW + 2 * KW;
-    if (int r = gemm("gemm_qkv", a, kModeSeg, kEpiStore, lay.p_qkv)) return r;
+    if (int r = gemm("gemm_qkv", a, kModeSeg, kEpiStore, lay.p_qkv, fuse_qkv)) return r;
   }
   // 3. q/k norm + RoPE; keys/values of this call to knew/vnew and into the cache
   // (a windowed call with L > 1 writes the ring after attention instead)
@@ -490,6 +496,13 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
     r.B = B; r.L = L; r.H = c.n_heads; r.KV = c.n_kv_heads; r.hd = hd;
     r.cap = st ? st->capacity : 0; r.window = c.window; r.offset = offset; r.eps = c.norm_eps;
     r.defer_append = st && c.window > 0 && L > 1;
+    if (fuse_qkv) {
+      r.part = part;
+      r.splits = lay.p_qkv.splits;
+      r.bias[0] = static_cast<const float*>(blk->w[W_QB]);
+      r.bias[1] = static_cast<const float*>(blk->w[W_KB]);
+      r.bias[2] = static_cast<const float*>(blk->w[W_VB]);
+    }
     Scope sc(tm, "rope_append", s);
     HIP_TRY(launch_rope_append(r, et, s));
   }
@@ -532,6 +545,7 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
     HIP_TRY(launch_kv_append(r, et, s));
   }
   // 5. o_proj + residual: x1 = x + ctx Wo^T (float32)
+  const bool fuse_o = bf && lay.p_o.splits > 1 && rmsnorm_fuses_reduce(d);
   {
     GemmArgs a{};
     a.A = ctx; a.lda = QW;
@@ -539,10 +553,14 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
     a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = d;
     a.M = T; a.N = d; a.K = QW;
     a.C = x1; a.ldc = d; a.resid = x; a.ldr = d;
-    if (int r = gemm("gemm_o", a, kModeSeg, kEpiResid, lay.p_o)) return r;
+    if (int r = gemm("gemm_o", a, kModeSeg, kEpiResid, lay.p_o, fuse_o)) return r;
   }
-  // 6. post-attention RMSNorm
-  {
+  // 6. post-attention RMSNorm (summing o_proj's K-split partials + x into x1 first when fused)
+  if (fuse_o) {
+    Scope sc(tm, "resid_rmsnorm", s);
+    HIP_TRY(launch_resid_rmsnorm(part, lay.p_o.splits, x, x1, static_cast<const float*>(blk->w[W_POST_NORM]), h2, et,
+                                 T, d, c.norm_eps, offset, s));
+  } else {
     Scope sc(tm, "rmsnorm", s);
     HIP_TRY(launch_rmsnorm(x1, static_cast<const float*>(blk->w[W_POST_NORM]), h2, et, T, d, c.norm_eps, offset,
                            nullptr, s));

@@ -67,6 +67,11 @@ hipError_t launch_splitk_reduce(const GemmArgs& a, int mode, int epi, int out_ty
 
 hipError_t launch_rmsnorm(const float* x, const float* w, void* out, int out_type, int rows, int d,
                           float eps, int offset, int* nonfinite_flag, hipStream_t s);
+// Fused K-split reduction + residual + RMSNorm: x1 = resid + sum over z < splits
+// of part[z, row, :] (written to x1, float32), then out = rmsnorm(x1).
+bool rmsnorm_fuses_reduce(int d);
+hipError_t launch_resid_rmsnorm(const float* part, int splits, const float* resid, float* x1, const float* w,
+                                void* out, int out_type, int rows, int d, float eps, int offset, hipStream_t s);
 
 struct RopeArgs {
   void* qkv;               // [T, ld] activations: q | k | v columns
@@ -83,7 +88,16 @@ struct RopeArgs {
   int B, L, H, KV, hd, cap, window, offset;
   int defer_append;        // 1: leave the cache to launch_kv_append (after attention)
   float eps;
+  // Optional fused K-split reduction of the q/k/v GEMM: if `part` is set, the
+  // q|k|v row is the sum over z < splits of part[z, token, :] (row stride ld)
+  // plus the per-segment bias, rounded to the activation type, and q is
+  // written (rotated) to qkv.  Only the vector form takes it.
+  const float* part;
+  int splits;
+  const float* bias[3];    // q, k, v biases (may be null)
 };
+// True if launch_rope_append takes `part` for this shape and element type.
+bool rope_append_fuses_reduce(int hd, int64_t ld, int elem);
 hipError_t launch_rope_append(const RopeArgs& a, int elem, hipStream_t s);
 hipError_t launch_kv_append(const RopeArgs& a, int elem, hipStream_t s);
 

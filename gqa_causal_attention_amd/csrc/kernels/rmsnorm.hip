@@ -6,7 +6,9 @@
 // once into registers (float4 loads), the sum of squares is reduced across the
 // wavefront with lane shuffles and across waves through LDS, and the scaled
 // row is written in the GEMM operand type.  The same pass flags non-finite
-// inputs (a plain store of 1 into a status word) at no extra bytes.
+// inputs (a plain store of 1 into a status word) at no extra bytes.  A
+// second entry point first forms the row as a residual plus the K-split
+// partial sums of the o_proj GEMM (fusing that GEMM's reduction).
 #include "common.h"
 #include "launch.h"
 
@@ -29,13 +31,34 @@ __device__ __forceinline__ void store4<bf16>(bf16* p, float a, float b, float c,
 }
 
 // Vector path: d % 4 == 0 and d <= NT * 4 * MAXV.
+// sum over z < splits of p[z * stride] (4 floats), in split order; the loads of
+// 8 splits are issued together (indices clamp, surplus terms are masked) so
+// their latencies overlap instead of forming a chain.
+__device__ __forceinline__ f32x4 sum_splits(const float* p, int64_t stride, int splits) {
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int z0 = 0; z0 < splits; z0 += 8) {
+    f32x4 t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] = *reinterpret_cast<const f32x4*>(p + min(z0 + u, splits - 1) * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (z0 + u < splits) acc += t[u];
+  }
+  return acc;
+}
+
+// With `part` set (the fused K-split reduction of the o_proj GEMM), the row is
+// x[row] + sum over z < splits of part[z, row, :] and is also stored to x1.
 template <typename OutT>
 __global__ __launch_bounds__(NT) void rmsnorm_vec_kernel(const float* __restrict__ x,
                                                         const float* __restrict__ w, OutT* __restrict__ out,
-                                                        int d, float eps, int offset, int* flag) {
+                                                        int d, float eps, int offset, int* flag,
+                                                        const float* __restrict__ part, int splits,
+                                                        float* __restrict__ x1) {
   __shared__ float red[NT / WAVE];
   const int64_t row = blockIdx.x;
   const float* xr = x + row * d;
+  const int64_t pstride = (int64_t)gridDim.x * d;
   f32x4 v[MAXV];
   float ss = 0.f;
   bool bad = false;
@@ -44,6 +67,7 @@ __global__ __launch_bounds__(NT) void rmsnorm_vec_kernel(const float* __restrict
     const int idx = (threadIdx.x + i * NT) * 4;
     if (idx < d) {
       v[i] = *reinterpret_cast<const f32x4*>(xr + idx);
+      if (part) v[i] += sum_splits(part + row * d + idx, pstride, splits);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         ss += v[i][e] * v[i][e];
@@ -58,6 +82,7 @@ __global__ __launch_bounds__(NT) void rmsnorm_vec_kernel(const float* __restrict
   for (int i = 0; i < MAXV; ++i) {
     const int idx = (threadIdx.x + i * NT) * 4;
     if (idx < d) {
+      if (part) *reinterpret_cast<f32x4*>(x1 + row * d + idx) = v[i];
       f32x4 g = *reinterpret_cast<const f32x4*>(w + idx);
       if (offset) g = g + 1.0f;
       store4<OutT>(o + idx, v[i][0] * r * g[0], v[i][1] * r * g[1], v[i][2] * r * g[2], v[i][3] * r * g[3]);
@@ -96,7 +121,7 @@ hipError_t launch_t(const float* x, const float* w, void* out, int rows, int d, 
   if (rows <= 0) return hipSuccess;
   if (d % 4 == 0 && d <= NT * 4 * MAXV)
     hipLaunchKernelGGL(rmsnorm_vec_kernel<OutT>, dim3(rows), dim3(NT), 0, s, x, w,
-                       static_cast<OutT*>(out), d, eps, offset, flag);
+                       static_cast<OutT*>(out), d, eps, offset, flag, nullptr, 0, nullptr);
   else
     hipLaunchKernelGGL(rmsnorm_any_kernel<OutT>, dim3(rows), dim3(NT), 0, s, x, w,
                        static_cast<OutT*>(out), d, eps, offset, flag);
@@ -109,6 +134,21 @@ hipError_t launch_rmsnorm(const float* x, const float* w, void* out, int out_typ
                           float eps, int offset, int* flag, hipStream_t s) {
   return out_type == kBF16 ? launch_t<bf16>(x, w, out, rows, d, eps, offset, flag, s)
                            : launch_t<float>(x, w, out, rows, d, eps, offset, flag, s);
+}
+
+bool rmsnorm_fuses_reduce(int d) { return d % 4 == 0 && d <= NT * 4 * MAXV; }
+
+hipError_t launch_resid_rmsnorm(const float* part, int splits, const float* resid, float* x1, const float* w,
+                                void* out, int out_type, int rows, int d, float eps, int offset, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (!rmsnorm_fuses_reduce(d) || splits < 1 || !part || !x1) return hipErrorInvalidValue;
+  if (out_type == kBF16)
+    hipLaunchKernelGGL(rmsnorm_vec_kernel<bf16>, dim3(rows), dim3(NT), 0, s, resid, w, static_cast<bf16*>(out), d,
+                       eps, offset, nullptr, part, splits, x1);
+  else
+    hipLaunchKernelGGL(rmsnorm_vec_kernel<float>, dim3(rows), dim3(NT), 0, s, resid, w, static_cast<float*>(out), d,
+                       eps, offset, nullptr, part, splits, x1);
+  return hipGetLastError();
 }
 
 }  // namespace gqa

@@ -140,7 +140,41 @@ __global__ __launch_bounds__(256) void rope_append_vec_kernel(RopeArgs a) {
   const int p = 4 * g;
 
   bf16x4 lo = bf16x4{}, hi = bf16x4{};
-  if (live) {
+  if (live && a.part) {
+    // fused K-split reduction: this row's columns c .. c+3 and c+HALF .. summed
+    // over the splits in order, plus the segment's bias, rounded as the GEMM
+    // epilogue would have stored them
+    const int64_t c = (src - row) + p;
+    const int64_t pstride = T_ * a.ld;
+    const float* pr = a.part + tok * a.ld + c;
+    f32x4 sl = f32x4{0.f, 0.f, 0.f, 0.f}, sh = sl;
+    for (int z0 = 0; z0 < a.splits; z0 += 4) {  // 4 splits' loads in flight together
+      f32x4 tl[4], th[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float* q = pr + min(z0 + u, a.splits - 1) * pstride;
+        tl[u] = *reinterpret_cast<const f32x4*>(q);
+        th[u] = *reinterpret_cast<const f32x4*>(q + HALF);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (z0 + u < a.splits) {
+          sl += tl[u];
+          sh += th[u];
+        }
+    }
+    const float* bias = a.bias[kind];
+    if (bias) {
+      const float* bb = bias + head * HD + p;
+      sl += *reinterpret_cast<const f32x4*>(bb);
+      sh += *reinterpret_cast<const f32x4*>(bb + HALF);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lo[e] = from_f32<bf16>(sl[e]);
+      hi[e] = from_f32<bf16>(sh[e]);
+    }
+  } else if (live) {
     lo = *reinterpret_cast<const bf16x4*>(src + p);
     hi = *reinterpret_cast<const bf16x4*>(src + p + HALF);
   }
@@ -180,7 +214,7 @@ __global__ __launch_bounds__(256) void rope_append_vec_kernel(RopeArgs a) {
     }
   }
   if (!live) return;
-  if (kind == 0) {
+  if (kind == 0) {  // q, rotated (in place, or from the fused reduction)
     *reinterpret_cast<bf16x4*>(src + p) = lo;
     *reinterpret_cast<bf16x4*>(src + p + HALF) = hi;
     return;
@@ -235,9 +269,14 @@ hipError_t launch_vec(const RopeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+bool rope_append_fuses_reduce(int hd, int64_t ld, int elem) {
+  return elem == kBF16 && ld % 4 == 0 && (hd == 64 || hd == 128 || hd == 256);
+}
+
 hipError_t launch_rope_append(const RopeArgs& a, int elem, hipStream_t s) {
   const int64_t waves = (int64_t)a.B * a.L * (a.H + 2 * a.KV);
   if (waves == 0) return hipSuccess;
+  if (a.part && (!rope_append_fuses_reduce(a.hd, a.ld, elem) || a.splits < 1)) return hipErrorInvalidValue;
   if (elem == kBF16 && a.ld % 4 == 0) {
     if (a.hd == 64) return launch_vec<64>(a, s);
     if (a.hd == 128) return launch_vec<128>(a, s);
