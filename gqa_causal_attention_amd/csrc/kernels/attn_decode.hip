@@ -16,11 +16,15 @@
 // processed as one piece per row, each writing its own partial.  A workgroup
 // of 4 waves streams a piece in sub-tiles of 128 keys, 32 per wave; each wave
 // issues all of its K and V loads for a sub-tile at once (16 KB in flight per
-// wave), full sub-tiles taking a short address path:
+// wave at hd 128), every load instruction covering whole 256-byte row pieces
+// (measured on gfx950, whole-piece loads stream faster than loads shaped as
+// MFMA operands, which cover 64 bytes of each of 16 rows); full sub-tiles
+// take a short address path:
 //  * scores on the matrix cores: S^T[16 keys][16 heads] = K Q^T with
-//    v_mfma_f32_16x16x32_bf16, K read straight from HBM in the operand layout
-//    (lane -> key lane%16, 16-byte dim pieces), Q^T resident in registers
-//    (heads past G are zero columns) — no conversions, no cross-lane sums;
+//    v_mfma_f32_16x16x32_bf16, K passed through a per-wave LDS slab into the
+//    operand layout (lane -> key lane%16, 16-byte dim pieces), Q^T resident
+//    in registers (heads past G are zero columns) — no conversions, no
+//    cross-lane sums;
 //  * per-wave online softmax in float32 (base 2; the reference max is raised
 //    lazily, beyond 2^8), the weights handed through a 16 x G slab of LDS;
 //  * values on the vector ALUs: each lane owns 8 dims of one value row and
@@ -38,8 +42,6 @@ namespace {
 
 constexpr int NT = 256;
 constexpr int NWV = NT / WAVE;
-constexpr int KPW = 32;                 // keys per wave per sub-tile (two 16-key MFMA blocks)
-constexpr int SUBK = KPW * NWV;         // keys per sub-tile (128)
 constexpr int kMaxRows = 2048;          // rows whose key-count prefix fits the workgroup's LDS
 constexpr int kMaxSeg = 1024;           // segments per kv head (records per row the combine merges)
 constexpr float kSlack = 8.0f;          // lazy rescale threshold (log2 units)
@@ -52,6 +54,9 @@ __device__ __forceinline__ u32x4 stream_load(const bf16* p) {
 
 template <int HD, int G>
 __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs a) {
+  constexpr int KPW = 32;               // keys per wave per sub-tile (16 KB of K and V at hd 128)
+  constexpr int NKB = KPW / 16;         // 16-key MFMA blocks per wave per sub-tile
+  constexpr int SUBK = KPW * NWV;       // keys per sub-tile
   constexpr int NK = HD / 32;           // 16-byte K pieces per lane per 16-key block (= MFMA k-steps)
   constexpr int LPR = HD / 8;           // lanes per V row
   constexpr int RPV = WAVE / LPR;       // V rows per wave load
@@ -59,6 +64,7 @@ __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs a) {
   __shared__ float sp[NWV][KPW][G];     // this sub-tile's weights, per wave
   __shared__ float wm[NWV][G], wl[NWV][G];
   __shared__ float wo[NWV][G][HD];
+  __shared__ u32x4 kslab[NWV][KPW * HD / 8];  // each wave's K sub-tile, swizzled 16-byte pieces
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   // ---- prefix of the key counts n_b = p_b + 1 - klo_b: pre[b] = sum over rows < b ----
@@ -162,43 +168,57 @@ __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[g][e] = 0.f;
 
-  for (int n = 0; n < nsub; ++n) {
+  // ---- loads of sub-tile n: all of this wave's K and V at once, each load
+  // instruction covering whole 256-byte row pieces (K: keys k0 + 4i + l / 16,
+  // 16-byte piece l % 16; V: rows t * RPV + l / LPR, piece l % LPR) ----
+  constexpr int KI = KPW * HD * 2 / 1024;           // K load instructions per wave per sub-tile
+  constexpr int KRI = 1024 / (HD * 2);              // keys per K load instruction
+  constexpr int KPC = HD / 8;                       // 16-byte pieces per key row
+  constexpr int KX = KPC < 16 ? KPC : 16;           // XOR range of the slab swizzle
+  auto load = [&](int n, u32x4 (&kr)[KI], u32x4 (&vr)[NV]) {
     const int k0 = ks0 + n * SUBK + w * KPW;
-    // ---- loads: all of this wave's K and V for the sub-tile at once ----
-    u32x4 kr[2][NK], vr[NV];
     if (W == 0 && k0 + KPW <= min(start, kend)) {   // every row a cache slot = position
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int s2 = 0; s2 < NK; ++s2)
-          kr[h2][s2] = stream_load(kbase + (int64_t)(k0 + 16 * h2 + kkey) * HD + kdim + 32 * s2);
+      for (int i = 0; i < KI; ++i)
+        kr[i] = stream_load(kbase + (int64_t)(k0 + KRI * i + lane / KPC) * HD + 8 * (lane % KPC));
 #pragma unroll
       for (int t = 0; t < NV; ++t)
         vr[t] = stream_load(vbase + (int64_t)(k0 + t * RPV + vkey) * HD + vdim);
     } else {
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const bf16* kp = row(kfresh, kbase, k0 + 16 * h2 + kkey) + kdim;
-#pragma unroll
-        for (int s2 = 0; s2 < NK; ++s2) kr[h2][s2] = stream_load(kp + 32 * s2);
-      }
+      for (int i = 0; i < KI; ++i)
+        kr[i] = stream_load(row(kfresh, kbase, k0 + KRI * i + lane / KPC) + 8 * (lane % KPC));
 #pragma unroll
       for (int t = 0; t < NV; ++t)
         vr[t] = stream_load(row(vfresh, vbase, k0 + t * RPV + vkey) + vdim);
     }
+  };
 
+  auto compute = [&](int n, const u32x4 (&kr)[KI], const u32x4 (&vr)[NV]) {
+    const int k0 = ks0 + n * SUBK + w * KPW;
+    // K through the wave's slab into the MFMA A layout: key row r, piece c at
+    // slot r * KPC + (c ^ (r % KX)); lane l reads key 16 h2 + l % 16, pieces
+    // 4 s2 + l / 16 (dims 32 s2 + 8 (l / 16), matching Q^T)
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int r = KRI * i + lane / KPC, c = lane % KPC;
+      kslab[w][r * KPC + (c ^ (r % KX))] = kr[i];
+    }
     // ---- scores: S^T[16 keys][16 heads] per block; lane holds keys 4(lane/16)+e ----
-    f32x4 sc[2];
+    f32x4 sc[NKB];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+    for (int h2 = 0; h2 < NKB; ++h2) {
       sc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int r = 16 * h2 + kkey;
 #pragma unroll
-      for (int s2 = 0; s2 < NK; ++s2)
-        sc[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[h2][s2]), qf[s2], sc[h2], 0, 0, 0);
+      for (int s2 = 0; s2 < NK; ++s2) {
+        const u32x4 kf = kslab[w][r * KPC + ((4 * s2 + lane / 16) ^ (kkey % KX))];
+        sc[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf), qf[s2], sc[h2], 0, 0, 0);
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+    for (int h2 = 0; h2 < NKB; ++h2)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float v = cap > 0.f ? cap * kLog2e * tanh_exp(sc[h2][e] * scale / cap) : sc[h2][e] * (scale * kLog2e);
@@ -222,7 +242,7 @@ __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs a) {
     }
     const float mr = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+    for (int h2 = 0; h2 < NKB; ++h2)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float pw = exp2_fast(sc[h2][e] - mr);
@@ -251,6 +271,12 @@ __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs a) {
       }
     }
     __builtin_amdgcn_wave_barrier();
+  };
+
+  for (int n = 0; n < nsub; ++n) {
+    u32x4 kr[KI], vr[NV];
+    load(n, kr, vr);
+    compute(n, kr, vr);
   }
 
   // wave totals: l over the 4 lanes of a head, o over the V row groups
