@@ -58,11 +58,18 @@ __device__ __forceinline__ void wait_slices(int later) {
   }
 }
 
-// Workgroup barrier that orders LDS accesses only (global loads stay in flight).
+// Workgroup barrier that orders LDS accesses only: this wave's LDS reads are
+// complete (lgkmcnt 0) and the caller has waited (vmcnt) for the slices it
+// publishes.  No memory fence: a workgroup-scope release fence also covers the
+// direct-to-LDS loads still in flight and would wait for all of them
+// (vmcnt 0), which would cut a ring deeper than two stages to one slice of
+// lookahead.  The empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
 __device__ __forceinline__ void lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0) only
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ int seg_of(const GemmArgs& a, int64_t n) {
