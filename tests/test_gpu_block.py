@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from gqa_causal_attention_amd.workloads import make_workload, random_block, round_bf16
-from tests.helpers import (OracleState, block_forward, block_step, check_close, fill_state_gpu,
+from tests.helpers import (OracleState, block_forward, block_step, check_close, fill_state_gpu, rel_err,
                            oracle_dtype, to_gpu)
 
 pytestmark = pytest.mark.gpu
@@ -196,3 +196,29 @@ def test_f32_block_variants(torch_cuda, name):
         check_close(blk.step(to_gpu(xt), st).cpu().numpy(), block_step(cfg, W, xt, ost, dtype=np.float64),
                     xt, "f32", f"{name} step {i}")
     np.testing.assert_allclose(st.k.cpu().numpy(), ost.k, rtol=1e-4, atol=1e-4 * np.abs(ost.k).max())
+
+
+@pytest.mark.gpu
+def test_page_worked_example_golden(torch_cuda):
+    """The HIP block on the mojolearn page's usage example (float32 weights,
+    TransformerBlock(weights, n_heads=4) on x of shape (2, 16, 64)) against the
+    stored float64 oracle output in tests/golden: sampled rows (y and y - x)
+    and the whole-output sum, within the float32 tolerance."""
+    from tests.golden.make_mojolearn_example import CFG, example_inputs, read
+    W, x = example_inputs()
+    y = _block(CFG, W).forward(to_gpu(x)).cpu().numpy().astype(np.float64)
+    assert y.shape == x.shape
+    ref = read()
+    got = np.stack([y[b, t] for (b, t) in ref["rows"]])
+    exp = np.stack(list(ref["rows"].values()))
+    xs = np.stack([x[b, t] for (b, t) in ref["rows"]]).astype(np.float64)
+    # The example's norm gains are 0.02-scale, so y - x is ~1e-3 of |y| and the
+    # float32 output's own rounding (half an ulp of y, which the float64
+    # reference does not have) is ~1e-4 of max|y - x|: the y - x bar adds two
+    # ulps of max|y| to the float32 tolerance.
+    e1 = rel_err(got, exp)
+    dev = np.max(np.abs(got - exp))
+    bar = 1e-4 * np.max(np.abs(exp - xs)) + 2.0 ** -22 * np.max(np.abs(exp))
+    print(f"[parity] page example: err(y)={e1:.3e} max|dy|={dev:.3e} bar(y-x)={bar:.3e}")
+    assert e1 <= 1e-4 and dev <= bar
+    assert abs(y.sum() - ref["sum"]) <= 1e-4 * np.abs(y).sum()

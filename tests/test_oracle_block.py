@@ -301,3 +301,19 @@ def test_rows_form_matches_full_form(over):
     ref = block_forward(cfg, W, x2, st.copy(), dtype=np.float64)
     got = block_forward_rows(cfg, W, x2, [(0, 5), (1, 0)], st, dtype=np.float64)
     np.testing.assert_allclose(got, np.stack([ref[0, 5], ref[1, 0]]), rtol=1e-12, atol=1e-12)
+
+
+def test_page_worked_example_golden():
+    """The oracle on the mojolearn page's usage example (TransformerBlock,
+    Examples) reproduces the stored output in tests/golden (written by the
+    committed script from the float64 oracle; the page prints the example's
+    inputs, not its output).  Also checks the example's documented shape
+    contract: the output has the input's shape (B, L, d_model)."""
+    from tests.golden.make_mojolearn_example import oracle_output, read
+    y = np.asarray(oracle_output(), dtype=np.float64)
+    assert y.shape == (2, 16, 64)
+    ref = read()
+    assert abs(y.sum() - ref["sum"]) <= 1e-9 * max(1.0, abs(ref["sum"]))
+    assert abs(np.square(y).sum() - ref["sumsq"]) <= 1e-9 * ref["sumsq"]
+    for (b, t), row in ref["rows"].items():
+        np.testing.assert_allclose(y[b, t], row, rtol=0, atol=1e-12)
