@@ -115,7 +115,7 @@ struct Scope {
   }
 };
 
-struct GemmPlan { int tile; int splits; };
+struct GemmPlan { int tile; int splits; int waves = 0; };
 
 }  // namespace
 
@@ -212,36 +212,40 @@ GemmPlan plan_gemm(int M, int N, int K, bool gated) {
     while (tiles * splits < 512 && K / (splits * 2) >= 256 && (K / 64) % (splits * 2) == 0) splits *= 2;
     return {kTile64x128, splits};
   }
-  // M <= 64: the weight-streaming kernel (128 weight rows per workgroup).
-  // Split K only until there are about 192 workgroups (three quarters of the
-  // CUs), and not below 512-deep splits:
-  // a split's float32 partials cost M * 4 bytes per weight row (written and
-  // read back) against 2 * k_split weight bytes, and measured on the 8B decode
-  // shapes fewer, longer-running workgroups stream the weights faster.
-  static const int target = [] {
-    const char* e = getenv("GQA_SKINNY_TARGET");  // tuning override
-    return e ? atoi(e) : 192;
+  // M <= 64: the weight-streaming kernel, one 16-row weight group per wave.
+  // Choose the K split s (a divisor of K / 256, splits at least kmin deep) and
+  // the waves per workgroup w (4..8, dividing the group count) by a simple
+  // cost: the bytes moved (weights, plus for s > 1 the float32 partials,
+  // written and read back: 2 * s * M * 4 bytes per weight row) over the rate,
+  // taken as full with 6 or more waves streaming per CU and proportional
+  // below, divided by the share of CU slots the grid's last round uses.
+  static const int cus = [] {
+    const char* e = getenv("GQA_SKINNY_CUS");  // tuning override
+    return e ? atoi(e) : 256;
   }();
   static const int kmin = [] {
     const char* e = getenv("GQA_SKINNY_KMIN");  // tuning override
     return e ? atoi(e) : 512;
   }();
-  if (gemm_skinny_supported(M, N, K, K)) {
-    // splits: the smallest divisor s of K / 256 (whole 256-deep super-chunks
-    // per split, at least kmin deep) that reaches the target, among depths
-    // that are multiples of 512 (the kernel's deeper weight ring) if any
-    const long tiles = ((gated ? 2L * N : (long)N) + 127) / 128;
-    if (tiles >= target) return {kTileSkinny, 1};
-    const int units = K / 256;
-    int best = 1;
-    for (int pass = 0; pass < 2 && best == 1; ++pass)
-      for (int s = 2; s <= units; ++s) {
-        if (units % s != 0 || K / s < kmin) continue;
-        if (pass == 0 && (K / s) % 512 != 0) continue;
-        best = s;
-        if (tiles * s >= target) break;
+  if (M <= 64 && K % 256 == 0) {
+    const long groups = gemm_skinny_groups(N, gated);
+    const double rows = 16.0 * (double)groups;
+    GemmPlan best{kTileSkinny, 0, 0};
+    double best_cost = 0.0;
+    for (int w = 8; w >= 4; --w)
+      for (int sp = 1; sp <= K / 256; ++sp) {
+        if ((K / 256) % sp != 0 || (sp > 1 && K / sp < kmin)) continue;
+        if (!gemm_skinny_supported(M, N, K, K / sp, w, gated)) continue;
+        const long wgs = groups / w * sp;
+        const double fill = (double)wgs / (double)(((wgs + cus - 1) / cus) * cus);
+        const double bytes = rows * K * 2.0 + (sp > 1 ? 2.0 * sp * M * 4.0 * rows : 0.0);
+        const double cost = bytes / (w >= 6 ? 1.0 : w / 6.0) / fill;
+        if (best.waves == 0 || cost < best_cost * (1.0 - 1e-9)) {
+          best_cost = cost;
+          best = {kTileSkinny, sp, w};
+        }
       }
-    return {kTileSkinny, best};
+    if (best.waves > 0) return best;
   }
   const int cols = gated ? 32 : 64;
   const long tiles = (N + cols - 1) / cols;
@@ -429,6 +433,7 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
   auto gemm = [&](const char* name, GemmArgs a, int mode, int epi, const GemmPlan& p,
                   bool defer_reduce = false) -> int {
     a.order = gemm_tile_order();
+    a.wg_waves = p.waves;
     if (!bf) {
       Scope sc(tm, name, s);
       HIP_TRY(launch_gemm_f32(a, mode, epi, s));

@@ -5,22 +5,33 @@
 // used by at most 64 rows and the kernel is bound by streaming W from HBM.
 //
 // Streaming W at full HBM bandwidth is a question of how the loads are shaped
-// (measured on gfx950 with this kernel's geometry, 4 waves x 32 rows per
-// workgroup, M = 64): loads straight into LDS (global_load_lds) top out near
-// 3.5 TB/s; register loads in MFMA operand layout (each instruction 64 bytes of
-// 16 rows) near 4.3 TB/s; register loads that cover whole 256-byte row pieces
-// (each instruction 4 rows x 256 bytes) near 5.3 TB/s.  So each wave streams
-// its 32 weight rows in that whole-piece shape into a register ring of SK_D
-// 128-deep chunks, and when a chunk comes due writes it to a private LDS slab
-// (XOR-swizzled on 16-byte pieces) and reads it back in A-operand layout (lane
-// l: row l % 16 of a 16-row group, 8 consecutive k at 8 (l / 16) of each
-// 32-deep step); only the wave itself touches its slab, so no barrier is
+// and spread (measured on gfx950 with M = 64):
+//  * loads straight into LDS (global_load_lds) top out near 3.5 TB/s, plain
+//    register loads reach 5-6 TB/s;
+//  * loads shaped as MFMA operands (64 bytes of each of 16 rows per
+//    instruction) stream ~15 % slower than loads covering whole 256-byte row
+//    pieces (4 rows x 256 bytes per instruction);
+//  * every CU should stream the same number of bytes with several
+//    independent waves: 256 workgroups of 7 waves, one 16-row weight group
+//    each, beat 224 workgroups of 4 waves x 32 rows on the same matrix.
+// So the work is cut into (16-row weight group, K split) tasks, one per wave;
+// a workgroup holds `wg_waves` tasks of one K split, and the host picks the
+// split count and the waves per workgroup so that the grid is (close to) one
+// workgroup per CU.  Each wave streams its rows in whole-piece loads into a
+// register ring of SK_D 128-deep chunks; a chunk coming due goes through the
+// wave's private LDS slab (XOR-swizzled on 16-byte pieces) into the MFMA
+// A-operand layout (lane l: row l % 16, 8 consecutive k at 8 (l / 16) of each
+// 32-deep step) -- only the wave itself touches its slab, so no barrier is
 // involved.  The activations (at most 64 rows, reused by every weight row) are
-// shared through LDS in B-operand fragment order a 256-deep super-chunk at a
+// shared through LDS in B-operand fragment order, a 256-deep super-chunk at a
 // time, double-buffered: each thread loads its share of super-chunk s + 1
 // (whole row pieces again) into registers while super-chunk s is multiplied
 // and writes it to LDS before the one barrier per super-chunk.  That barrier
 // has no memory fence, so the weight loads stay in flight across it.
+//
+// Gated mode (gate/up with act(gate) * up): a 16-row group is 8 gate rows and
+// the 8 up rows of the same 8 output columns, so the gate and up results of a
+// column sit in lanes l and l + 32 of one wave and meet through a lane swap.
 #include "common.h"
 #include "launch.h"
 
@@ -31,10 +42,7 @@ constexpr int SK_KX = 128;           // k per chunk (256 bytes of a row)
 constexpr int SK_SC = 2;             // chunks per super-chunk (one LDS activation buffer)
 constexpr int SK_D = 2;              // weight chunks in flight per wave (register ring)
 constexpr int SK_KS = SK_KX / 32;    // MFMA k-steps per chunk
-constexpr int SK_NW = 4;             // waves per workgroup
-constexpr int SK_RG = 2;             // 16-row weight groups per wave
-constexpr int SK_ROWS = SK_NW * SK_RG * 16;
-constexpr int SK_WI = SK_RG * 4;     // weight load instructions per wave per chunk (4 rows each)
+constexpr int SK_MINW = 4, SK_MAXW = 8;  // waves per workgroup
 
 __device__ __forceinline__ float act_of(int act, float g) {
   return act == kActGeluTanh ? gelu_tanh(g) : silu(g);
@@ -63,61 +71,62 @@ __device__ __forceinline__ bf16x8 load_global16(const bf16* p) {
   return *(const __attribute__((address_space(1))) bf16x8*)p;
 }
 
-template <int MT, int MODE, int EPI>
-__global__ __launch_bounds__(SK_NW * 64, 1) void gemm_skinny_kernel(GemmArgs a) {
-  constexpr int WROWS = SK_RG * 16;              // weight rows per wave (32)
+// Global row of row r (0..15) of weight group g.
+template <int MODE>
+__device__ __forceinline__ const bf16* group_row(const GemmArgs& a, int64_t g, int r) {
+  if (MODE == kModeGated) {  // rows 0-7: gate columns 8g .., rows 8-15: up, same columns
+    const int64_t col = min(8 * g + (r & 7), (int64_t)a.N - 1);
+    return static_cast<const bf16*>(a.B[r >> 3]) + col * a.K;
+  }
+  const int64_t n = min(16 * g + r, (int64_t)a.N - 1);
+  const int sg = seg_index(a, n);
+  return static_cast<const bf16*>(a.B[sg]) + (n - (sg == 0 ? 0 : a.seg_end[sg - 1])) * a.K;
+}
+
+template <int MT, int NWV, int MODE, int EPI>
+__global__ __launch_bounds__(NWV * 64, 1) void gemm_skinny_kernel(GemmArgs a) {
+  constexpr int NT = NWV * 64;
   constexpr int XF = SK_SC * SK_KS * MT;         // activation fragments (1 KB each) per super-chunk
-  constexpr int XT = XF / SK_NW;                 // 16-byte activation pieces per thread per super-chunk
-  static_assert(XF % SK_NW == 0, "activation pieces split evenly over the threads");
+  constexpr int XP = XF * 64;                    // 16-byte activation pieces per super-chunk
+  constexpr int XT = (XP + NT - 1) / NT;         // pieces per thread (the last may be a repeat)
   __shared__ __attribute__((aligned(1024))) bf16x8 xs[2][XF][64];
-  __shared__ __attribute__((aligned(1024))) bf16x8 wslab[SK_NW][WROWS * 16];
+  __shared__ __attribute__((aligned(1024))) bf16x8 wslab[NWV][16 * 16];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int z = blockIdx.y;
+  const int64_t g = (int64_t)blockIdx.x * NWV + wave;   // this wave's 16-row weight group
   const int64_t kb = (int64_t)z * a.k_split;
   const int nchunks = a.k_split / SK_KX;
 
   if (a.bump && blockIdx.x == 0 && blockIdx.y == 0)
-    for (int i = threadIdx.x; i < a.bump_n; i += SK_NW * 64) a.bump[i] += a.bump_by;
+    for (int i = threadIdx.x; i < a.bump_n; i += NT) a.bump[i] += a.bump_by;
 
-  // ---- weights: load instruction q moves rows 4 q .. 4 q + 3 of the wave's 32
-  // (rows 0-15 row group 0, 16-31 group 1), lane l: row 4 q + l / 16, 16-byte
-  // piece l % 16 of the chunk's 256 bytes ----
-  const bf16* wp[SK_WI];
+  // ---- weights: load instruction q moves rows 4 q .. 4 q + 3 of the group,
+  // lane l: row 4 q + l / 16, 16-byte piece l % 16 of the chunk's 256 bytes ----
+  const bf16* wp[4];
 #pragma unroll
-  for (int q = 0; q < SK_WI; ++q) {
-    const int wr = 4 * q + (lane >> 4);          // row within the wave's 32
-    const bf16* row;
-    if (MODE == kModeGated) {                    // group 0 gate, group 1 up, same 16 columns
-      const int col = min(blockIdx.x * (SK_ROWS / 2) + wave * 16 + (wr & 15), a.N - 1);
-      row = static_cast<const bf16*>(a.B[wr >> 4]) + (int64_t)col * a.K;
-    } else {
-      const int64_t n = min((int64_t)blockIdx.x * SK_ROWS + wave * WROWS + wr, (int64_t)a.N - 1);
-      const int sg = seg_index(a, n);
-      row = static_cast<const bf16*>(a.B[sg]) + (n - (sg == 0 ? 0 : a.seg_end[sg - 1])) * a.K;
-    }
-    wp[q] = row + kb + 8 * (lane & 15);
-  }
-  bf16x8 wr[SK_D][SK_WI];
-  auto load_w = [&](int c, bf16x8 (&dst)[SK_WI]) {
+  for (int q = 0; q < 4; ++q) wp[q] = group_row<MODE>(a, g, 4 * q + lg) + kb + 8 * lr;
+  bf16x8 wr[SK_D][4];
+  auto load_w = [&](int c, bf16x8 (&dst)[4]) {
 #pragma unroll
-    for (int q = 0; q < SK_WI; ++q)
+    for (int q = 0; q < 4; ++q)
       dst[q] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(wp[q] + c * SK_KX));
   };
-  // slab slot of (row r of the wave's 32, 16-byte piece p): r * 16 + (p ^ (r % 16))
+  // slab slot of (row r, 16-byte piece p): r * 16 + (p ^ r)
   bf16x8* slab = wslab[wave];
 
-  // ---- activations: a super-chunk is MT*16 rows x 256 k = 32 pieces of 16 bytes
-  // per row; this thread loads pieces tid + 256 i (row p / 32, piece p % 32;
-  // rows past M repeat row M-1) and stores piece kp of row m at fragment
-  // (kp / 4) * MT + m / 16, lane m % 16 + 16 (kp % 4) (B-operand order) ----
+  // ---- activations: a super-chunk is MT*16 rows x 256 k = 32 pieces of 16
+  // bytes per row; this thread loads pieces tid + NT i (row p / 32, piece
+  // p % 32; rows past M repeat row M-1; a piece index past the super-chunk
+  // repeats the last piece and is not stored) and stores piece kp of row m at
+  // fragment (kp / 4) * MT + m / 16, lane m % 16 + 16 (kp % 4) ----
   const bf16* xbase = static_cast<const bf16*>(a.A) + kb;
   bf16x8 xr[XT];
   auto load_x = [&](int sc) {
 #pragma unroll
     for (int i = 0; i < XT; ++i) {
-      const int p = threadIdx.x + SK_NW * 64 * i;
+      const int p = min((int)threadIdx.x + NT * i, XP - 1);
       const int m = min(p / 32, a.M - 1);
       const int k = min(sc * (SK_SC * SK_KX) + (p % 32) * 8, a.k_split - 8);  // past the end: never read
       xr[i] = load_global16(xbase + (int64_t)m * a.lda + k);
@@ -126,41 +135,34 @@ __global__ __launch_bounds__(SK_NW * 64, 1) void gemm_skinny_kernel(GemmArgs a) 
   auto store_x = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < XT; ++i) {
-      const int p = threadIdx.x + SK_NW * 64 * i;
-      const int m = p / 32, kp = p % 32;
-      xs[buf][(kp / 4) * MT + m / 16][(m % 16) + 16 * (kp % 4)] = xr[i];
+      const int p = threadIdx.x + NT * i;
+      if (XP % NT == 0 || p < XP) {
+        const int m = p / 32, kp = p % 32;
+        xs[buf][(kp / 4) * MT + m / 16][(m % 16) + 16 * (kp % 4)] = xr[i];
+      }
     }
   };
 
-  f32x4 acc[SK_RG][MT];
+  f32x4 acc[MT];
 #pragma unroll
-  for (int r = 0; r < SK_RG; ++r)
-#pragma unroll
-    for (int t = 0; t < MT; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int c, const bf16x8 (&w)[SK_WI]) {
+  auto compute = [&](int c, const bf16x8 (&w)[4]) {
     // the chunk through the wave's slab, from whole row pieces to A-operand layout
 #pragma unroll
-    for (int q = 0; q < SK_WI; ++q) {
-      const int r = 4 * q + (lane >> 4), p = lane & 15;
-      slab[r * 16 + (p ^ (r & 15))] = w[q];
+    for (int q = 0; q < 4; ++q) {
+      const int r = 4 * q + lg;
+      slab[r * 16 + (lr ^ r)] = w[q];
     }
     const int buf = (c / SK_SC) & 1, cl = c % SK_SC;
 #pragma unroll
     for (int ks = 0; ks < SK_KS; ++ks) {
-      bf16x8 wf[SK_RG], xf[MT];
-#pragma unroll
-      for (int r = 0; r < SK_RG; ++r) {
-        const int row = 16 * r + lr;
-        wf[r] = slab[row * 16 + ((4 * ks + lg) ^ lr)];
-      }
+      const bf16x8 wf = slab[lr * 16 + ((4 * ks + lg) ^ lr)];
+      bf16x8 xf[MT];
 #pragma unroll
       for (int t = 0; t < MT; ++t) xf[t] = xs[buf][(cl * SK_KS + ks) * MT + t][lane];
 #pragma unroll
-      for (int r = 0; r < SK_RG; ++r)
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-          acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[r], xf[t], acc[r][t], 0, 0, 0);
+      for (int t = 0; t < MT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[t], acc[t], 0, 0, 0);
     }
   };
 
@@ -170,12 +172,12 @@ __global__ __launch_bounds__(SK_NW * 64, 1) void gemm_skinny_kernel(GemmArgs a) 
   // loaded into registers while super-chunk s is multiplied and written to LDS
   // buffer (s + 1) & 1 after it: that buffer was last read in super-chunk
   // s - 1, which every wave finished before the barrier that closed it.  Every
-  // load is unconditional (indices clamp to the last chunk), and loads and
-  // stores of one activation super-chunk fall in one loop iteration, so the
-  // compiler's waits stay exact and never drain the weight stream. ----
+  // load is unconditional (indices clamp), and loads and stores of one
+  // activation super-chunk fall in one loop iteration, so the compiler's waits
+  // stay exact and never drain the weight stream; sched_barrier pins the
+  // issue order (the waits derived for the loop must hold for the prologue's
+  // order as well). ----
   static_assert(SK_D == SK_SC, "one activation super-chunk per loop iteration");
-  // (sched_barrier pins the issue order: the waits the compiler derives for
-  // the loop must hold for the prologue's order as well)
   load_x(0);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -193,80 +195,102 @@ __global__ __launch_bounds__(SK_NW * 64, 1) void gemm_skinny_kernel(GemmArgs a) 
       const int c = c0 + u;
       compute(c, wr[u]);
       load_w(min(c + SK_D, nchunks - 1), wr[u]);
-      // keep the issue order: the scheduler would otherwise sink these loads
-      // below the activation stores and the waits would cover them
       __builtin_amdgcn_sched_barrier(0);
     }
     store_x((c0 / SK_SC + 1) & 1);
     lds_barrier();
   }
 
-  // Epilogue: acc[r][t] element e is weight row 4*lg + e of row group r and
-  // activation row 16*t + lr, so each lane owns 4 consecutive output columns.
+  // ---- epilogue: acc[t] element e is weight row 4 lg + e of the group and
+  // activation row 16 t + lr ----
+  if constexpr (MODE == kModeGated && EPI == kEpiGated) {
+    // gate rows 4 lg + e (lanes 0-31) and up rows 8 + 4 (lg - 2) + e (lanes
+    // 32-63) are the same columns 8 g + 4 (lg & 1) + e: bring up to the gate lanes
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      f32x4 up;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) up[e] = xor32(acc[t][e]);
+      const int m = 16 * t + lr;
+      const int64_t col = 8 * g + 4 * (lg & 1);
+      if (lane < 32 && m < a.M && col < a.N) {
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = from_f32<bf16>(act_of(a.act, acc[t][e]) * up[e]);
+        *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.C) + (int64_t)m * a.ldc + col) = o;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int m = 16 * t + lr;
     if (m >= a.M) continue;
-    if constexpr (MODE == kModeGated) {
-      const int col = blockIdx.x * (SK_ROWS / 2) + wave * 16 + 4 * lg;
+    const f32x4 v = acc[t];
+    if constexpr (MODE == kModeGated) {  // kEpiPartial: gate at column col, up at N + col
+      const int64_t col = 8 * g + 4 * (lg & 1);
       if (col >= a.N) continue;
+      float* p = a.partial + ((int64_t)z * a.M + m) * (2 * (int64_t)a.N);
+      *reinterpret_cast<f32x4*>(p + (lg >= 2 ? a.N : 0) + col) = v;
+    } else {
+      const int64_t n = 16 * g + 4 * lg;
+      if (n >= a.N) continue;
       if constexpr (EPI == kEpiPartial) {
-        float* p = a.partial + ((int64_t)z * a.M + m) * (2 * (int64_t)a.N);
-        *reinterpret_cast<f32x4*>(p + col) = acc[0][t];
-        *reinterpret_cast<f32x4*>(p + a.N + col) = acc[1][t];
-      } else {  // kEpiGated
+        *reinterpret_cast<f32x4*>(a.partial + ((int64_t)z * a.M + m) * a.N + n) = v;
+      } else if constexpr (EPI == kEpiResid) {
+        const f32x4 rv = *reinterpret_cast<const f32x4*>(a.resid + (int64_t)m * a.ldr + n);
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.C) + (int64_t)m * a.ldc + n) = rv + v;
+      } else {  // kEpiStore (+ bias); a segment boundary may fall inside the 4 columns
         bf16x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = from_f32<bf16>(act_of(a.act, acc[0][t][e]) * acc[1][t][e]);
-        *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.C) + (int64_t)m * a.ldc + col) = o;
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < SK_RG; ++r) {
-        const int64_t n = (int64_t)blockIdx.x * SK_ROWS + wave * (SK_RG * 16) + r * 16 + 4 * lg;
-        if (n >= a.N) continue;
-        const f32x4 v = acc[r][t];
-        if constexpr (EPI == kEpiPartial) {
-          *reinterpret_cast<f32x4*>(a.partial + ((int64_t)z * a.M + m) * a.N + n) = v;
-        } else if constexpr (EPI == kEpiResid) {
-          const f32x4 rv = *reinterpret_cast<const f32x4*>(a.resid + (int64_t)m * a.ldr + n);
-          *reinterpret_cast<f32x4*>(static_cast<float*>(a.C) + (int64_t)m * a.ldc + n) = rv + v;
-        } else {  // kEpiStore (+ bias); a segment boundary may fall inside the 4 columns
-          bf16x4 o;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int64_t col = n + e;
-            const int s = seg_index(a, col);
-            const float b = a.bias[s] ? a.bias[s][col - (s == 0 ? 0 : a.seg_end[s - 1])] : 0.f;
-            o[e] = from_f32<bf16>(v[e] + b);
-          }
-          *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.C) + (int64_t)m * a.ldc + n) = o;
+        for (int e = 0; e < 4; ++e) {
+          const int64_t col = n + e;
+          const int s = seg_index(a, col);
+          const float b = a.bias[s] ? a.bias[s][col - (s == 0 ? 0 : a.seg_end[s - 1])] : 0.f;
+          o[e] = from_f32<bf16>(v[e] + b);
         }
+        *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.C) + (int64_t)m * a.ldc + n) = o;
       }
     }
   }
 }
 
+template <int MT, int MODE, int EPI>
+hipError_t launch_w(const GemmArgs& a, dim3 grid, hipStream_t s) {
+  switch (a.wg_waves) {
+    case 4: hipLaunchKernelGGL((gemm_skinny_kernel<MT, 4, MODE, EPI>), grid, dim3(4 * 64), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((gemm_skinny_kernel<MT, 5, MODE, EPI>), grid, dim3(5 * 64), 0, s, a); break;
+    case 6: hipLaunchKernelGGL((gemm_skinny_kernel<MT, 6, MODE, EPI>), grid, dim3(6 * 64), 0, s, a); break;
+    case 7: hipLaunchKernelGGL((gemm_skinny_kernel<MT, 7, MODE, EPI>), grid, dim3(7 * 64), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((gemm_skinny_kernel<MT, 8, MODE, EPI>), grid, dim3(8 * 64), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int MODE, int EPI>
 hipError_t launch_mt(const GemmArgs& a, hipStream_t s) {
-  const int64_t rows = MODE == kModeGated ? 2 * (int64_t)a.N : a.N;
-  dim3 grid((unsigned)((rows + SK_ROWS - 1) / SK_ROWS), a.splits);
-  dim3 block(SK_NW * 64);
-  if (a.M <= 16) hipLaunchKernelGGL((gemm_skinny_kernel<1, MODE, EPI>), grid, block, 0, s, a);
-  else if (a.M <= 32) hipLaunchKernelGGL((gemm_skinny_kernel<2, MODE, EPI>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((gemm_skinny_kernel<4, MODE, EPI>), grid, block, 0, s, a);
-  return hipGetLastError();
+  const int64_t groups = gemm_skinny_groups(a.N, MODE == kModeGated);
+  dim3 grid((unsigned)(groups / a.wg_waves), a.splits);
+  if (a.M <= 16) return launch_w<1, MODE, EPI>(a, grid, s);
+  if (a.M <= 32) return launch_w<2, MODE, EPI>(a, grid, s);
+  return launch_w<4, MODE, EPI>(a, grid, s);
 }
 
 }  // namespace
 
-bool gemm_skinny_supported(int M, int N, int K, int k_split) {
-  // whole super-chunks (an even number of 128-deep chunks) per split
-  return M >= 1 && M <= 64 && N % 4 == 0 && K % 8 == 0 && k_split >= SK_SC * SK_KX && k_split % (SK_SC * SK_KX) == 0;
+int64_t gemm_skinny_groups(int N, bool gated) { return gated ? ((int64_t)N + 7) / 8 : ((int64_t)N + 15) / 16; }
+
+bool gemm_skinny_supported(int M, int N, int K, int k_split, int waves, bool gated) {
+  // whole super-chunks (an even number of 128-deep chunks) per split, and the
+  // weight groups split evenly over the workgroups
+  return M >= 1 && M <= 64 && N % 4 == 0 && K % 8 == 0 && k_split >= SK_SC * SK_KX &&
+         k_split % (SK_SC * SK_KX) == 0 && waves >= SK_MINW && waves <= SK_MAXW &&
+         gemm_skinny_groups(N, gated) % waves == 0;
 }
 
 hipError_t launch_gemm_skinny(const GemmArgs& a, int mode, int epi, hipStream_t s) {
-  if (!gemm_skinny_supported(a.M, a.N, a.K, a.k_split) || a.splits < 1 ||
+  if (!gemm_skinny_supported(a.M, a.N, a.K, a.k_split, a.wg_waves, mode == kModeGated) || a.splits < 1 ||
       (int64_t)a.k_split * a.splits != a.K)
     return hipErrorInvalidValue;
   if (mode == kModeGated) {

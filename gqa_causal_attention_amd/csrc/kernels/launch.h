@@ -40,6 +40,7 @@ struct GemmArgs {
   int* bump;               // if non-null: bump[i] += bump_by for i < bump_n (once)
   int bump_n, bump_by;
   int order;               // tile order of the pipelined kernel (0 = XCD-aware groups; others for tuning)
+  int wg_waves;            // weight-streaming kernel: waves (16-row weight groups) per workgroup
 };
 
 // Tile shapes of the bf16 MFMA GEMM.
@@ -58,7 +59,9 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, int mode, int epi, int tile, hipS
 bool gemm_dma_tile(int tile);
 hipError_t launch_gemm_dma(const GemmArgs& a, int mode, int epi, int tile, hipStream_t s);
 // Weight-streaming GEMM for M <= 64 (decode); K split in multiples of 256.
-bool gemm_skinny_supported(int M, int N, int K, int k_split);
+// Its weight groups: 16 rows each (gated: 8 gate + 8 up rows of 8 columns).
+int64_t gemm_skinny_groups(int N, bool gated);
+bool gemm_skinny_supported(int M, int N, int K, int k_split, int waves, bool gated);
 hipError_t launch_gemm_skinny(const GemmArgs& a, int mode, int epi, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& a, int mode, int epi, hipStream_t s);
 // Sum the K-split partials in split order, then apply `epi` (kEpiStore / kEpiResid /
