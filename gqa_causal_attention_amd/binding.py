@@ -22,7 +22,8 @@ STATUS = {0: "OK", -1: "ARG", -2: "SHAPE", -3: "DTYPE", -4: "NONFINITE", -5: "CA
 # Exported entry points declared in include/gqa_block.h.
 EXPORTS = ("gqa_block_create", "gqa_block_destroy", "gqa_state_bytes", "gqa_block_allocate_state",
            "gqa_state_set_lengths", "gqa_state_get_lengths", "gqa_state_free", "gqa_workspace_bytes",
-           "gqa_block_forward", "gqa_block_step", "gqa_block_status", "gqa_block_set_timing",
+           "gqa_block_forward", "gqa_block_forward_ragged", "gqa_block_step", "gqa_block_status",
+           "gqa_block_set_timing",
            "gqa_block_kernel_times", "gqa_last_error", "gqa_version")
 
 
@@ -68,6 +69,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gqa_state_free": ([P], None),
         "gqa_workspace_bytes": ([P, I32, I32, ctypes.POINTER(SZ)], I32),
         "gqa_block_forward": ([P, P, P, P, I32, I32, P, SZ, P], I32),
+        "gqa_block_forward_ragged": ([P, P, P, I32, I32, ctypes.POINTER(I32), P, SZ, P], I32),
         "gqa_block_step": ([P, P, P, P, I32, P, SZ, P], I32),
         "gqa_block_status": ([P, P], I32),
         "gqa_block_set_timing": ([P, I32], I32),
@@ -173,12 +175,23 @@ class Block:
     def allocate_state(self, batch: int, max_tokens: int) -> "State":
         return State(self, batch, max_tokens)
 
-    def forward(self, x, state: "State | None" = None, out=None, stream=None):
+    def forward(self, x, state: "State | None" = None, out=None, stream=None, lengths=None):
+        """mojolearn TransformerBlock.forward; `lengths` (B ints in [1, L], no
+        state) makes the batch ragged: padding positions output +0.0."""
         import torch
         assert x.dtype == torch.float32 and x.is_contiguous() and x.dim() == 3
         B, L, _ = x.shape
         y = torch.empty_like(x) if out is None else out
         ws, nb = self.workspace(B, L)
+        if lengths is not None:
+            if state is not None:
+                raise ValueError("lengths is not allowed together with state")
+            lens = (ctypes.c_int32 * B)(*[int(v) for v in lengths])
+            _check(self.lib.gqa_block_forward_ragged(self.handle, ctypes.c_void_p(x.data_ptr()),
+                                                     ctypes.c_void_p(y.data_ptr()), B, L, lens,
+                                                     ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                                     _stream_ptr(stream)))
+            return y
         _check(self.lib.gqa_block_forward(self.handle, state.handle if state else None,
                                           ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
                                           B, L, ctypes.c_void_p(ws.data_ptr()), ws.numel(),

@@ -752,6 +752,24 @@ int gqa_block_forward(gqa_block* blk, gqa_state* st, const float* x, float* y, i
   return run_block(blk, st, x, y, B, L, ws, wsb, static_cast<hipStream_t>(stream));
 }
 
+int gqa_block_forward_ragged(gqa_block* blk, const float* x, float* y, int32_t B, int32_t L,
+                             const int32_t* lengths, void* ws, size_t wsb, void* stream) {
+  if (!blk) return fail(GQA_ERR_ARG, "block is NULL");
+  if (B < 0 || L < 0) return fail(GQA_ERR_ARG, "B and L must be >= 0");
+  if (B > 0 && L > 0 && !lengths) return fail(GQA_ERR_ARG, "lengths is NULL");
+  for (int b = 0; b < B && L > 0; ++b)
+    if (lengths[b] < 1 || lengths[b] > L)
+      return fail(GQA_ERR_ARG, "row %d: length %d outside [1, %d]", b, lengths[b], L);
+  // Causal (and windowed) attention never lets a real position read a later
+  // one, and every other step is per token, so the real positions of the
+  // padded batch are exactly those of each row run alone; the padding
+  // positions are then overwritten with +0.0.
+  if (int r = run_block(blk, nullptr, x, y, B, L, ws, wsb, static_cast<hipStream_t>(stream))) return r;
+  if (B == 0 || L == 0) return GQA_OK;
+  HIP_TRY(launch_zero_padding(y, lengths, B, L, blk->cfg.d_model, static_cast<hipStream_t>(stream)));
+  return GQA_OK;
+}
+
 int gqa_block_step(gqa_block* blk, gqa_state* st, const float* x, float* y, int32_t B, void* ws, size_t wsb,
                    void* stream) {
   if (!st) return fail(GQA_ERR_STATE, "step requires a state");

@@ -1,6 +1,8 @@
 // Small device utilities: a non-finite scan of a weight tensor (run once when
 // a block is created: the mojolearn page rejects non-finite weights before any
-// computation) and a per-row length bump.
+// computation), a per-row length bump, and the zeroing of the padding positions
+// of a ragged prefill (mojolearn TransformerBlock.forward `lengths`: padding
+// positions output exactly +0.0).
 #include "common.h"
 #include "launch.h"
 
@@ -20,7 +22,41 @@ __global__ void bump_kernel(int* lengths, int n, int by) {
   if (i < n) lengths[i] += by;
 }
 
+// Rows first .. first + count - 1 of y [B, L, d]: positions t >= n[row - first]
+// get +0.0.  Grid: (elements per row / 256, count).
+constexpr int kPadRows = 256;
+struct PadLens {
+  int32_t n[kPadRows];
+};
+__global__ __launch_bounds__(256) void zero_padding_kernel(float* y, PadLens lens, int first, int L, int d) {
+  const int r = blockIdx.y;
+  const int64_t per_row = (int64_t)L * d;
+  const int64_t start = (int64_t)lens.n[r] * d;
+  float* row = y + (int64_t)(first + r) * per_row;
+  for (int64_t i = start + (int64_t)blockIdx.x * 256 + threadIdx.x; i < per_row; i += (int64_t)gridDim.x * 256)
+    row[i] = 0.0f;
+}
+
 }  // namespace
+
+hipError_t launch_zero_padding(float* y, const int32_t* lengths_host, int B, int L, int d, hipStream_t s) {
+  for (int first = 0; first < B; first += kPadRows) {
+    const int count = B - first < kPadRows ? B - first : kPadRows;
+    PadLens lens{};
+    int maxpad = 0;
+    for (int r = 0; r < count; ++r) {
+      lens.n[r] = lengths_host[first + r];
+      if (L - lens.n[r] > maxpad) maxpad = L - lens.n[r];
+    }
+    if (maxpad == 0) continue;
+    const int64_t blocks = std::min<int64_t>(((int64_t)maxpad * d + 255) / 256, 1024);
+    hipLaunchKernelGGL(zero_padding_kernel, dim3((unsigned)blocks, (unsigned)count), dim3(256), 0, s, y, lens, first,
+                       L, d);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
 
 hipError_t launch_count_nonfinite(const void* p, int elem, int64_t n, int* flag, hipStream_t s) {
   if (n <= 0) return hipSuccess;

@@ -150,6 +150,18 @@ int gqa_workspace_bytes(const gqa_block* blk, int32_t B, int32_t L, size_t* out)
 int gqa_block_forward(gqa_block* blk, gqa_state* st, const float* x_dev, float* y_dev, int32_t B,
                       int32_t L, void* workspace_dev, size_t workspace_bytes, void* hip_stream);
 
+/* mojolearn TransformerBlock.forward with `lengths` (a ragged batch, no state):
+ * row b is real at positions [0, lengths[b]) and padding after.  Each real
+ * position's output equals that row run alone at its own length; padding
+ * positions output exactly +0.0.  lengths is a HOST array of B values in
+ * [1, L] (checked before any launch; not retained).  x, y, workspace as in
+ * gqa_block_forward with state NULL (workspace sized by gqa_workspace_bytes(B, L)).
+ * Errors: ARG (NULL lengths, a length outside [1, L]), and those of
+ * gqa_block_forward. */
+int gqa_block_forward_ragged(gqa_block* blk, const float* x_dev, float* y_dev, int32_t B, int32_t L,
+                             const int32_t* lengths_host, void* workspace_dev, size_t workspace_bytes,
+                             void* hip_stream);
+
 /* mojolearn TransformerBlock.step: forward with L = 1 on a required state; x
  * is [B, d] or [B, 1, d] (the same memory).  Errors: as forward, STATE if st
  * is NULL. */

@@ -288,7 +288,7 @@ def _mlp(cfg, w, x1, layout):
 
 
 def block_forward(cfg: dict, W: dict, x: np.ndarray, state: OracleState | None = None,
-                  *, dtype=np.float32, layout: str = "batched") -> np.ndarray:
+                  *, dtype=np.float32, layout: str = "batched", lengths=None) -> np.ndarray:
     """Run the block on x [B, L, d]; returns y [B, L, d] in ``dtype``.
 
     mojolearn ``TransformerBlock.forward``: with ``state=None`` a
@@ -297,7 +297,24 @@ def block_forward(cfg: dict, W: dict, x: np.ndarray, state: OracleState | None =
     the lengths advance by L.  Positions must stay below ``max_positions``
     and, without a window, within the state's capacity (the page's errors
     before any computation).
+
+    ``lengths`` (the page's ragged batch; not allowed with a state): B values
+    in [1, L]; row i is real at positions [0, lengths[i]) and padding after.
+    Written as the page states it: each row's real positions are that row run
+    alone at its own length, and padding positions are exactly +0.0.
     """
+    if lengths is not None:
+        if state is not None:
+            raise ValueError("lengths is not allowed together with state")
+        x = np.asarray(x)
+        B, L = x.shape[0], x.shape[1]
+        lens = [int(n) for n in lengths]
+        if len(lens) != B or any(n < 1 or n > L for n in lens):
+            raise ValueError("lengths must hold B values in [1, L]")
+        y = np.zeros(x.shape, dtype=np.dtype(dtype))
+        for i, n in enumerate(lens):
+            y[i, :n] = block_forward(cfg, W, x[i:i + 1, :n], dtype=dtype, layout=layout)[0]
+        return y
     dt = np.dtype(dtype)
     x = np.asarray(x).astype(dt)
     B, L, d = x.shape

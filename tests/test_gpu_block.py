@@ -222,3 +222,43 @@ def test_page_worked_example_golden(torch_cuda):
     print(f"[parity] page example: err(y)={e1:.3e} max|dy|={dev:.3e} bar(y-x)={bar:.3e}")
     assert e1 <= 1e-4 and dev <= bar
     assert abs(y.sum() - ref["sum"]) <= 1e-4 * np.abs(y).sum()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ragged_prefill_lengths(torch_cuda, dtype):
+    """mojolearn forward(x, lengths=...): a ragged batch against the oracle's
+    reading of it (each row alone at its own length, padding +0.0), padding
+    exactly positive zero, real positions bitwise equal to the unragged run's
+    (causality), padding inputs changing nothing, and the argument errors.
+    The bf16 case has T = 600 tokens, so it runs the large-M GEMM tiles."""
+    import torch
+    from gqa_causal_attention_amd.binding import GqaError
+    if dtype == "bf16":
+        cfg, W = random_block(41, dtype="bf16", d_model=256, n_heads=8, n_kv_heads=2, head_dim=128,
+                              intermediate=384)
+        B, L, lens = 3, 200, [200, 57, 1]
+    else:
+        cfg, W = random_block(42, dtype="f32", window=6, attn_softcap=20.0)
+        B, L, lens = 3, 13, [13, 5, 1]
+    rng = np.random.default_rng(17)
+    x = rng.standard_normal((B, L, cfg["d_model"]), dtype=np.float32)
+    blk = _block(cfg, W)
+    y = blk.forward(to_gpu(x), lengths=lens).cpu().numpy()
+    ref = block_forward(cfg, W, x, dtype=oracle_dtype(cfg), lengths=lens)
+    check_close(y, ref, x, dtype, f"ragged {dtype}")
+    full = blk.forward(to_gpu(x)).cpu().numpy()
+    x2 = x.copy()
+    for i, n in enumerate(lens):
+        pad = y[i, n:]
+        assert np.all(pad == 0.0) and not np.any(np.signbit(pad)), f"row {i}: padding not +0.0"
+        np.testing.assert_array_equal(y[i, :n], full[i, :n])
+        x2[i, n:] = rng.standard_normal((L - n, cfg["d_model"]), dtype=np.float32) * 3
+    np.testing.assert_array_equal(blk.forward(to_gpu(x2), lengths=lens).cpu().numpy(), y)
+    with pytest.raises(GqaError):
+        blk.forward(to_gpu(x), lengths=[0] + lens[1:])
+    with pytest.raises(GqaError):
+        blk.forward(to_gpu(x), lengths=[L + 1] + lens[1:])
+    with pytest.raises(ValueError):
+        blk.forward(to_gpu(x), blk.allocate_state(B, L), lengths=lens)
+    torch.cuda.synchronize()

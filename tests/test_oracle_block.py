@@ -317,3 +317,48 @@ def test_page_worked_example_golden():
     assert abs(np.square(y).sum() - ref["sumsq"]) <= 1e-9 * ref["sumsq"]
     for (b, t), row in ref["rows"].items():
         np.testing.assert_allclose(y[b, t], row, rtol=0, atol=1e-12)
+
+
+def test_ragged_lengths_reading_and_pins():
+    """mojolearn forward(x, lengths=...): the page's ragged batch.  Pins that do
+    not restate the definition: (a) lengths all equal to L is the plain
+    batched forward; (b) by causality, a row's real positions equal the first
+    lengths[i] positions of the same row run unragged at full L; (c) padding
+    outputs are exactly +0.0 (positive zero) and the padding inputs change
+    nothing; (d) a state is refused, as are lengths outside [1, L]."""
+    cfg, W = random_block(31, window=0)
+    rng = np.random.default_rng(5)
+    B, L = 3, 9
+    x = rng.standard_normal((B, L, cfg["d_model"]), dtype=np.float32)
+    full = block_forward(cfg, W, x, dtype=np.float64)
+    np.testing.assert_allclose(block_forward(cfg, W, x, dtype=np.float64, lengths=[L] * B), full, rtol=0,
+                               atol=1e-12)
+    lens = [4, 9, 1]
+    y = block_forward(cfg, W, x, dtype=np.float64, lengths=lens)
+    for i, n in enumerate(lens):
+        np.testing.assert_allclose(y[i, :n], full[i, :n], rtol=0, atol=1e-12)
+        pad = y[i, n:]
+        assert np.all(pad == 0.0) and not np.any(np.signbit(pad))
+    x2 = x.copy()
+    for i, n in enumerate(lens):
+        x2[i, n:] = rng.standard_normal((L - n, cfg["d_model"]), dtype=np.float32) * 5
+    np.testing.assert_array_equal(block_forward(cfg, W, x2, dtype=np.float64, lengths=lens), y)
+    with pytest.raises(ValueError):
+        block_forward(cfg, W, x, OracleState(cfg, B, 16), lengths=lens)
+    with pytest.raises(ValueError):
+        block_forward(cfg, W, x, lengths=[0, 9, 1])
+    with pytest.raises(ValueError):
+        block_forward(cfg, W, x, lengths=[10, 9, 1])
+
+
+def test_ragged_window_softcap_pin():
+    """The ragged reading under a window, softcap and GQA: still the causal
+    prefix of the unragged run (windowed keys are never later positions)."""
+    cfg, W = random_block(32, window=3, attn_softcap=5.0, n_heads=4, n_kv_heads=1, mlp="geglu_tanh")
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((2, 7, cfg["d_model"]), dtype=np.float32)
+    full = block_forward(cfg, W, x, dtype=np.float64)
+    y = block_forward(cfg, W, x, dtype=np.float64, lengths=[5, 2])
+    np.testing.assert_allclose(y[0, :5], full[0, :5], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(y[1, :2], full[1, :2], rtol=0, atol=1e-12)
+    assert np.all(y[0, 5:] == 0) and np.all(y[1, 2:] == 0)
