@@ -2,7 +2,7 @@
 tests, the smoke check and the bench's CPU baseline leg, never by the product
 path.  See ``oracle.block`` for what it computes and the passages it follows."""
 from .block import (OracleState, apply_rope, attention_row, block_forward, block_forward_rows, block_step,
-                    gelu_tanh, rms_norm, rope_cos_sin, silu)
+                    gelu_tanh, rms_norm, rope_cos_sin, rope_inv_freq, silu)
 
 __all__ = ["OracleState", "apply_rope", "attention_row", "block_forward", "block_forward_rows", "block_step",
-           "gelu_tanh", "rms_norm", "rope_cos_sin", "silu"]
+           "gelu_tanh", "rms_norm", "rope_cos_sin", "rope_inv_freq", "silu"]

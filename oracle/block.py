@@ -24,6 +24,13 @@ design notes of the repository):
     interleaved pairs (2i, 2i+1), which is the same map up to a fixed
     permutation of each head's dimensions.  Angles and cos/sin are formed in
     float64 and rounded to the oracle's working precision.
+  * Partial rotary (``rope_dim`` r < hd) rotates the rotate-half pairs
+    (i, i + r/2) of a head's first r dimensions with frequencies
+    base^(-2i/r) and leaves dimensions r .. hd-1 as they are (Hugging Face's
+    partial_rotary_factor convention, which the page's layer follows).
+  * ``rope_scaling`` "linear" divides every frequency by its factor; "llama3"
+    applies Hugging Face's Llama 3 wavelength ramp (``rope_inv_freq``); the
+    page names both and their parameters but prints neither formula.
   * A window W means W keys including the query's own position: keys
     [max(0, p - W + 1), p] (mojolearn ``window`` parameter).
   * Masked keys are excluded from the softmax (not given a -1e9 bias).
@@ -52,7 +59,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "rms_norm", "rope_cos_sin", "apply_rope", "silu", "gelu_tanh", "attention_row",
+    "rms_norm", "rope_inv_freq", "rope_cos_sin", "apply_rope", "silu", "gelu_tanh", "attention_row",
     "OracleState", "block_forward", "block_step", "block_forward_rows",
 ]
 
@@ -76,32 +83,79 @@ def rms_norm(x: np.ndarray, w: np.ndarray, eps: float, offset: bool = False) -> 
     return x / np.sqrt(ms + dt.type(eps)) * g
 
 
-def rope_cos_sin(positions: np.ndarray, head_dim: int, theta: float) -> tuple[np.ndarray, np.ndarray]:
-    """cos and sin of p * theta_i for i in [0, hd/2), in float64.
+def rope_inv_freq(rot_dim: int, theta: float, scaling: dict | None = None) -> np.ndarray:
+    """Inverse frequencies theta_i for i in [0, rot_dim/2), in float64.
 
-    DantinoX "Core Layers" page, Positional Encoding / RoPE: rotation of each
-    dimension pair by p * theta_i with theta_i = base^(-2i/d_h); the base is
-    the block's ``rope_theta`` (mojolearn parameter).  Returns arrays of shape
-    positions.shape + (hd/2,).
+    DantinoX "Core Layers" page, Positional Encoding / RoPE: theta_i =
+    base^(-2i/d) with d the number of rotated dimensions; the base is the
+    block's ``rope_theta`` (mojolearn parameter; the page's NTK-aware variant
+    is this same formula with the base multiplied by lambda).  mojolearn
+    ``rope_dim`` (partial rotary) sets d below head_dim.
+
+    mojolearn ``rope_scaling`` (the TransformerBlock parameter list):
+      * {"type": "linear", "factor": f}: every frequency divided by f, so
+        position p turns as position p / f did.
+      * {"type": "llama3", "factor": f, "low_freq_factor": lo,
+        "high_freq_factor": hi, "original_max_position_embeddings": n}: the
+        Llama 3 ramp the block inherits from Hugging Face's layer, read from
+        wavelengths w_i = 2 pi / theta_i.  A frequency whose wavelength is
+        longer than n / lo is divided by f; one shorter than n / hi is kept;
+        between the two it is the blend (1 - s) theta_i / f + s theta_i with
+        s = (n / w_i - lo) / (hi - lo), which meets the two ends continuously.
     """
-    i = np.arange(head_dim // 2, dtype=np.float64)
-    inv_freq = np.float64(theta) ** (-2.0 * i / head_dim)
+    i = np.arange(rot_dim // 2, dtype=np.float64)
+    inv = np.float64(theta) ** (-2.0 * i / rot_dim)
+    if not scaling:
+        return inv
+    kind = scaling.get("type", scaling.get("rope_type"))
+    f = np.float64(scaling["factor"])
+    if kind == "linear":
+        return inv / f
+    if kind != "llama3":
+        raise ValueError(f"unknown rope_scaling type {kind!r}")
+    lo = np.float64(scaling["low_freq_factor"])
+    hi = np.float64(scaling["high_freq_factor"])
+    n = np.float64(scaling["original_max_position_embeddings"])
+    out = np.empty_like(inv)
+    for j, th in enumerate(inv):
+        wavelen = 2.0 * np.pi / th
+        if wavelen > n / lo:          # long wavelengths: interpolated by f
+            out[j] = th / f
+        elif wavelen < n / hi:        # short wavelengths: unchanged
+            out[j] = th
+        else:                         # the ramp between them
+            s = (n / wavelen - lo) / (hi - lo)
+            out[j] = (1.0 - s) * th / f + s * th
+    return out
+
+
+def rope_cos_sin(positions: np.ndarray, rot_dim: int, theta: float,
+                 scaling: dict | None = None) -> tuple[np.ndarray, np.ndarray]:
+    """cos and sin of p * theta_i for i in [0, rot_dim/2), in float64.
+
+    DantinoX "Core Layers" page, Positional Encoding / RoPE: the rotation of
+    each dimension pair by the angle p * theta_i, theta_i from
+    ``rope_inv_freq``.  Returns arrays of shape positions.shape + (rot_dim/2,).
+    """
+    inv_freq = rope_inv_freq(rot_dim, theta, scaling)
     ang = np.asarray(positions, dtype=np.float64)[..., None] * inv_freq
     return np.cos(ang), np.sin(ang)
 
 
 def apply_rope(u: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
-    """Rotate pairs (i, i + hd/2) of the last axis by the given angles.
+    """Rotate pairs (i, i + r/2) of the first r = 2 * cos.shape[-1] dims.
 
-    u' _i        = u_i cos a_i - u_{i+hd/2} sin a_i
-    u'_{i+hd/2}  = u_{i+hd/2} cos a_i + u_i sin a_i
-    (the page's 2x2 rotation, applied to Hugging Face's rotate-half pairs).
-    ``cos``/``sin`` broadcast against u[..., :hd/2].
+    u'_i       = u_i cos a_i - u_{i+r/2} sin a_i
+    u'_{i+r/2} = u_{i+r/2} cos a_i + u_i sin a_i
+    (the page's 2x2 rotation, applied to Hugging Face's rotate-half pairs);
+    dimensions r .. hd-1 pass through unchanged (partial rotary, mojolearn
+    ``rope_dim``).  ``cos``/``sin`` broadcast against u[..., :r/2].
     """
-    half = u.shape[-1] // 2
-    a, b = u[..., :half], u[..., half:]
+    half = cos.shape[-1]
+    r = 2 * half
+    a, b, rest = u[..., :half], u[..., half:r], u[..., r:]
     c, s = cos.astype(u.dtype), sin.astype(u.dtype)
-    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+    return np.concatenate([a * c - b * s, b * c + a * s, rest], axis=-1)
 
 
 def silu(z: np.ndarray) -> np.ndarray:
@@ -240,6 +294,12 @@ def _linear(h, w, b=None):
     return y
 
 
+def _rope(cfg, positions):
+    """cos/sin tables of the block's RoPE options (rope_theta, rope_dim, rope_scaling)."""
+    rd = cfg.get("rope_dim") or cfg["head_dim"]
+    return rope_cos_sin(positions, rd, cfg["rope_theta"], cfg.get("rope_scaling"))
+
+
 def _project(cfg, W, x, dt, positions, layout):
     """Steps up to RoPE: returns q [B,L,H,hd], k, v [B,L,KV,hd] (k, q rotated)."""
     B, L, d = x.shape
@@ -264,7 +324,7 @@ def _project(cfg, W, x, dt, positions, layout):
     if cfg.get("qk_norm"):
         q = rms_norm(q, w["q_norm.weight"], eps, offset)
         k = rms_norm(k, w["k_norm.weight"], eps, offset)
-    cos, sin = rope_cos_sin(positions, hd, cfg["rope_theta"])  # [B, L, hd/2]
+    cos, sin = _rope(cfg, positions)  # [B, L, rope_dim/2]
     q = apply_rope(q, cos[:, :, None, :], sin[:, :, None, :])
     k = apply_rope(k, cos[:, :, None, :], sin[:, :, None, :])
     return w, q, k, v
@@ -434,7 +494,7 @@ def block_forward_rows(cfg: dict, W: dict, x: np.ndarray, rows, state: OracleSta
         if cfg.get("qk_norm"):
             k = rms_norm(k, w["k_norm.weight"], eps, offset)
         pos = s0 + np.arange(L)
-        cos, sin = rope_cos_sin(pos, hd, cfg["rope_theta"])
+        cos, sin = _rope(cfg, pos)
         k = apply_rope(k, cos[:, None, :], sin[:, None, :])
         lo = max(0, s0 - window) if window > 0 else 0
         if state is not None and s0 > lo:
@@ -450,7 +510,7 @@ def block_forward_rows(cfg: dict, W: dict, x: np.ndarray, rows, state: OracleSta
         q = _linear(hq, w["q_proj.weight"], w.get("q_proj.bias")).reshape(len(ts), H, hd)
         if cfg.get("qk_norm"):
             q = rms_norm(q, w["q_norm.weight"], eps, offset)
-        cq, sq = rope_cos_sin(s0 + ts, hd, cfg["rope_theta"])
+        cq, sq = _rope(cfg, s0 + ts)
         q = apply_rope(q, cq[:, None, :], sq[:, None, :])
         ctx = attention_row(q, kall, vall, s0 + ts, kpos, window, cfg.get("attn_softcap", 0.0))
         x1 = xb[ts] + ctx.reshape(len(ts), H * hd) @ w["o_proj.weight"].T
