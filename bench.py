@@ -172,7 +172,8 @@ def bench_prefill(args, torch):
     from gqa_causal_attention_amd.workloads import make_workload
     t0 = time.time()
     wl = make_workload("llama3_8b_prefill_4k")
-    cfg, B, L = wl["cfg"], wl["batch"], wl["seq_len"]
+    wl["cfg"] = cfg = dict(wl["cfg"], **ROPE_VARIANTS[args.rope])
+    B, L = wl["batch"], wl["seq_len"]
     blk = Block(cfg, wl["weights"])
     x = torch.from_numpy(wl["x"]).cuda()
     y = torch.empty_like(x)
@@ -245,7 +246,8 @@ def bench_decode(args, torch):
     from gqa_causal_attention_amd.workloads import make_workload
     t0 = time.time()
     wl = make_workload("llama3_8b_decode_b64")
-    cfg, B, cap = wl["cfg"], wl["batch"], wl["capacity"]
+    wl["cfg"] = cfg = dict(wl["cfg"], **ROPE_VARIANTS[args.rope])
+    B, cap = wl["batch"], wl["capacity"]
     lengths = wl["lengths"]
     blk = Block(cfg, wl["weights"])
     st = blk.allocate_state(B, cap)
@@ -330,12 +332,26 @@ def cpu_baseline(pre, budget_s=20.0):
                       f"{el:.1f}s wall"}
 
 
+# RoPE options of the block on the same shapes: Llama 3.1's frequency ramp
+# (factor 8 over an original 8192-token context) changes only the table; half
+# rotary (64 of 128 dimensions) splits each head's RoPE lanes into rotated and
+# pass-through ones.
+ROPE_VARIANTS = {
+    "plain": {},
+    "llama31": {"rope_scaling": {"type": "llama3", "factor": 8.0, "low_freq_factor": 1.0,
+                                 "high_freq_factor": 4.0, "original_max_position_embeddings": 8192}},
+    "half_rotary": {"rope_dim": 64},
+}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rope", choices=list(ROPE_VARIANTS), default="plain",
+                    help="RoPE option of the benchmarked block (default: plain RoPE, every dimension)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="decode line only (profiling); no JSON headline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -382,7 +398,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "llama3-8b-shaped block prefill (d=4096, 32/8 heads, hd=128, IT=14336)",
-                   "batch": pre["B"], "seq_len": pre["L"], "parallelism": "none"},
+                   "batch": pre["B"], "seq_len": pre["L"], "parallelism": "none",
+                   **({"rope": args.rope} if args.rope != "plain" else {})},
         "prefill_mfma": pre["step"],
         "roofline": pre["roofline"],
         "cpu_baseline": cpu,

@@ -39,7 +39,12 @@ class Config(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("intermediate", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("max_positions", ctypes.c_int32), ("rope_theta", ctypes.c_float), ("norm_eps", ctypes.c_float),
                 ("attn_softcap", ctypes.c_float), ("norm", ctypes.c_int32), ("mlp", ctypes.c_int32),
-                ("qkv_bias", ctypes.c_int32), ("qk_norm", ctypes.c_int32), ("weight_dtype", ctypes.c_int32)]
+                ("qkv_bias", ctypes.c_int32), ("qk_norm", ctypes.c_int32), ("weight_dtype", ctypes.c_int32),
+                ("rope_dim", ctypes.c_int32), ("rope_scaling", ctypes.c_int32), ("rope_factor", ctypes.c_float),
+                ("rope_low_freq_factor", ctypes.c_float), ("rope_high_freq_factor", ctypes.c_float),
+                ("rope_original_max_positions", ctypes.c_int32)]
+
+ROPE_SCALING = {None: 0, "linear": 1, "llama3": 2}
 
 
 class Tensor(ctypes.Structure):
@@ -101,7 +106,25 @@ def make_config(cfg: dict) -> Config:
         norm=1 if cfg.get("norm", "rmsnorm") == "rmsnorm_offset" else 0,
         mlp=1 if cfg.get("mlp", "swiglu") == "geglu_tanh" else 0,
         qkv_bias=int(bool(cfg.get("qkv_bias"))), qk_norm=int(bool(cfg.get("qk_norm"))),
-        weight_dtype=GQA_BF16 if cfg.get("dtype", "f32") == "bf16" else GQA_F32)
+        weight_dtype=GQA_BF16 if cfg.get("dtype", "f32") == "bf16" else GQA_F32,
+        rope_dim=cfg.get("rope_dim") or 0, **_rope_scaling_fields(cfg.get("rope_scaling")))
+
+
+def _rope_scaling_fields(sc) -> dict:
+    """mojolearn ``rope_scaling`` (None, {"type": "linear", "factor": f} or
+    {"type": "llama3", "factor", "low_freq_factor", "high_freq_factor",
+    "original_max_position_embeddings"}) as the C config's fields."""
+    if not sc:
+        return {}
+    kind = sc.get("type", sc.get("rope_type"))
+    if kind not in ("linear", "llama3"):
+        raise ValueError(f"unknown rope_scaling type {kind!r}")
+    out = dict(rope_scaling=ROPE_SCALING[kind], rope_factor=float(sc["factor"]))
+    if kind == "llama3":
+        out.update(rope_low_freq_factor=float(sc["low_freq_factor"]),
+                   rope_high_freq_factor=float(sc["high_freq_factor"]),
+                   rope_original_max_positions=int(sc["original_max_position_embeddings"]))
+    return out
 
 
 def _stream_ptr(stream=None):

@@ -304,6 +304,37 @@ WsLayout layout_for(const gqa_block* blk, int B, int L) {
   return w;
 }
 
+// RoPE frequencies theta_i, i < rope_dim/2 (DantinoX "Core Layers" page,
+// Positional Encoding / RoPE: base^(-2i/d) with d the rotated dimensions),
+// scaled as mojolearn ``rope_scaling`` names: "linear" divides each by the
+// factor; "llama3" is Hugging Face's Llama 3 wavelength ramp (long
+// wavelengths divided by the factor, short ones kept, a linear blend in
+// n / wavelength between).  Double precision throughout.
+std::vector<double> rope_frequencies(const gqa_block_config& c) {
+  const int rd = c.rope_dim, half = rd / 2;
+  std::vector<double> inv(half);
+  const double f = c.rope_factor;
+  for (int i = 0; i < half; ++i) {
+    const double th = std::pow((double)c.rope_theta, -2.0 * i / rd);
+    double out = th;
+    if (c.rope_scaling == GQA_ROPE_LINEAR) {
+      out = th / f;
+    } else if (c.rope_scaling == GQA_ROPE_LLAMA3) {
+      const double lo = c.rope_low_freq_factor, hi = c.rope_high_freq_factor;
+      const double ctx = c.rope_original_max_positions;
+      const double wavelen = 2.0 * M_PI / th;
+      if (wavelen > ctx / lo) {
+        out = th / f;
+      } else if (!(wavelen < ctx / hi)) {
+        const double s = (ctx / wavelen - lo) / (hi - lo);
+        out = (1.0 - s) * th / f + s * th;
+      }
+    }
+    inv[i] = out;
+  }
+  return inv;
+}
+
 int check_config(const gqa_block_config* c) {
   if (!c) return fail(GQA_ERR_ARG, "config is NULL");
   if (c->d_model <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 || c->intermediate <= 0)
@@ -323,6 +354,18 @@ int check_config(const gqa_block_config* c) {
   if ((c->qkv_bias != 0 && c->qkv_bias != 1) || (c->qk_norm != 0 && c->qk_norm != 1))
     return fail(GQA_ERR_ARG, "qkv_bias and qk_norm must be 0 or 1");
   if (c->weight_dtype != GQA_F32 && c->weight_dtype != GQA_BF16) return fail(GQA_ERR_DTYPE, "unknown weight dtype");
+  if (c->rope_dim != 0 && (c->rope_dim < 2 || c->rope_dim > c->head_dim || c->rope_dim % 2))
+    return fail(GQA_ERR_ARG, "rope_dim (%d) must be 0 (= head_dim) or even in [2, head_dim=%d]", c->rope_dim,
+                c->head_dim);
+  if (c->rope_scaling != GQA_ROPE_PLAIN && c->rope_scaling != GQA_ROPE_LINEAR && c->rope_scaling != GQA_ROPE_LLAMA3)
+    return fail(GQA_ERR_ARG, "unknown rope_scaling kind %d", c->rope_scaling);
+  if (c->rope_scaling != GQA_ROPE_PLAIN && (!(c->rope_factor > 0.f) || !std::isfinite(c->rope_factor)))
+    return fail(GQA_ERR_ARG, "rope_factor must be > 0");
+  if (c->rope_scaling == GQA_ROPE_LLAMA3 &&
+      (!(c->rope_low_freq_factor > 0.f) || !(c->rope_high_freq_factor > c->rope_low_freq_factor) ||
+       !std::isfinite(c->rope_high_freq_factor) || c->rope_original_max_positions <= 0))
+    return fail(GQA_ERR_ARG, "llama3 rope scaling needs 0 < low_freq_factor < high_freq_factor and "
+                             "original_max_positions > 0");
   if (c->weight_dtype == GQA_BF16) {
     const int QW = c->n_heads * c->head_dim;
     if (c->d_model % 64 || QW % 64 || c->intermediate % 64)
@@ -474,7 +517,7 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
   }
   // 2. q/k/v projections (+ bias) in one GEMM over three weight segments (a
   // K-split GEMM leaves its partials to the RoPE/append kernel when it can sum them)
-  const bool fuse_qkv = bf && lay.p_qkv.splits > 1 && rope_append_fuses_reduce(hd, QW + 2 * KW, et);
+  const bool fuse_qkv = bf && lay.p_qkv.splits > 1 && rope_append_fuses_reduce(hd, c.rope_dim, QW + 2 * KW, et);
   {
     GemmArgs a{};
     a.A = h; a.lda = d;
@@ -498,7 +541,7 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
     r.cos_tab = blk->cos_tab; r.sin_tab = blk->sin_tab;
     r.q_norm = static_cast<const float*>(blk->w[W_QN]);
     r.k_norm = static_cast<const float*>(blk->w[W_KN]);
-    r.B = B; r.L = L; r.H = c.n_heads; r.KV = c.n_kv_heads; r.hd = hd;
+    r.B = B; r.L = L; r.H = c.n_heads; r.KV = c.n_kv_heads; r.hd = hd; r.rd = c.rope_dim;
     r.cap = st ? st->capacity : 0; r.window = c.window; r.offset = offset; r.eps = c.norm_eps;
     r.defer_append = st && c.window > 0 && L > 1;
     if (fuse_qkv) {
@@ -622,12 +665,13 @@ int gqa_block_create(const gqa_block_config* cfg, const gqa_tensor* weights, int
     gqa_block_destroy(blk);
     return code;
   };
-  // RoPE table: angle p * base^(-2i/hd) and its cos/sin in double, stored as float32.
-  const int half = cfg->head_dim / 2;
+  // RoPE table: angle p * theta_i and its cos/sin in double, stored as float32
+  // [max_positions, rope_dim/2].
+  if (blk->cfg.rope_dim == 0) blk->cfg.rope_dim = cfg->head_dim;
+  const int half = blk->cfg.rope_dim / 2;
   const size_t n = (size_t)cfg->max_positions * half;
   std::vector<float> ct(n), sn(n);
-  std::vector<double> inv(half);
-  for (int i = 0; i < half; ++i) inv[i] = std::pow((double)cfg->rope_theta, -2.0 * i / cfg->head_dim);
+  const std::vector<double> inv = rope_frequencies(blk->cfg);
   for (int p = 0; p < cfg->max_positions; ++p)
     for (int i = 0; i < half; ++i) {
       const double a = (double)p * inv[i];

@@ -84,11 +84,12 @@ struct RopeArgs {
   void* kcache;            // [B, KV, cap, hd] or null
   void* vcache;
   const int* lengths;      // [B] start positions (null: zeros)
-  const float* cos_tab;    // [max_positions, hd/2]
+  const float* cos_tab;    // [max_positions, rd/2]
   const float* sin_tab;
   const float* q_norm;     // [hd] or null
   const float* k_norm;
   int B, L, H, KV, hd, cap, window, offset;
+  int rd;                  // rotated dimensions (even, <= hd); hd .. rd-1 pass through
   int defer_append;        // 1: leave the cache to launch_kv_append (after attention)
   float eps;
   // Optional fused K-split reduction of the q/k/v GEMM: if `part` is set, the
@@ -100,7 +101,7 @@ struct RopeArgs {
   const float* bias[3];    // q, k, v biases (may be null)
 };
 // True if launch_rope_append takes `part` for this shape and element type.
-bool rope_append_fuses_reduce(int hd, int64_t ld, int elem);
+bool rope_append_fuses_reduce(int hd, int rd, int64_t ld, int elem);
 hipError_t launch_rope_append(const RopeArgs& a, int elem, hipStream_t s);
 hipError_t launch_kv_append(const RopeArgs& a, int elem, hipStream_t s);
 

@@ -4,13 +4,18 @@
 // then the KV key heads, then the KV value heads of the q|k|v projection row.
 // For q and k: optional RMSNorm over head_dim (mojolearn ``qk_norm``: Qwen3
 // style, before RoPE), then RoPE (DantinoX "Core Layers" page, Positional
-// Encoding / RoPE: each pair rotated by p * theta_i, theta_i = base^(-2i/hd))
-// on Hugging Face's rotate-half pairs (i, i + hd/2), reading cos/sin from a
-// float32 table indexed by the absolute position p = lengths[b] + t.  Lane i
-// holds pairs i, i + 64, ... so a pair never crosses lanes.
+// Encoding / RoPE: each pair rotated by p * theta_i) on Hugging Face's
+// rotate-half pairs (i, i + r/2) of the first r = rope_dim dimensions,
+// reading cos/sin from a float32 table [max_positions, r/2] indexed by the
+// absolute position p = lengths[b] + t; the table already holds the block's
+// frequencies (base, partial-rotary denominator, linear or Llama 3 scaling).
+// Dimensions r .. hd-1 pass through (partial rotary, mojolearn ``rope_dim``),
+// normalised like the rest under qk_norm.  Lane i holds pairs i, i + 64, ...
+// so a pair never crosses lanes.
 //
-// bf16 blocks with head_dim 64 / 128 / 256 use the vector form (a thread per
-// 4 pairs); other shapes the wave-per-head form.
+// bf16 blocks with head_dim 64 / 128 / 256 and rope_dim a multiple of 8 use
+// the vector form (a thread per 8 elements); other shapes the wave-per-head
+// form.
 //
 // Outputs: q rotated in place; this call's keys (rotated) and values into
 // knew/vnew [B, KV, L, hd]; and, with a cache, the same keys/values into
@@ -64,59 +69,74 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
     return;
   }
 
-  // q or k: load pairs (p, p + half) for p = lane, lane + 64, ...
-  constexpr int MAXP = 2;  // hd <= 256
-  float lo[MAXP], hi[MAXP];
+  // q or k: rotated pairs (p, p + rh) for p = lane, lane + 64, ... < rh, and
+  // the pass-through dimensions e = rd + lane, rd + lane + 64, ... < hd
+  constexpr int MAXP = 2, MAXR = 4;  // hd <= 256
+  const int rd = a.rd, rh = rd / 2;
+  float lo[MAXP], hi[MAXP], pt[MAXR];
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < MAXP; ++i) {
     const int p = lane + i * WAVE;
     lo[i] = hi[i] = 0.f;
-    if (p < half) {
+    if (p < rh) {
       lo[i] = to_f32(src[p]);
-      hi[i] = to_f32(src[p + half]);
+      hi[i] = to_f32(src[p + rh]);
       ss += lo[i] * lo[i] + hi[i] * hi[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < MAXR; ++i) {
+    const int e = rd + lane + i * WAVE;
+    pt[i] = 0.f;
+    if (e < hd) {
+      pt[i] = to_f32(src[e]);
+      ss += pt[i] * pt[i];
     }
   }
   const float* nw = kind == 0 ? a.q_norm : a.k_norm;
   float r = 1.f;
   if (nw) r = 1.0f / sqrtf(wave_sum(ss) / (float)hd + a.eps);
-  const float* ct = a.cos_tab + (int64_t)pos * half;
-  const float* st = a.sin_tab + (int64_t)pos * half;
-  T* kn = kind == 1 ? static_cast<T*>(a.knew) + new_off : nullptr;
+  auto gain = [&](int e) { return a.offset ? 1.0f + nw[e] : nw[e]; };
+  const float* ct = a.cos_tab + (int64_t)pos * rh;
+  const float* st = a.sin_tab + (int64_t)pos * rh;
+  T* dst = kind == 0 ? src : static_cast<T*>(a.knew) + new_off;
   T* kc = (kind == 1 && to_cache) ? static_cast<T*>(a.kcache) + cache_off : nullptr;
 #pragma unroll
   for (int i = 0; i < MAXP; ++i) {
     const int p = lane + i * WAVE;
-    if (p >= half) continue;
+    if (p >= rh) continue;
     float x1 = lo[i], x2 = hi[i];
     if (nw) {
-      const float g1 = a.offset ? 1.0f + nw[p] : nw[p];
-      const float g2 = a.offset ? 1.0f + nw[p + half] : nw[p + half];
-      x1 = x1 * r * g1;
-      x2 = x2 * r * g2;
+      x1 = x1 * r * gain(p);
+      x2 = x2 * r * gain(p + rh);
     }
-    const float c = ct[p], s = st[p];
-    const T y1 = from_f32<T>(x1 * c - x2 * s);
-    const T y2 = from_f32<T>(x2 * c + x1 * s);
-    if (kind == 0) {
-      src[p] = y1;
-      src[p + half] = y2;
-    } else {
-      kn[p] = y1;
-      kn[p + half] = y2;
-      if (kc) {
-        kc[p] = y1;
-        kc[p + half] = y2;
-      }
+    const float c = ct[p], sv = st[p];
+    const T y1 = from_f32<T>(x1 * c - x2 * sv);
+    const T y2 = from_f32<T>(x2 * c + x1 * sv);
+    dst[p] = y1;
+    dst[p + rh] = y2;
+    if (kc) {
+      kc[p] = y1;
+      kc[p + rh] = y2;
     }
+  }
+#pragma unroll
+  for (int i = 0; i < MAXR; ++i) {
+    const int e = rd + lane + i * WAVE;
+    if (e >= hd) continue;
+    const T y = from_f32<T>(nw ? pt[i] * r * gain(e) : pt[i]);
+    dst[e] = y;
+    if (kc) kc[e] = y;
   }
 }
 
-// Vector form for bf16 activations and head_dim 64 / 128 / 256: a thread
-// owns 4 consecutive pairs (p .. p+3, p+half .. p+half+3) of one head slot, so
-// every access is an 8-byte vector and a head is handled by half/4 adjacent
-// lanes (the qk-norm sum of squares is reduced across them with shuffles).
+// Vector form for bf16 activations and head_dim 64 / 128 / 256, rope_dim r a
+// multiple of 8: a head slot is handled by hd/8 adjacent lanes, each owning 8
+// elements as two 8-byte vectors.  Lane g < r/8 owns the rotated pairs
+// (4g .. 4g+3, 4g+r/2 .. 4g+r/2+3); lane g >= r/8 owns the pass-through
+// elements 8g .. 8g+7.  The qk-norm sum of squares is reduced across the
+// head's lanes with shuffles.
 template <int HD>
 __global__ __launch_bounds__(256) void rope_append_vec_kernel(RopeArgs a) {
   constexpr int HALF = HD / 2, GH = HALF / 4;  // lanes per head slot
@@ -137,14 +157,17 @@ __global__ __launch_bounds__(256) void rope_append_vec_kernel(RopeArgs a) {
   if (slot < a.H) { kind = 0; head = slot; src = row + head * HD; }
   else if (slot < a.H + a.KV) { kind = 1; head = slot - a.H; src = row + QW + head * HD; }
   else { kind = 2; head = slot - a.H - a.KV; src = row + QW + KW + head * HD; }
-  const int p = 4 * g;
+  const int rh = a.rd >> 1;
+  const bool rot = 4 * g < rh;
+  const int o1 = rot ? 4 * g : 8 * g;        // first 4 elements
+  const int o2 = rot ? 4 * g + rh : o1 + 4;  // second 4 (the rotation partners)
 
   bf16x4 lo = bf16x4{}, hi = bf16x4{};
   if (live && a.part) {
-    // fused K-split reduction: this row's columns c .. c+3 and c+HALF .. summed
-    // over the splits in order, plus the segment's bias, rounded as the GEMM
-    // epilogue would have stored them
-    const int64_t c = (src - row) + p;
+    // fused K-split reduction: this row's columns c .. c+3 and c-o1+o2 ..
+    // summed over the splits in order, plus the segment's bias, rounded as the
+    // GEMM epilogue would have stored them
+    const int64_t c = (src - row) + o1;
     const int64_t pstride = T_ * a.ld;
     const float* pr = a.part + tok * a.ld + c;
     f32x4 sl = f32x4{0.f, 0.f, 0.f, 0.f}, sh = sl;
@@ -154,7 +177,7 @@ __global__ __launch_bounds__(256) void rope_append_vec_kernel(RopeArgs a) {
       for (int u = 0; u < 4; ++u) {
         const float* q = pr + min(z0 + u, a.splits - 1) * pstride;
         tl[u] = *reinterpret_cast<const f32x4*>(q);
-        th[u] = *reinterpret_cast<const f32x4*>(q + HALF);
+        th[u] = *reinterpret_cast<const f32x4*>(q + (o2 - o1));
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
@@ -165,9 +188,9 @@ __global__ __launch_bounds__(256) void rope_append_vec_kernel(RopeArgs a) {
     }
     const float* bias = a.bias[kind];
     if (bias) {
-      const float* bb = bias + head * HD + p;
-      sl += *reinterpret_cast<const f32x4*>(bb);
-      sh += *reinterpret_cast<const f32x4*>(bb + HALF);
+      const float* bb = bias + head * HD;
+      sl += *reinterpret_cast<const f32x4*>(bb + o1);
+      sh += *reinterpret_cast<const f32x4*>(bb + o2);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -175,8 +198,8 @@ __global__ __launch_bounds__(256) void rope_append_vec_kernel(RopeArgs a) {
       hi[e] = from_f32<bf16>(sh[e]);
     }
   } else if (live) {
-    lo = *reinterpret_cast<const bf16x4*>(src + p);
-    hi = *reinterpret_cast<const bf16x4*>(src + p + HALF);
+    lo = *reinterpret_cast<const bf16x4*>(src + o1);
+    hi = *reinterpret_cast<const bf16x4*>(src + o2);
   }
   const int64_t new_off = (((int64_t)b * a.KV + head) * a.L + t) * HD;
   const bool to_cache = a.kcache && !a.defer_append && (a.window == 0 || t >= a.L - a.window);
@@ -199,33 +222,41 @@ __global__ __launch_bounds__(256) void rope_append_vec_kernel(RopeArgs a) {
       const float r = 1.0f / sqrtf(ss / (float)HD + a.eps);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float g1 = a.offset ? 1.0f + nw[p + e] : nw[p + e];
-        const float g2 = a.offset ? 1.0f + nw[p + HALF + e] : nw[p + HALF + e];
+        const float g1 = a.offset ? 1.0f + nw[o1 + e] : nw[o1 + e];
+        const float g2 = a.offset ? 1.0f + nw[o2 + e] : nw[o2 + e];
         x1[e] *= r * g1;
         x2[e] *= r * g2;
       }
     }
-    const f32x4 c = *reinterpret_cast<const f32x4*>(a.cos_tab + (int64_t)pos * HALF + p);
-    const f32x4 s = *reinterpret_cast<const f32x4*>(a.sin_tab + (int64_t)pos * HALF + p);
+    if (rot) {
+      const f32x4 c = *reinterpret_cast<const f32x4*>(a.cos_tab + (int64_t)pos * rh + o1);
+      const f32x4 s = *reinterpret_cast<const f32x4*>(a.sin_tab + (int64_t)pos * rh + o1);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      lo[e] = from_f32<bf16>(x1[e] * c[e] - x2[e] * s[e]);
-      hi[e] = from_f32<bf16>(x2[e] * c[e] + x1[e] * s[e]);
+      for (int e = 0; e < 4; ++e) {
+        lo[e] = from_f32<bf16>(x1[e] * c[e] - x2[e] * s[e]);
+        hi[e] = from_f32<bf16>(x2[e] * c[e] + x1[e] * s[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo[e] = from_f32<bf16>(x1[e]);
+        hi[e] = from_f32<bf16>(x2[e]);
+      }
     }
   }
   if (!live) return;
   if (kind == 0) {  // q, rotated (in place, or from the fused reduction)
-    *reinterpret_cast<bf16x4*>(src + p) = lo;
-    *reinterpret_cast<bf16x4*>(src + p + HALF) = hi;
+    *reinterpret_cast<bf16x4*>(src + o1) = lo;
+    *reinterpret_cast<bf16x4*>(src + o2) = hi;
     return;
   }
   bf16* dn = static_cast<bf16*>(kind == 1 ? a.knew : a.vnew) + new_off;
-  *reinterpret_cast<bf16x4*>(dn + p) = lo;
-  *reinterpret_cast<bf16x4*>(dn + p + HALF) = hi;
+  *reinterpret_cast<bf16x4*>(dn + o1) = lo;
+  *reinterpret_cast<bf16x4*>(dn + o2) = hi;
   if (to_cache) {
     bf16* dc = static_cast<bf16*>(kind == 1 ? a.kcache : a.vcache) + cache_off;
-    *reinterpret_cast<bf16x4*>(dc + p) = lo;
-    *reinterpret_cast<bf16x4*>(dc + p + HALF) = hi;
+    *reinterpret_cast<bf16x4*>(dc + o1) = lo;
+    *reinterpret_cast<bf16x4*>(dc + o2) = hi;
   }
 }
 
@@ -269,15 +300,19 @@ hipError_t launch_vec(const RopeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-bool rope_append_fuses_reduce(int hd, int64_t ld, int elem) {
-  return elem == kBF16 && ld % 4 == 0 && (hd == 64 || hd == 128 || hd == 256);
+// The vector form (the only one that takes `part`) covers these shapes.
+bool rope_append_fuses_reduce(int hd, int rd, int64_t ld, int elem) {
+  return elem == kBF16 && ld % 4 == 0 && (hd == 64 || hd == 128 || hd == 256) && rd % 8 == 0 && rd >= 8 &&
+         rd <= hd;
 }
 
 hipError_t launch_rope_append(const RopeArgs& a, int elem, hipStream_t s) {
   const int64_t waves = (int64_t)a.B * a.L * (a.H + 2 * a.KV);
   if (waves == 0) return hipSuccess;
-  if (a.part && (!rope_append_fuses_reduce(a.hd, a.ld, elem) || a.splits < 1)) return hipErrorInvalidValue;
-  if (elem == kBF16 && a.ld % 4 == 0) {
+  if (a.rd < 2 || a.rd > a.hd || a.rd % 2) return hipErrorInvalidValue;
+  const bool vec = rope_append_fuses_reduce(a.hd, a.rd, a.ld, elem);
+  if (a.part && (!vec || a.splits < 1)) return hipErrorInvalidValue;
+  if (vec) {
     if (a.hd == 64) return launch_vec<64>(a, s);
     if (a.hd == 128) return launch_vec<128>(a, s);
     if (a.hd == 256) return launch_vec<256>(a, s);

@@ -54,6 +54,8 @@ typedef enum {
 typedef enum { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype;
 typedef enum { GQA_NORM_RMS = 0, GQA_NORM_RMS_OFFSET = 1 } gqa_norm_kind;
 typedef enum { GQA_MLP_SWIGLU = 0, GQA_MLP_GEGLU_TANH = 1 } gqa_mlp_kind;
+/* RoPE frequency scaling (mojolearn ``rope_scaling``: None, "linear", "llama3"). */
+typedef enum { GQA_ROPE_PLAIN = 0, GQA_ROPE_LINEAR = 1, GQA_ROPE_LLAMA3 = 2 } gqa_rope_scaling;
 
 /* Block options: mojolearn TransformerBlock constructor parameters. */
 typedef struct {
@@ -78,6 +80,23 @@ typedef struct {
   int32_t weight_dtype;   /* gqa_dtype of the weights, the GEMM operands, the
                              activations between kernels and the KV cache.  x and y
                              are always float32 and the residual stream is float32. */
+  /* RoPE options (mojolearn ``rope_dim`` and ``rope_scaling``; frequencies of
+   * the DantinoX "Core Layers" page, Positional Encoding / RoPE).  A zeroed
+   * tail gives plain RoPE over every dimension. */
+  int32_t rope_dim;       /* rotated dimensions per head, r: 0 = head_dim, else even
+                             and in [2, head_dim].  Pairs (i, i + r/2), i < r/2, turn
+                             at p * base^(-2i/r); dimensions r .. hd-1 pass through
+                             (partial rotary) */
+  int32_t rope_scaling;   /* gqa_rope_scaling.  LINEAR: every frequency / rope_factor.
+                             LLAMA3: with wavelength w = 2 pi / freq and
+                             n = rope_original_max_positions, w > n / low_freq_factor
+                             divides by rope_factor, w < n / high_freq_factor keeps,
+                             between blends (1 - s) freq / factor + s freq with
+                             s = (n / w - low) / (high - low) */
+  float rope_factor;              /* > 0 (LINEAR, LLAMA3) */
+  float rope_low_freq_factor;     /* LLAMA3: > 0 and < rope_high_freq_factor */
+  float rope_high_freq_factor;    /* LLAMA3 */
+  int32_t rope_original_max_positions; /* LLAMA3: > 0 */
 } gqa_block_config;
 
 /* One weight tensor, keyed by its Hugging Face parameter name, in torch's
@@ -102,8 +121,8 @@ typedef struct gqa_block gqa_block;
 typedef struct gqa_state gqa_state;
 
 /* Validate the config and the weight table (names, shapes, dtypes), upload
- * the RoPE cos/sin table (angles formed in double precision, stored as
- * float32 [max_positions, hd/2]) and check every weight for non-finite values
+ * the RoPE cos/sin table (frequencies and angles formed in double precision,
+ * stored as float32 [max_positions, rope_dim/2]) and check every weight for non-finite values
  * (one device pass, synchronous, on the null stream).  Errors: ARG, SHAPE,
  * DTYPE, NONFINITE, UNSUPPORTED, HIP.  On success *out owns the block. */
 int gqa_block_create(const gqa_block_config* cfg, const gqa_tensor* weights, int32_t n_weights,

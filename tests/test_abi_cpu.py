@@ -84,6 +84,12 @@ def test_weight_table_errors(case, code):
 @pytest.mark.parametrize("field,value,code", [
     ("n_kv_heads", 3, -2), ("head_dim", 15, -2), ("head_dim", 512, -11), ("window", -1, -1),
     ("max_positions", 0, -1), ("rope_theta", 0.0, -1), ("attn_softcap", -1.0, -1),
+    ("rope_dim", 3, -1), ("rope_dim", 18, -1), ("rope_dim", -2, -1),
+    ("rope_scaling", {"type": "linear", "factor": 0.0}, -1),
+    ("rope_scaling", {"type": "llama3", "factor": 8.0, "low_freq_factor": 4.0, "high_freq_factor": 1.0,
+                      "original_max_position_embeddings": 8192}, -1),
+    ("rope_scaling", {"type": "llama3", "factor": 8.0, "low_freq_factor": 1.0, "high_freq_factor": 4.0,
+                      "original_max_position_embeddings": 0}, -1),
 ])
 def test_config_errors(field, value, code):
     cfg, W = random_block(2)
@@ -91,6 +97,19 @@ def test_config_errors(field, value, code):
     arr, n = _records(cfg, W)
     rc, msg = _create(cfg, arr, n)
     assert rc == code, msg
+
+
+def test_rope_scaling_kind_is_checked():
+    cfg, W = random_block(2, rope_scaling={"type": "yarn", "factor": 2.0})
+    with pytest.raises(ValueError):
+        make_config(cfg)
+    c = make_config(dict(cfg, rope_scaling=None))
+    c.rope_scaling = 7
+    lib = _lib()
+    arr, n = _records(cfg, W)
+    h = ctypes.c_void_p()
+    assert lib.gqa_block_create(ctypes.byref(c), arr, n, ctypes.byref(h)) == -1
+    assert "rope_scaling" in lib.gqa_last_error().decode()
 
 
 def test_bf16_shape_rule():
@@ -107,10 +126,14 @@ def test_valid_table_passes_validation():
     import torch
     if torch.cuda.is_available():
         pytest.skip("fake device pointers must not reach a GPU")
-    cfg, W = random_block(4, qkv_bias=True, qk_norm=True)
-    arr, n = _records(cfg, W)
-    rc, msg = _create(cfg, arr, n)
-    assert rc == -10, msg
+    for over in ({}, dict(rope_dim=6, rope_scaling={"type": "linear", "factor": 4.0}),
+                 dict(rope_dim=16, rope_scaling={"type": "llama3", "factor": 8.0, "low_freq_factor": 1.0,
+                                                 "high_freq_factor": 4.0,
+                                                 "original_max_position_embeddings": 8192})):
+        cfg, W = random_block(4, qkv_bias=True, qk_norm=True, **over)
+        arr, n = _records(cfg, W)
+        rc, msg = _create(cfg, arr, n)
+        assert rc == -10, msg
 
 
 def test_null_arguments():

@@ -52,6 +52,9 @@ def test_tiny_llama_prefill_then_decode(torch_cuda):
     check_close(y0, block_forward(cfg, W, x, dtype=np.float64), x, "f32", "stateless")
 
 
+LLAMA31_ROPE = {"type": "llama3", "factor": 8.0, "low_freq_factor": 1.0, "high_freq_factor": 4.0,
+                "original_max_position_embeddings": 8192}
+
 BF16_CASES = {
     # name: (block overrides, B, prefill L, continuation L, decode steps)
     "llama_g4_hd128": (dict(d_model=256, n_heads=8, n_kv_heads=2, head_dim=128, intermediate=512,
@@ -65,6 +68,16 @@ BF16_CASES = {
     "mha_g1": (dict(d_model=256, n_heads=2, n_kv_heads=2, head_dim=128, intermediate=256), 1, 70, 0, 2),
     "big_m_tiles": (dict(d_model=512, n_heads=4, n_kv_heads=1, head_dim=128, intermediate=768,
                          rope_theta=5e5), 1, 1100, 0, 1),
+    # RoPE options: the Llama 3.1 ramp; partial rotary with linear scaling and
+    # qk_norm (vector RoPE form: rotated and pass-through lanes); a rope_dim
+    # that is not a multiple of 8 (wave-per-head form)
+    "llama31_rope_scaling": (dict(d_model=256, n_heads=8, n_kv_heads=2, head_dim=128, intermediate=512,
+                                  rope_theta=5e5, rope_scaling=LLAMA31_ROPE), 2, 150, 37, 3),
+    "partial_rotary_linear_qknorm": (dict(d_model=256, n_heads=8, n_kv_heads=2, head_dim=128,
+                                          intermediate=256, rope_dim=32, qk_norm=True, qkv_bias=True,
+                                          rope_scaling={"type": "linear", "factor": 4.0}), 2, 90, 10, 3),
+    "partial_rotary_rd20_hd64": (dict(d_model=256, n_heads=4, n_kv_heads=2, head_dim=64, intermediate=256,
+                                      rope_dim=20, qk_norm=True), 1, 70, 6, 2),
 }
 
 
@@ -122,6 +135,10 @@ DECODE_GEMM_BLOCKS = {
     # no split: the fused bias / residual / gated epilogues (4- and 6-chunk depths)
     "fused": dict(d_model=512, n_heads=8, n_kv_heads=2, head_dim=64, intermediate=768, qkv_bias=True,
                   mlp="geglu_tanh"),
+    # split q/k/v GEMM with partial rotary: the RoPE kernel sums the partials
+    # of rotated and pass-through columns alike
+    "split_partial_rotary": dict(d_model=1024, n_heads=8, n_kv_heads=2, head_dim=128, intermediate=1280,
+                                 qkv_bias=True, rope_dim=64, rope_theta=5e5, rope_scaling=LLAMA31_ROPE),
 }
 
 
@@ -171,6 +188,12 @@ F32_CASES = {
     "bias_qknorm_g3": (dict(n_heads=6, n_kv_heads=2, head_dim=12, d_model=48, qkv_bias=True,
                             qk_norm=True), 3, 9, 4, 3),
     "odd_dims": (dict(d_model=50, n_heads=5, n_kv_heads=5, head_dim=10, intermediate=37), 1, 13, 0, 2),
+    "partial_rotary_llama3_window_qknorm": (dict(rope_dim=6, window=5, qk_norm=True,
+                                                 rope_scaling=dict(LLAMA31_ROPE,
+                                                                   original_max_position_embeddings=32)),
+                                            2, 19, 6, 5),
+    "partial_rotary_odd_linear": (dict(d_model=50, n_heads=5, n_kv_heads=5, head_dim=10, intermediate=37,
+                                       rope_dim=4, rope_scaling={"type": "linear", "factor": 2.5}), 1, 13, 3, 2),
 }
 
 
