@@ -28,12 +28,21 @@ REQUIRED_NAMES = (
 )
 BIAS_NAMES = ("q_proj.bias", "k_proj.bias", "v_proj.bias")
 QK_NORM_NAMES = ("q_norm.weight", "k_norm.weight")
+# Optional tensors of the page's other options, in the order they are drawn
+# (after the ones above, so turning an option on leaves earlier draws alone).
+O_BIAS_NAMES = ("o_proj.bias",)
+MLP_BIAS_NAMES = ("gate_proj.bias", "up_proj.bias", "down_proj.bias")
+SANDWICH_NAMES = ("pre_feedforward_layernorm.weight", "post_feedforward_layernorm.weight")
+NORM_BIAS_NAMES = ("input_layernorm.bias", "post_attention_layernorm.bias",
+                   "pre_feedforward_layernorm.bias", "post_feedforward_layernorm.bias")
+UNGATED_MLPS = ("gelu", "gelu_tanh")
 
 # Block configurations.  Keys mirror the C struct gqa_block_config; the
 # workload keys (batch, seq_len, ...) describe the synthetic run.
 _BASE = dict(window=0, rope_theta=10000.0, norm_eps=1e-6, attn_softcap=0.0,
              norm="rmsnorm", mlp="swiglu", qkv_bias=False, qk_norm=False,
-             max_positions=8192)
+             max_positions=8192, o_bias=False, mlp_bias=False, norm_bias=False,
+             sandwich_norms=False)
 
 LLAMA3_8B_BLOCK = dict(_BASE, d_model=4096, n_heads=32, n_kv_heads=8, head_dim=128,
                        intermediate=14336, rope_theta=500000.0, dtype="bf16")
@@ -88,6 +97,21 @@ def weight_shapes(cfg: dict) -> dict:
         shapes.update({"q_proj.bias": (qw,), "k_proj.bias": (kw,), "v_proj.bias": (kw,)})
     if cfg.get("qk_norm"):
         shapes.update({"q_norm.weight": (hd,), "k_norm.weight": (hd,)})
+    ungated = cfg.get("mlp", "swiglu") in UNGATED_MLPS
+    if ungated:
+        del shapes["gate_proj.weight"]
+    if cfg.get("o_bias"):
+        shapes["o_proj.bias"] = (d,)
+    if cfg.get("mlp_bias"):
+        if not ungated:
+            shapes["gate_proj.bias"] = (it,)
+        shapes.update({"up_proj.bias": (it,), "down_proj.bias": (d,)})
+    if cfg.get("sandwich_norms"):
+        shapes.update({n: (d,) for n in SANDWICH_NAMES})
+    if cfg.get("norm_bias"):
+        for n in NORM_BIAS_NAMES:
+            if n.replace(".bias", ".weight") in shapes:
+                shapes[n] = (d,)
     return shapes
 
 
@@ -107,19 +131,25 @@ def _is_norm_weight(name: str) -> bool:
     return name.endswith("layernorm.weight") or name in QK_NORM_NAMES
 
 
+def _is_norm_bias(name: str) -> bool:
+    return name.endswith("layernorm.bias")
+
+
 def draw_weights(cfg: dict, rng: np.random.Generator) -> dict:
     """Draw the block's tensors in the fixed order: required table, biases, q/k norms.
 
     Projection weights and biases: 0.02 * N(0, 1).  Norm gains: 1 + 0.1 * N(0, 1)
-    for a plain RMSNorm; for the (1 + w) RMSNorm the stored w is 0.1 * N(0, 1),
-    so the effective gain has the same law.
+    for a plain RMSNorm or LayerNorm; for the (1 + w) RMSNorm the stored w is
+    0.1 * N(0, 1), so the effective gain has the same law.  LayerNorm biases:
+    0.1 * N(0, 1).  Tensors an option does not use are not drawn.
     """
     shapes = weight_shapes(cfg)
-    order = list(REQUIRED_NAMES)
+    order = [n for n in REQUIRED_NAMES if n in shapes]
     if cfg.get("qkv_bias"):
         order += list(BIAS_NAMES)
     if cfg.get("qk_norm"):
         order += list(QK_NORM_NAMES)
+    order += [n for n in O_BIAS_NAMES + MLP_BIAS_NAMES + SANDWICH_NAMES + NORM_BIAS_NAMES if n in shapes]
     out = {}
     offset_norm = cfg.get("norm") == "rmsnorm_offset"
     for name in order:
@@ -129,6 +159,8 @@ def draw_weights(cfg: dict, rng: np.random.Generator) -> dict:
             w = z * np.float32(0.1)
             if not offset_norm:
                 w = w + np.float32(1.0)
+        elif _is_norm_bias(name):
+            w = z * np.float32(0.1)
         else:
             w = z * np.float32(0.02)
         out[name] = w.astype(np.float32)

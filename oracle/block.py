@@ -28,6 +28,19 @@ design notes of the repository):
     (i, i + r/2) of a head's first r dimensions with frequencies
     base^(-2i/r) and leaves dimensions r .. hd-1 as they are (Hugging Face's
     partial_rotary_factor convention, which the page's layer follows).
+  * ``norm='layernorm'`` uses the population variance (mean of squared
+    deviations); its biases exist only with ``norm_bias``.  qk_norm stays an
+    RMSNorm (the page: "RMS-normalize"), with gain 1 + w under
+    ``rmsnorm_offset`` and w otherwise.
+  * ``mlp``: 'gelu' / 'geglu' are the exact (erf) GELU, '_tanh' the tanh
+    approximation (the dew page calls the tanh gated form "geglu" and the erf
+    one "geglu_exact"; the mojolearn names are kept).  Ungated forms have no
+    gate_proj.
+  * Sandwich norms (not a mojolearn option; Gemma 2/3 as the dew pages
+    describe them): post_attention_layernorm normalises the attention output
+    before its residual add, pre_feedforward_layernorm is the MLP's input
+    norm and post_feedforward_layernorm normalises the MLP output before its
+    add, all of the block's norm kind (Hugging Face's names).
   * ``rope_scaling`` "linear" divides every frequency by its factor; "llama3"
     applies Hugging Face's Llama 3 wavelength ramp (``rope_inv_freq``); the
     page names both and their parameters but prints neither formula.
@@ -59,7 +72,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "rms_norm", "rope_inv_freq", "rope_cos_sin", "apply_rope", "silu", "gelu_tanh", "attention_row",
+    "rms_norm", "layer_norm", "gelu_erf", "MLP_KINDS", "rope_inv_freq", "rope_cos_sin", "apply_rope", "silu", "gelu_tanh", "attention_row",
     "OracleState", "block_forward", "block_step", "block_forward_rows",
 ]
 
@@ -81,6 +94,25 @@ def rms_norm(x: np.ndarray, w: np.ndarray, eps: float, offset: bool = False) -> 
     if offset:
         g = dt.type(1.0) + g
     return x / np.sqrt(ms + dt.type(eps)) * g
+
+
+def layer_norm(x: np.ndarray, w: np.ndarray, b: np.ndarray | None, eps: float) -> np.ndarray:
+    """LayerNorm over the last axis: (x - mu) / sqrt(var + eps) * gamma + beta.
+
+    DantinoX "Core Layers" page, Normalisation / LayerNorm: mean and variance
+    over the d features of each token (the population variance), eps inside
+    the square root, a gain and a bias.  mojolearn ``norm='layernorm'``; the
+    bias is present with ``norm_bias`` (else beta = 0).  Computed in the dtype
+    of ``x``.
+    """
+    dt = x.dtype
+    mu = np.mean(x, axis=-1, keepdims=True)
+    xc = x - mu
+    var = np.mean(xc * xc, axis=-1, keepdims=True)
+    y = xc / np.sqrt(var + dt.type(eps)) * w.astype(dt)
+    if b is not None:
+        y = y + b.astype(dt)
+    return y
 
 
 def rope_inv_freq(rot_dim: int, theta: float, scaling: dict | None = None) -> np.ndarray:
@@ -173,6 +205,29 @@ def gelu_tanh(z: np.ndarray) -> np.ndarray:
     t = z.dtype.type
     c = t(np.sqrt(2.0 / np.pi))
     return t(0.5) * z * (t(1.0) + np.tanh(c * (z + t(0.044715) * z * z * z)))
+
+
+def gelu_erf(z: np.ndarray) -> np.ndarray:
+    """GELU, exact form: z * Phi(z) = 0.5 z (1 + erf(z / sqrt(2))).
+
+    DantinoX page, Feed-Forward Network / GELU: x times the standard normal
+    CDF (the page prints the tanh approximation beside it).  mojolearn
+    ``mlp='gelu'`` (ungated) and ``'geglu'`` (gated) use this form; the
+    ``_tanh`` names the approximation.
+    """
+    from scipy.special import erf
+    t = z.dtype.type
+    return (t(0.5) * z * (t(1.0) + erf(z / t(np.sqrt(2.0))))).astype(z.dtype)
+
+
+# mojolearn ``mlp``: name -> (activation, gated)
+MLP_KINDS = {
+    "swiglu": (silu, True),
+    "geglu_tanh": (gelu_tanh, True),
+    "geglu": (gelu_erf, True),
+    "gelu_tanh": (gelu_tanh, False),
+    "gelu": (gelu_erf, False),
+}
 
 
 def attention_row(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos: np.ndarray,
@@ -307,7 +362,7 @@ def _project(cfg, W, x, dt, positions, layout):
     offset = cfg.get("norm", "rmsnorm") == "rmsnorm_offset"
     eps = cfg["norm_eps"]
     w = {k: v.astype(dt) for k, v in W.items()}
-    h = rms_norm(x, w["input_layernorm.weight"], eps, offset)
+    h = _norm(cfg, w, "input_layernorm", x)
     if layout == "rowwise":
         q = np.stack([np.stack([w["q_proj.weight"] @ h[b, t] for t in range(L)]) for b in range(B)])
         k = np.stack([np.stack([w["k_proj.weight"] @ h[b, t] for t in range(L)]) for b in range(B)])
@@ -330,21 +385,80 @@ def _project(cfg, W, x, dt, positions, layout):
     return w, q, k, v
 
 
-def _mlp(cfg, w, x1, layout):
-    offset = cfg.get("norm", "rmsnorm") == "rmsnorm_offset"
-    h2 = rms_norm(x1, w["post_attention_layernorm.weight"], cfg["norm_eps"], offset)
-    act = gelu_tanh if cfg.get("mlp", "swiglu") == "geglu_tanh" else silu
+def _norm(cfg, w, name, x):
+    """The block's norm kind (mojolearn ``norm``) applied with weights ``name``.*:
+    RMSNorm with gain w or 1 + w, or LayerNorm with gain w and, with
+    ``norm_bias``, bias ``name``.bias."""
+    kind = cfg.get("norm", "rmsnorm")
+    if kind == "layernorm":
+        return layer_norm(x, w[name + ".weight"], w.get(name + ".bias"), cfg["norm_eps"])
+    if kind not in ("rmsnorm", "rmsnorm_offset"):
+        raise ValueError(f"unknown norm {kind!r}")
+    return rms_norm(x, w[name + ".weight"], cfg["norm_eps"], kind == "rmsnorm_offset")
+
+
+def _attn_residual(cfg, w, x, ctx2, layout):
+    """x1 = x + o_proj(ctx) (+ o_proj.bias with ``o_bias``).  With sandwich
+    norms the attention output is normalised by post_attention_layernorm
+    before the add (Hugging Face's Gemma 2/3 naming; the dew DecoderBlock
+    page's output norms, and the gemma4 text page's block equations)."""
     if layout == "rowwise":
-        B, L, _ = x1.shape
-        out = np.empty_like(x1)
+        B, L, _ = x.shape
+        a = np.empty_like(x)
         for b in range(B):
             for t in range(L):
-                g = w["gate_proj.weight"] @ h2[b, t]
-                u = w["up_proj.weight"] @ h2[b, t]
-                out[b, t] = x1[b, t] + w["down_proj.weight"] @ (act(g) * u)
-        return out
-    m = act(h2 @ w["gate_proj.weight"].T) * (h2 @ w["up_proj.weight"].T)
-    return x1 + m @ w["down_proj.weight"].T
+                a[b, t] = w["o_proj.weight"] @ ctx2[b, t]
+    else:
+        a = ctx2 @ w["o_proj.weight"].T
+    if "o_proj.bias" in w:
+        a = a + w["o_proj.bias"]
+    if cfg.get("sandwich_norms"):
+        a = _norm(cfg, w, "post_attention_layernorm", a)
+    return x + a
+
+
+def _mlp(cfg, w, x1, layout):
+    """y = x1 + MLP(norm(x1)).
+
+    Gated (mojolearn ``mlp`` swiglu / geglu / geglu_tanh): down(act(gate(h)) *
+    up(h)); ungated (gelu / gelu_tanh): down(act(up(h))); each projection
+    adds its bias with ``mlp_bias``.  The pre-MLP norm is
+    post_attention_layernorm, or pre_feedforward_layernorm with sandwich norms,
+    which also normalise the MLP output by post_feedforward_layernorm before
+    the add.
+    """
+    sandwich = bool(cfg.get("sandwich_norms"))
+    h2 = _norm(cfg, w, "pre_feedforward_layernorm" if sandwich else "post_attention_layernorm", x1)
+    act, gated = MLP_KINDS[cfg.get("mlp", "swiglu")]
+    bg, bu, bd = w.get("gate_proj.bias"), w.get("up_proj.bias"), w.get("down_proj.bias")
+
+    def ff_row(h):  # one token, matrix-vector products
+        u = w["up_proj.weight"] @ h
+        if bu is not None:
+            u = u + bu
+        if gated:
+            g = w["gate_proj.weight"] @ h
+            if bg is not None:
+                g = g + bg
+            m = act(g) * u
+        else:
+            m = act(u)
+        o = w["down_proj.weight"] @ m
+        return o + bd if bd is not None else o
+
+    if layout == "rowwise":
+        B, L, _ = x1.shape
+        f = np.empty_like(x1)
+        for b in range(B):
+            for t in range(L):
+                f[b, t] = ff_row(h2[b, t])
+    else:
+        u = _linear(h2, w["up_proj.weight"], bu)
+        m = act(_linear(h2, w["gate_proj.weight"], bg)) * u if gated else act(u)
+        f = _linear(m, w["down_proj.weight"], bd)
+    if sandwich:
+        f = _norm(cfg, w, "post_feedforward_layernorm", f)
+    return x1 + f
 
 
 def block_forward(cfg: dict, W: dict, x: np.ndarray, state: OracleState | None = None,
@@ -432,13 +546,7 @@ def block_forward(cfg: dict, W: dict, x: np.ndarray, state: OracleState | None =
         state.lengths += L
 
     ctx2 = ctx.reshape(B, L, H * hd)
-    if layout == "rowwise":
-        x1 = np.empty_like(x)
-        for b in range(B):
-            for t in range(L):
-                x1[b, t] = x[b, t] + w["o_proj.weight"] @ ctx2[b, t]
-    else:
-        x1 = x + ctx2 @ w["o_proj.weight"].T
+    x1 = _attn_residual(cfg, w, x, ctx2, layout)
     return _mlp(cfg, w, x1, layout)
 
 
@@ -488,7 +596,7 @@ def block_forward_rows(cfg: dict, W: dict, x: np.ndarray, rows, state: OracleSta
     for b, items in by_row.items():
         s0 = int(start[b])
         xb = x[b].astype(dt)
-        h = rms_norm(xb, w["input_layernorm.weight"], eps, offset)              # [L, d]
+        h = _norm(cfg, w, "input_layernorm", xb)                                # [L, d]
         k = _linear(h, w["k_proj.weight"], w.get("k_proj.bias")).reshape(L, KV, hd)
         v = _linear(h, w["v_proj.weight"], w.get("v_proj.bias")).reshape(L, KV, hd)
         if cfg.get("qk_norm"):
@@ -513,8 +621,8 @@ def block_forward_rows(cfg: dict, W: dict, x: np.ndarray, rows, state: OracleSta
         cq, sq = _rope(cfg, s0 + ts)
         q = apply_rope(q, cq[:, None, :], sq[:, None, :])
         ctx = attention_row(q, kall, vall, s0 + ts, kpos, window, cfg.get("attn_softcap", 0.0))
-        x1 = xb[ts] + ctx.reshape(len(ts), H * hd) @ w["o_proj.weight"].T
-        y = _mlp(cfg, w, x1[None], "batched")[0]
+        x1 = _attn_residual(cfg, w, xb[ts][None], ctx.reshape(1, len(ts), H * hd), "batched")
+        y = _mlp(cfg, w, x1, "batched")[0]
         for (i, _), yr in zip(items, y):
             out[i] = yr
     return out
