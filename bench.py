@@ -51,12 +51,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def mlp_matrices(cfg):
+    """Weight matrices of the MLP: gate, up, down (ungated MLPs have no gate)."""
+    return 2 if cfg.get("mlp", "swiglu") in ("gelu", "gelu_tanh") else 3
+
+
 def prefill_flops(cfg, B, L):
     """Algorithmic flops of one block prefill: GEMMs plus unmasked attention pairs."""
     d, H, KV, hd, IT = cfg["d_model"], cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["intermediate"]
     QW, KW = H * hd, KV * hd
     T = B * L
-    gemm = 2 * T * (d * (QW + 2 * KW) + QW * d + 3 * d * IT)
+    gemm = 2 * T * (d * (QW + 2 * KW) + QW * d + mlp_matrices(cfg) * d * IT)
     W = cfg.get("window", 0)
     pairs = 0
     for t in range(L):
@@ -69,7 +74,7 @@ def decode_bytes(cfg, lengths, elem=2):
     d, KV, hd, IT, H = cfg["d_model"], cfg["n_kv_heads"], cfg["head_dim"], cfg["intermediate"], cfg["n_heads"]
     QW, KW = H * hd, KV * hd
     B = len(lengths)
-    weights = (d * (QW + 2 * KW) + QW * d + 3 * d * IT) * elem
+    weights = (d * (QW + 2 * KW) + QW * d + mlp_matrices(cfg) * d * IT) * elem
     W = cfg.get("window", 0)
     keys = sum(min(int(p) + 1, W) if W else int(p) + 1 for p in lengths)
     kv_read = keys * KV * hd * 2 * elem          # every attended key and value once (incl. the new one)
@@ -172,7 +177,8 @@ def bench_prefill(args, torch):
     from gqa_causal_attention_amd.workloads import make_workload
     t0 = time.time()
     wl = make_workload("llama3_8b_prefill_4k")
-    wl["cfg"] = cfg = dict(wl["cfg"], **ROPE_VARIANTS[args.rope])
+    wl["cfg"] = cfg = dict(wl["cfg"], **VARIANTS[args.variant])
+    wl["weights"] = variant_weights(wl, cfg)
     B, L = wl["batch"], wl["seq_len"]
     blk = Block(cfg, wl["weights"])
     x = torch.from_numpy(wl["x"]).cuda()
@@ -209,10 +215,12 @@ def bench_prefill(args, torch):
     gemm_f, attn_f = prefill_flops(cfg, B, L)
     d, IT = cfg["d_model"], cfg["intermediate"]
     T = B * L
+    gated = mlp_matrices(cfg) == 3
+    mlp_in = "gemm_gate_up" if gated else "gemm_up"
     per_kernel_flops = {
         "gemm_qkv": 2 * T * d * (cfg["n_heads"] + 2 * cfg["n_kv_heads"]) * cfg["head_dim"],
         "gemm_o": 2 * T * cfg["n_heads"] * cfg["head_dim"] * d,
-        "gemm_gate_up": 2 * T * d * 2 * IT,
+        mlp_in: 2 * T * d * (2 if gated else 1) * IT,
         "gemm_down": 2 * T * IT * d,
         "attn_prefill": attn_f,
     }
@@ -225,14 +233,15 @@ def bench_prefill(args, torch):
     log("[prefill] per-kernel (HIP events over the timed region):")
     for k, v in breakdown.items():
         log(f"   {k:16s} {v}")
-    gu = breakdown["gemm_gate_up"]
-    achieved = per_kernel_flops["gemm_gate_up"] / (gu["avg_ms"] * 1e-3) / 1e12
-    tr = stored_traffic()
-    roofline = {"bound": "mfma", "kernel": "gemm_gate_up", "achieved": round(achieved, 1),
+    gu = breakdown[mlp_in]
+    achieved = per_kernel_flops[mlp_in] / (gu["avg_ms"] * 1e-3) / 1e12
+    # the stored counter record is the plain block's gate/up launch
+    tr = stored_traffic() if args.variant == "plain" else None
+    roofline = {"bound": "mfma", "kernel": mlp_in, "achieved": round(achieved, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": tr["traffic_bytes"] if tr else None,
-                "algorithmic_bytes": 2 * (T * d + 2 * IT * d + T * IT),
-                "flops_per_launch": per_kernel_flops["gemm_gate_up"]}
+                "algorithmic_bytes": 2 * (T * d + (2 if gated else 1) * IT * d + T * IT),
+                "flops_per_launch": per_kernel_flops[mlp_in]}
     total_f = gemm_f + attn_f
     step_tflops = total_f / (ms * 1e-3) / 1e12
     return dict(cfg=cfg, B=B, L=L, ms=ms, ms_eager=ms_eager, tokens_per_s=T / (ms * 1e-3), roofline=roofline,
@@ -246,7 +255,8 @@ def bench_decode(args, torch):
     from gqa_causal_attention_amd.workloads import make_workload
     t0 = time.time()
     wl = make_workload("llama3_8b_decode_b64")
-    wl["cfg"] = cfg = dict(wl["cfg"], **ROPE_VARIANTS[args.rope])
+    wl["cfg"] = cfg = dict(wl["cfg"], **VARIANTS[args.variant])
+    wl["weights"] = variant_weights(wl, cfg)
     B, cap = wl["batch"], wl["capacity"]
     lengths = wl["lengths"]
     blk = Block(cfg, wl["weights"])
@@ -332,16 +342,34 @@ def cpu_baseline(pre, budget_s=20.0):
                       f"{el:.1f}s wall"}
 
 
-# RoPE options of the block on the same shapes: Llama 3.1's frequency ramp
-# (factor 8 over an original 8192-token context) changes only the table; half
-# rotary (64 of 128 dimensions) splits each head's RoPE lanes into rotated and
-# pass-through ones.
-ROPE_VARIANTS = {
+# Options of the block on the same 8B shapes (the default is the plain
+# block): Llama 3.1's RoPE ramp (factor 8 over an original 8192-token context)
+# changes only the table; half rotary (64 of 128 dimensions) splits each head's
+# RoPE lanes into rotated and pass-through ones; Gemma-style sandwich norms add
+# two output norms ((1 + w) RMSNorm, tanh GeGLU); LayerNorm with every bias;
+# an ungated exact-GELU MLP (no gate_proj: two thirds of the MLP weights).
+VARIANTS = {
     "plain": {},
     "llama31": {"rope_scaling": {"type": "llama3", "factor": 8.0, "low_freq_factor": 1.0,
                                  "high_freq_factor": 4.0, "original_max_position_embeddings": 8192}},
     "half_rotary": {"rope_dim": 64},
+    "gemma_sandwich": {"norm": "rmsnorm_offset", "mlp": "geglu_tanh", "sandwich_norms": True},
+    "layernorm_biases": {"norm": "layernorm", "norm_bias": True, "qkv_bias": True, "o_bias": True,
+                         "mlp_bias": True},
+    "ungated_gelu": {"mlp": "gelu"},
 }
+
+
+def variant_weights(wl, cfg):
+    """The workload's weights for a variant config: the same draws for the
+    tensors both have, the variant's extra tensors drawn after them."""
+    from gqa_causal_attention_amd.workloads import draw_weights, weight_shapes
+    W = wl["weights"]
+    shapes = weight_shapes(cfg)
+    if set(shapes) == set(W):
+        return W
+    extra = draw_weights(cfg, np.random.default_rng(12345))
+    return {k: (W[k] if k in W else extra[k]) for k in shapes}
 
 
 def main():
@@ -350,8 +378,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--rope", choices=list(ROPE_VARIANTS), default="plain",
-                    help="RoPE option of the benchmarked block (default: plain RoPE, every dimension)")
+    ap.add_argument("--variant", choices=list(VARIANTS), default="plain",
+                    help="block options on the same shapes (default: the plain Llama-shaped block)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="decode line only (profiling); no JSON headline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -399,7 +427,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "llama3-8b-shaped block prefill (d=4096, 32/8 heads, hd=128, IT=14336)",
                    "batch": pre["B"], "seq_len": pre["L"], "parallelism": "none",
-                   **({"rope": args.rope} if args.rope != "plain" else {})},
+                   **({"variant": args.variant} if args.variant != "plain" else {})},
         "prefill_mfma": pre["step"],
         "roofline": pre["roofline"],
         "cpu_baseline": cpu,

@@ -42,7 +42,11 @@ class Config(ctypes.Structure):
                 ("qkv_bias", ctypes.c_int32), ("qk_norm", ctypes.c_int32), ("weight_dtype", ctypes.c_int32),
                 ("rope_dim", ctypes.c_int32), ("rope_scaling", ctypes.c_int32), ("rope_factor", ctypes.c_float),
                 ("rope_low_freq_factor", ctypes.c_float), ("rope_high_freq_factor", ctypes.c_float),
-                ("rope_original_max_positions", ctypes.c_int32)]
+                ("rope_original_max_positions", ctypes.c_int32), ("o_bias", ctypes.c_int32),
+                ("mlp_bias", ctypes.c_int32), ("norm_bias", ctypes.c_int32), ("sandwich_norms", ctypes.c_int32)]
+
+NORM_KINDS = {"rmsnorm": 0, "rmsnorm_offset": 1, "layernorm": 2}
+MLP_KINDS = {"swiglu": 0, "geglu_tanh": 1, "geglu": 2, "gelu": 3, "gelu_tanh": 4}
 
 ROPE_SCALING = {None: 0, "linear": 1, "llama3": 2}
 
@@ -103,11 +107,19 @@ def make_config(cfg: dict) -> Config:
         head_dim=cfg["head_dim"], intermediate=cfg["intermediate"], window=cfg.get("window", 0),
         max_positions=cfg.get("max_positions", 8192), rope_theta=cfg.get("rope_theta", 10000.0),
         norm_eps=cfg.get("norm_eps", 1e-6), attn_softcap=cfg.get("attn_softcap", 0.0) or 0.0,
-        norm=1 if cfg.get("norm", "rmsnorm") == "rmsnorm_offset" else 0,
-        mlp=1 if cfg.get("mlp", "swiglu") == "geglu_tanh" else 0,
+        norm=_kind(NORM_KINDS, cfg.get("norm", "rmsnorm"), "norm"),
+        mlp=_kind(MLP_KINDS, cfg.get("mlp", "swiglu"), "mlp"),
         qkv_bias=int(bool(cfg.get("qkv_bias"))), qk_norm=int(bool(cfg.get("qk_norm"))),
+        o_bias=int(bool(cfg.get("o_bias"))), mlp_bias=int(bool(cfg.get("mlp_bias"))),
+        norm_bias=int(bool(cfg.get("norm_bias"))), sandwich_norms=int(bool(cfg.get("sandwich_norms"))),
         weight_dtype=GQA_BF16 if cfg.get("dtype", "f32") == "bf16" else GQA_F32,
         rope_dim=cfg.get("rope_dim") or 0, **_rope_scaling_fields(cfg.get("rope_scaling")))
+
+
+def _kind(table: dict, name: str, what: str) -> int:
+    if name not in table:
+        raise ValueError(f"unknown {what} {name!r} (one of {', '.join(table)})")
+    return table[name]
 
 
 def _rope_scaling_fields(sc) -> dict:

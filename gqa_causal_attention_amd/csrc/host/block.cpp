@@ -47,12 +47,26 @@ int fail(int code, const char* fmt, ...) {
 
 enum WIdx {
   W_IN_NORM, W_POST_NORM, W_Q, W_K, W_V, W_O, W_GATE, W_UP, W_DOWN,
-  W_QB, W_KB, W_VB, W_QN, W_KN, W_COUNT
+  W_QB, W_KB, W_VB, W_QN, W_KN,
+  W_OB, W_GB, W_UB, W_DB, W_PRE_FF, W_POST_FF, W_IN_NB, W_POST_NB, W_PRE_FFB, W_POST_FFB, W_COUNT
 };
 const char* const kNames[W_COUNT] = {
     "input_layernorm.weight", "post_attention_layernorm.weight", "q_proj.weight", "k_proj.weight",
     "v_proj.weight", "o_proj.weight", "gate_proj.weight", "up_proj.weight", "down_proj.weight",
-    "q_proj.bias", "k_proj.bias", "v_proj.bias", "q_norm.weight", "k_norm.weight"};
+    "q_proj.bias", "k_proj.bias", "v_proj.bias", "q_norm.weight", "k_norm.weight",
+    "o_proj.bias", "gate_proj.bias", "up_proj.bias", "down_proj.bias",
+    "pre_feedforward_layernorm.weight", "post_feedforward_layernorm.weight",
+    "input_layernorm.bias", "post_attention_layernorm.bias", "pre_feedforward_layernorm.bias",
+    "post_feedforward_layernorm.bias"};
+
+bool mlp_gated(int mlp) { return mlp == GQA_MLP_SWIGLU || mlp == GQA_MLP_GEGLU_TANH || mlp == GQA_MLP_GEGLU; }
+int mlp_act(int mlp) {
+  switch (mlp) {
+    case GQA_MLP_GEGLU_TANH: case GQA_MLP_GELU_TANH: return kActGeluTanh;
+    case GQA_MLP_GEGLU: case GQA_MLP_GELU: return kActGelu;
+    default: return kActSilu;
+  }
+}
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -282,7 +296,8 @@ WsLayout layout_for(const gqa_block* blk, int B, int L) {
     const int M = (int)T;
     w.p_qkv = plan_gemm(M, QW + 2 * KW, d, false);
     w.p_o = plan_gemm(M, d, QW, false);
-    w.p_gu = plan_gemm(M, IT, d, true);
+    const bool gated = mlp_gated(c.mlp);
+    w.p_gu = plan_gemm(M, IT, d, gated);
     w.p_down = plan_gemm(M, d, IT, false);
     size_t part = 0;
     auto need = [&](const GemmPlan& p, size_t nb) {
@@ -290,7 +305,7 @@ WsLayout layout_for(const gqa_block* blk, int B, int L) {
     };
     need(w.p_qkv, QW + 2 * (size_t)KW);
     need(w.p_o, d);
-    need(w.p_gu, 2 * (size_t)IT);
+    need(w.p_gu, (gated ? 2 : 1) * (size_t)IT);
     need(w.p_down, d);
     if (part) w.part = take(part);
     if (L == 1 && attention_decode_bf16_supported(c.head_dim, blk->G) && B <= attention_decode_max_rows()) {
@@ -349,10 +364,16 @@ int check_config(const gqa_block_config* c) {
   if (!(c->norm_eps >= 0.f) || !std::isfinite(c->norm_eps)) return fail(GQA_ERR_ARG, "norm_eps must be >= 0");
   if (!(c->attn_softcap >= 0.f) || !std::isfinite(c->attn_softcap))
     return fail(GQA_ERR_ARG, "attn_softcap must be >= 0 (0 = off)");
-  if (c->norm != GQA_NORM_RMS && c->norm != GQA_NORM_RMS_OFFSET) return fail(GQA_ERR_ARG, "unknown norm kind");
-  if (c->mlp != GQA_MLP_SWIGLU && c->mlp != GQA_MLP_GEGLU_TANH) return fail(GQA_ERR_ARG, "unknown mlp kind");
-  if ((c->qkv_bias != 0 && c->qkv_bias != 1) || (c->qk_norm != 0 && c->qk_norm != 1))
-    return fail(GQA_ERR_ARG, "qkv_bias and qk_norm must be 0 or 1");
+  if (c->norm != GQA_NORM_RMS && c->norm != GQA_NORM_RMS_OFFSET && c->norm != GQA_NORM_LAYER)
+    return fail(GQA_ERR_ARG, "unknown norm kind");
+  if (c->mlp < GQA_MLP_SWIGLU || c->mlp > GQA_MLP_GELU_TANH) return fail(GQA_ERR_ARG, "unknown mlp kind");
+  for (int f : {c->qkv_bias, c->qk_norm, c->o_bias, c->mlp_bias, c->norm_bias, c->sandwich_norms})
+    if (f != 0 && f != 1)
+      return fail(GQA_ERR_ARG, "qkv_bias, qk_norm, o_bias, mlp_bias, norm_bias and sandwich_norms must be 0 or 1");
+  if (c->norm_bias && c->norm != GQA_NORM_LAYER) return fail(GQA_ERR_ARG, "norm_bias needs norm = LayerNorm");
+  if (!norm_supported(c->d_model))
+    return fail(GQA_ERR_UNSUPPORTED, "d_model %d is beyond the norm kernels (16384 when a multiple of 4, "
+                                     "else 12288)", c->d_model);
   if (c->weight_dtype != GQA_F32 && c->weight_dtype != GQA_BF16) return fail(GQA_ERR_DTYPE, "unknown weight dtype");
   if (c->rope_dim != 0 && (c->rope_dim < 2 || c->rope_dim > c->head_dim || c->rope_dim % 2))
     return fail(GQA_ERR_ARG, "rope_dim (%d) must be 0 (= head_dim) or even in [2, head_dim=%d]", c->rope_dim,
@@ -382,11 +403,22 @@ int check_weights(const gqa_block_config* c, const gqa_tensor* ws, int n, const 
   const int64_t d = c->d_model, hd = c->head_dim, QW = (int64_t)c->n_heads * hd,
                 KW = (int64_t)c->n_kv_heads * hd, IT = c->intermediate;
   const int64_t shapes[W_COUNT][2] = {{d, 0},  {d, 0},  {QW, d}, {KW, d}, {KW, d}, {d, QW}, {IT, d},
-                                      {IT, d}, {d, IT}, {QW, 0}, {KW, 0}, {KW, 0}, {hd, 0}, {hd, 0}};
+                                      {IT, d}, {d, IT}, {QW, 0}, {KW, 0}, {KW, 0}, {hd, 0}, {hd, 0},
+                                      {d, 0},  {IT, 0}, {IT, 0}, {d, 0},  {d, 0},  {d, 0},  {d, 0},
+                                      {d, 0},  {d, 0},  {d, 0}};
+  const bool gated = mlp_gated(c->mlp);
   bool wanted[W_COUNT];
   for (int i = 0; i < W_COUNT; ++i) wanted[i] = i <= W_DOWN;
+  if (!gated) wanted[W_GATE] = false;
   if (c->qkv_bias) wanted[W_QB] = wanted[W_KB] = wanted[W_VB] = true;
   if (c->qk_norm) wanted[W_QN] = wanted[W_KN] = true;
+  if (c->o_bias) wanted[W_OB] = true;
+  if (c->mlp_bias) wanted[W_UB] = wanted[W_DB] = true, wanted[W_GB] = gated;
+  if (c->sandwich_norms) wanted[W_PRE_FF] = wanted[W_POST_FF] = true;
+  if (c->norm_bias) {
+    wanted[W_IN_NB] = wanted[W_POST_NB] = true;
+    if (c->sandwich_norms) wanted[W_PRE_FFB] = wanted[W_POST_FFB] = true;
+  }
   for (int i = 0; i < W_COUNT; ++i) out[i] = nullptr;
   for (int t = 0; t < n; ++t) {
     const gqa_tensor& w = ws[t];
@@ -493,7 +525,7 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
     pa.splits = p.splits;
     pa.k_split = a.K / p.splits;
     pa.partial = part;
-    pa.bump = nullptr;
+    if (!defer_reduce) pa.bump = nullptr;  // the reduce kernel advances the lengths instead
     {
       Scope sc(tm, name, s);
       HIP_TRY(launch_gemm_bf16(pa, mode, kEpiPartial, p.tile, s));
@@ -509,11 +541,27 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
     return GQA_OK;
   };
 
-  // 1. input RMSNorm (flags non-finite x)
+  // Norm steps: the block's kind with a weight (and LayerNorm bias) pair.
+  const int nk = c.norm == GQA_NORM_LAYER ? kNormLayer : c.norm == GQA_NORM_RMS_OFFSET ? kNormRmsOffset : kNormRms;
+  auto spec = [&](int wi, int bi) {
+    return NormSpec{static_cast<const float*>(blk->w[wi]), static_cast<const float*>(blk->w[bi]), nk};
+  };
+  auto norm = [&](const char* name, NormArgs na) -> int {
+    na.d = d;
+    na.eps = c.norm_eps;
+    Scope sc(tm, name, s);
+    HIP_TRY(launch_norm(na, et, T, s));
+    return GQA_OK;
+  };
+  const bool sandwich = c.sandwich_norms != 0;
+  const float* o_bias = static_cast<const float*>(blk->w[W_OB]);
+  const float* down_bias = static_cast<const float*>(blk->w[W_DB]);
+
+  // 1. input norm (flags non-finite x)
   {
-    Scope sc(tm, "rmsnorm", s);
-    HIP_TRY(launch_rmsnorm(x, static_cast<const float*>(blk->w[W_IN_NORM]), h, et, T, d, c.norm_eps, offset,
-                           blk->status, s));
+    NormArgs na{};
+    na.x = x; na.norm = spec(W_IN_NORM, W_IN_NB); na.out = h; na.flag = blk->status;
+    if (int r = norm("rmsnorm", na)) return r;
   }
   // 2. q/k/v projections (+ bias) in one GEMM over three weight segments (a
   // K-split GEMM leaves its partials to the RoPE/append kernel when it can sum them)
@@ -592,47 +640,87 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
     Scope sc(tm, "kv_append", s);
     HIP_TRY(launch_kv_append(r, et, s));
   }
-  // 5. o_proj + residual: x1 = x + ctx Wo^T (float32)
-  const bool fuse_o = bf && lay.p_o.splits > 1 && rmsnorm_fuses_reduce(d);
+  // 5. o_proj (+ bias) and the residual: x1 = x + ctx Wo^T.  With sandwich
+  // norms the projection's output is normalised first (post_attention_layernorm),
+  // so the GEMM writes it alone (float32, into y, which is free until step 8)
+  // and the norm kernel forms x1.  A K-split decode GEMM leaves its partials
+  // to that kernel.
+  const bool fuse_o = bf && lay.p_o.splits > 1;
   {
     GemmArgs a{};
     a.A = ctx; a.lda = QW;
     a.B[0] = a.B[1] = a.B[2] = blk->w[W_O];
     a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = d;
+    a.bias[0] = o_bias;
     a.M = T; a.N = d; a.K = QW;
-    a.C = x1; a.ldc = d; a.resid = x; a.ldr = d;
+    a.C = sandwich ? y : x1; a.ldc = d; a.resid = sandwich ? nullptr : x; a.ldr = d;
     if (int r = gemm("gemm_o", a, kModeSeg, kEpiResid, lay.p_o, fuse_o)) return r;
   }
-  // 6. post-attention RMSNorm (summing o_proj's K-split partials + x into x1 first when fused)
-  if (fuse_o) {
-    Scope sc(tm, "resid_rmsnorm", s);
-    HIP_TRY(launch_resid_rmsnorm(part, lay.p_o.splits, x, x1, static_cast<const float*>(blk->w[W_POST_NORM]), h2, et,
-                                 T, d, c.norm_eps, offset, s));
-  } else {
-    Scope sc(tm, "rmsnorm", s);
-    HIP_TRY(launch_rmsnorm(x1, static_cast<const float*>(blk->w[W_POST_NORM]), h2, et, T, d, c.norm_eps, offset,
-                           nullptr, s));
-  }
-  // 7. gate/up + act(gate) * up
+  // 6. the MLP's input norm (post_attention_layernorm; pre_feedforward_layernorm
+  // with sandwich norms), forming x1 first where step 5 left it undone
   {
+    NormArgs na{};
+    if (fuse_o) {
+      na.part = part; na.splits = lay.p_o.splits; na.bias = o_bias;
+    } else {
+      na.x = sandwich ? y : x1;
+    }
+    if (sandwich) na.out_norm = spec(W_POST_NORM, W_POST_NB);
+    if (fuse_o || sandwich) {
+      na.resid = x; na.x1 = x1;
+    }
+    na.norm = sandwich ? spec(W_PRE_FF, W_PRE_FFB) : spec(W_POST_NORM, W_POST_NB);
+    na.out = h2;
+    if (int r = norm(fuse_o || sandwich ? "resid_rmsnorm" : "rmsnorm", na)) return r;
+  }
+  // 7. gate/up (+ biases) and act(gate) * up; ungated MLPs: act(up (+ bias))
+  if (mlp_gated(c.mlp)) {
     GemmArgs a{};
     a.A = h2; a.lda = d;
     a.B[0] = blk->w[W_GATE]; a.B[1] = blk->w[W_UP]; a.B[2] = nullptr;
+    a.bias[0] = static_cast<const float*>(blk->w[W_GB]);
+    a.bias[1] = static_cast<const float*>(blk->w[W_UB]);
     a.M = T; a.N = IT; a.K = d;
     a.C = act; a.ldc = IT;
-    a.act = c.mlp == GQA_MLP_GEGLU_TANH ? kActGeluTanh : kActSilu;
+    a.act = mlp_act(c.mlp);
     if (int r = gemm("gemm_gate_up", a, kModeGated, kEpiGated, lay.p_gu)) return r;
+  } else {
+    GemmArgs a{};
+    a.A = h2; a.lda = d;
+    a.B[0] = a.B[1] = a.B[2] = blk->w[W_UP];
+    a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = IT;
+    a.bias[0] = a.bias[1] = a.bias[2] = static_cast<const float*>(blk->w[W_UB]);
+    a.M = T; a.N = IT; a.K = d;
+    a.C = act; a.ldc = IT;
+    a.act = mlp_act(c.mlp);
+    if (int r = gemm("gemm_up", a, kModeSeg, kEpiStore, lay.p_gu)) return r;
   }
-  // 8. down + residual: y = x1 + act Wd^T; the last kernel also advances the lengths
+  // 8. down (+ bias) and the residual: y = x1 + act Wd^T; with sandwich norms
+  // y = x1 + post_feedforward_layernorm(act Wd^T), the norm kernel reading the
+  // GEMM's output (or its K-split partials) from y.  The down GEMM also
+  // advances the lengths (no later kernel reads them).
+  const bool fuse_down = sandwich && bf && lay.p_down.splits > 1;
   {
     GemmArgs a{};
     a.A = act; a.lda = IT;
     a.B[0] = a.B[1] = a.B[2] = blk->w[W_DOWN];
     a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = d;
+    a.bias[0] = down_bias;
     a.M = T; a.N = d; a.K = IT;
-    a.C = y; a.ldc = d; a.resid = x1; a.ldr = d;
+    a.C = y; a.ldc = d; a.resid = sandwich ? nullptr : x1; a.ldr = d;
     if (st) { a.bump = lengths; a.bump_n = B; a.bump_by = L; }
-    if (int r = gemm("gemm_down", a, kModeSeg, kEpiResid, lay.p_down)) return r;
+    if (int r = gemm("gemm_down", a, kModeSeg, kEpiResid, lay.p_down, fuse_down)) return r;
+  }
+  if (sandwich) {
+    NormArgs na{};
+    if (fuse_down) {
+      na.part = part; na.splits = lay.p_down.splits; na.bias = down_bias;
+    } else {
+      na.x = y;
+    }
+    na.out_norm = spec(W_POST_FF, W_POST_FFB);
+    na.resid = x1; na.x1 = y;
+    if (int r = norm("resid_norm_out", na)) return r;
   }
   if (st)
     for (int b = 0; b < B; ++b) st->lengths[b] += L;
@@ -689,7 +777,8 @@ int gqa_block_create(const gqa_block_config* cfg, const gqa_tensor* weights, int
 
   // Non-finite weights are refused before any computation.
   const int64_t d = cfg->d_model, hd = cfg->head_dim, QW = blk->QW, KW = blk->KW, IT = cfg->intermediate;
-  const int64_t counts[W_COUNT] = {d, d, QW * d, KW * d, KW * d, d * QW, IT * d, IT * d, d * IT, QW, KW, KW, hd, hd};
+  const int64_t counts[W_COUNT] = {d, d, QW * d, KW * d, KW * d, d * QW, IT * d, IT * d, d * IT, QW, KW, KW, hd, hd,
+                                   d, IT, IT, d, d, d, d, d, d, d};
   for (int i = 0; i < W_COUNT; ++i) {
     if (!blk->w[i]) continue;
     const bool matrix = i >= W_Q && i <= W_DOWN;

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.h"
+
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -46,6 +48,41 @@ __device__ __forceinline__ float gelu_tanh(float z) {
   const float c = 0.7978845608028654f;  // sqrt(2/pi)
   float u = c * (z + 0.044715f * z * z * z);
   return 0.5f * z * (1.0f + tanh_exp(u));
+}
+
+// GELU, exact form: z * Phi(z) = 0.5 z (1 + erf(z / sqrt(2))) (DantinoX
+// "Core Layers" page, Feed-Forward Network / GELU; erff from the device math
+// library).
+__device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.7071067811865476f)); }
+
+// The MLP activation named by an ActKind value (launch.h).
+__device__ __forceinline__ float act_fn(int act, float g) {
+  if (act == kActGeluTanh) return gelu_tanh(g);
+  if (act == kActGelu) return gelu_erf(g);
+  if (act == kActNone) return g;
+  return silu(g);
+}
+template <int ACT>
+__device__ __forceinline__ float act_t(float g) {
+  if constexpr (ACT == kActGeluTanh) return gelu_tanh(g);
+  else if constexpr (ACT == kActGelu) return gelu_erf(g);
+  else if constexpr (ACT == kActNone) return g;
+  else return silu(g);
+}
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+// Calls f(IntC<ACT>{}) for the run-time activation, so an epilogue loop is
+// compiled once per activation with no per-element branch.
+template <typename F>
+__device__ __forceinline__ void with_act(int act, F&& f) {
+  switch (act) {
+    case kActGeluTanh: f(IntC<kActGeluTanh>{}); break;
+    case kActGelu: f(IntC<kActGelu>{}); break;
+    case kActNone: f(IntC<kActNone>{}); break;
+    default: f(IntC<kActSilu>{}); break;
+  }
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -48,10 +48,6 @@ __device__ __forceinline__ const bf16* b_row(const GemmArgs& a, int tn, int r, i
   }
 }
 
-__device__ __forceinline__ float apply_act(int act, float g) {
-  return act == kActGeluTanh ? gelu_tanh(g) : silu(g);
-}
-
 template <int BM, int BN, int WGM, int WGN, int MODE, int EPI, int WPOS>
 __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int NT = WGM * WGN * 64;
@@ -181,6 +177,9 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_bf16_kernel(GemmArgs a)
   }
 
   // ---- epilogue: accumulator (i, lane) holds row (i/4)*8 + (lane/32)*4 + i%4, column lane%32 ----
+  // (the activation is resolved once: one compiled loop per activation)
+  with_act(EPI == kEpiGated || EPI == kEpiStore ? a.act : (int)kActNone, [&](auto act_c) {
+  constexpr int ACT = decltype(act_c)::value;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -192,8 +191,9 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_bf16_kernel(GemmArgs a)
         for (int j = 0; j < FN / 2; ++j) {
           const int n = tn * (BN / 2) + wn * (WTN / 2) + j * 32 + (lane & 31);
           if (n < a.N) {
-            const float g = acc[i][j][e], u = acc[i][j + FN / 2][e];
-            static_cast<bf16*>(a.C)[(int64_t)m * a.ldc + n] = from_f32<bf16>(apply_act(a.act, g) * u);
+            const float g = acc[i][j][e] + (a.bias[0] ? a.bias[0][n] : 0.f);
+            const float u = acc[i][j + FN / 2][e] + (a.bias[1] ? a.bias[1][n] : 0.f);
+            static_cast<bf16*>(a.C)[(int64_t)m * a.ldc + n] = from_f32<bf16>(act_t<ACT>(g) * u);
           }
         }
       } else {
@@ -220,17 +220,20 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_bf16_kernel(GemmArgs a)
             const int64_t n = (int64_t)tn * BN + cb;
             if (n >= a.N) continue;
             if (EPI == kEpiResid) {
-              static_cast<float*>(a.C)[(int64_t)m * a.ldc + n] = a.resid[(int64_t)m * a.ldr + n] + v;
+              const float t = v + (a.bias[0] ? a.bias[0][n] : 0.f);
+              static_cast<float*>(a.C)[(int64_t)m * a.ldc + n] = a.resid ? a.resid[(int64_t)m * a.ldr + n] + t : t;
             } else {  // kEpiStore
               const int s = seg_of(a, n);
               const float b = a.bias[s] ? a.bias[s][n - (s == 0 ? 0 : a.seg_end[s - 1])] : 0.f;
-              static_cast<bf16*>(a.C)[(int64_t)m * a.ldc + n] = from_f32<bf16>(v + b);
+              const float t = v + b;
+              static_cast<bf16*>(a.C)[(int64_t)m * a.ldc + n] = from_f32<bf16>(act_t<ACT>(t));
             }
           }
         }
       }
     }
   }
+  });
 }
 
 // Sum of the K-split partials in split order, then the epilogue.
@@ -250,19 +253,23 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a) {
     if (MODE == kModeGated) su += *reinterpret_cast<const f32x4*>(p + a.N + n);
   }
   if (EPI == kEpiResid) {
-    const f32x4 r = *reinterpret_cast<const f32x4*>(a.resid + m * a.ldr + n);
-    *reinterpret_cast<f32x4*>(static_cast<float*>(a.C) + m * a.ldc + n) = r + s;
+    if (a.bias[0]) s += *reinterpret_cast<const f32x4*>(a.bias[0] + n);
+    if (a.resid) s = *reinterpret_cast<const f32x4*>(a.resid + m * a.ldr + n) + s;
+    *reinterpret_cast<f32x4*>(static_cast<float*>(a.C) + m * a.ldc + n) = s;
   } else {
     OutT* c = static_cast<OutT*>(a.C) + m * a.ldc + n;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float v;
       if (EPI == kEpiGated) {
-        v = apply_act(a.act, s[e]) * su[e];
+        const float g = s[e] + (a.bias[0] ? a.bias[0][n + e] : 0.f);
+        const float u = su[e] + (a.bias[1] ? a.bias[1][n + e] : 0.f);
+        v = act_fn(a.act, g) * u;
       } else {
         const int64_t col = n + e;
         const int sg = seg_of(a, col);
         v = s[e] + (a.bias[sg] ? a.bias[sg][col - (sg == 0 ? 0 : a.seg_end[sg - 1])] : 0.f);
+        if (a.act != kActNone) v = act_fn(a.act, v);
       }
       c[e] = from_f32<OutT>(v);
     }

@@ -76,9 +76,6 @@ __device__ __forceinline__ int seg_of(const GemmArgs& a, int64_t n) {
   return n < a.seg_end[0] ? 0 : (n < a.seg_end[1] ? 1 : 2);
 }
 
-__device__ __forceinline__ float act_fn(int act, float g) {
-  return act == kActGeluTanh ? gelu_tanh(g) : silu(g);
-}
 
 // Global row pointer of B-tile row r (K offset k0) for tile column tn.  Gated
 // mode: each wave's WTN B rows are WTN/2 gate rows then the WTN/2 up rows of
@@ -292,6 +289,21 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
     step((KS - 1) & 1, (kt + 1) % ST, 0);
   }
 
+  // The activation (gated and store epilogues) and the presence of gate/up
+  // biases are resolved once here, so each epilogue loop below is compiled
+  // for one activation with no per-element branch.
+  const bool gbias = EPI == kEpiGated && (a.bias[0] || a.bias[1]);
+  auto epilogue = [&](auto act_c, auto bias_c) {
+    constexpr int ACT = decltype(act_c)::value;
+    constexpr bool GBIAS = decltype(bias_c)::value != 0;
+    // gate / up values of output column n (biases added when present)
+    auto gated = [&](float g, float u, int n) {
+      if constexpr (GBIAS) {
+        if (a.bias[0]) g += a.bias[0][n];
+        if (a.bias[1]) u += a.bias[1][n];
+      }
+      return act_t<ACT>(g) * u;
+    };
   // ---- epilogue through LDS (16x16 MFMA; residual and q/k/v epilogues): 64
   // rows at a time the owning waves write their accumulators into a float32
   // staging tile, then all threads read it back row-major and apply the
@@ -319,9 +331,10 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
           const int r = rb - pass * PR + MM::row(e, lane);
           if constexpr (MODE == kModeGated) {
 #pragma unroll
-            for (int jj = 0; jj < FN / 2; ++jj)
-              stg[r * SW + wn * (WTN / 2) + jj * 16 + (lane & 15)] =
-                  act_fn(a.act, acc[i][jj][e]) * acc[i][jj + FN / 2][e];
+            for (int jj = 0; jj < FN / 2; ++jj) {
+              const int n = min(col0 + wn * (WTN / 2) + jj * 16 + (lane & 15), a.N - 1);
+              stg[r * SW + wn * (WTN / 2) + jj * 16 + (lane & 15)] = gated(acc[i][jj][e], acc[i][jj + FN / 2][e], n);
+            }
           } else {
 #pragma unroll
             for (int jj = 0; jj < FN; ++jj) stg[r * SW + wn * WTN + jj * 16 + (lane & 15)] = acc[i][jj][e];
@@ -336,8 +349,10 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
         if (m >= a.M || n >= a.N) continue;
         const f32x4 v = *reinterpret_cast<const f32x4*>(stg + r * SW + c);
         if constexpr (EPI == kEpiResid) {
-          const f32x4 rv = *reinterpret_cast<const f32x4*>(a.resid + (int64_t)m * a.ldr + n);
-          *reinterpret_cast<f32x4*>(static_cast<float*>(a.C) + (int64_t)m * a.ldc + n) = rv + v;
+          f32x4 t = v;
+          if (a.bias[0]) t += *reinterpret_cast<const f32x4*>(a.bias[0] + n);
+          if (a.resid) t = *reinterpret_cast<const f32x4*>(a.resid + (int64_t)m * a.ldr + n) + t;
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.C) + (int64_t)m * a.ldc + n) = t;
         } else {
           bf16x4 o;
 #pragma unroll
@@ -346,6 +361,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
             if constexpr (EPI == kEpiStore) {
               const int sg = seg_of(a, n + e);
               if (a.bias[sg]) x += a.bias[sg][n + e - (sg == 0 ? 0 : a.seg_end[sg - 1])];
+              x = act_t<ACT>(x);
             }
             o[e] = from_f32<bf16>(x);
           }
@@ -359,6 +375,17 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
   // ---- direct epilogue: accumulator element e of block (i, j) is row i * MF + MM::row(e, lane),
   // B row / column j * MF + lane % MF of the wave tile ----
   const int lcol = lane % MF;
+  // gate / up biases of this lane's columns, loaded once (the output stores
+  // below would otherwise keep the compiler from hoisting them)
+  float bgv[FN / 2], buv[FN / 2];
+  if constexpr (EPI == kEpiGated && GBIAS) {
+#pragma unroll
+    for (int j = 0; j < FN / 2; ++j) {
+      const int n = min(tn * (BN / 2) + wn * (WTN / 2) + j * MF + lcol, a.N - 1);
+      bgv[j] = a.bias[0] ? a.bias[0][n] : 0.f;
+      buv[j] = a.bias[1] ? a.bias[1][n] : 0.f;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -369,10 +396,12 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
 #pragma unroll
         for (int j = 0; j < FN / 2; ++j) {
           const int n = tn * (BN / 2) + wn * (WTN / 2) + j * MF + lcol;
-          if (n < a.N) {
-            const float g = acc[i][j][e], u = acc[i][j + FN / 2][e];
-            static_cast<bf16*>(a.C)[(int64_t)m * a.ldc + n] = from_f32<bf16>(act_fn(a.act, g) * u);
+          float g = acc[i][j][e], u = acc[i][j + FN / 2][e];
+          if constexpr (GBIAS) {
+            g += bgv[j];
+            u += buv[j];
           }
+          if (n < a.N) static_cast<bf16*>(a.C)[(int64_t)m * a.ldc + n] = from_f32<bf16>(act_t<ACT>(g) * u);
         }
       } else {
 #pragma unroll
@@ -397,16 +426,28 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
             const int64_t n = (int64_t)tn * BN + cb;
             if (n >= a.N) continue;
             if (EPI == kEpiResid) {
-              static_cast<float*>(a.C)[(int64_t)m * a.ldc + n] = a.resid[(int64_t)m * a.ldr + n] + v;
+              const float t = v + (a.bias[0] ? a.bias[0][n] : 0.f);
+              static_cast<float*>(a.C)[(int64_t)m * a.ldc + n] = a.resid ? a.resid[(int64_t)m * a.ldr + n] + t : t;
             } else {  // kEpiStore
               const int s = seg_of(a, n);
               const float b = a.bias[s] ? a.bias[s][n - (s == 0 ? 0 : a.seg_end[s - 1])] : 0.f;
-              static_cast<bf16*>(a.C)[(int64_t)m * a.ldc + n] = from_f32<bf16>(v + b);
+              static_cast<bf16*>(a.C)[(int64_t)m * a.ldc + n] = from_f32<bf16>(act_t<ACT>(v + b));
             }
           }
         }
       }
     }
+  }
+  };
+  if constexpr (EPI == kEpiGated || EPI == kEpiStore) {
+    with_act(a.act, [&](auto act_c) {
+      if (gbias)
+        epilogue(act_c, IntC<1>{});
+      else
+        epilogue(act_c, IntC<0>{});
+    });
+  } else {
+    epilogue(IntC<kActNone>{}, IntC<0>{});
   }
 }
 

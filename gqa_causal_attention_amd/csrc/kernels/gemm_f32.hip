@@ -81,15 +81,17 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
       const int64_t n = n0 + tx + 16 * j;
       if (n >= a.N) continue;
       if (EPI == kEpiGated) {
-        const float g = acc[0][i][j];
-        const float act = a.act == kActGeluTanh ? gelu_tanh(g) : silu(g);
-        C[m * a.ldc + n] = act * acc[NB - 1][i][j];
+        const float g = acc[0][i][j] + (a.bias[0] ? a.bias[0][n] : 0.f);
+        const float u = acc[NB - 1][i][j] + (a.bias[1] ? a.bias[1][n] : 0.f);
+        C[m * a.ldc + n] = act_fn(a.act, g) * u;
       } else if (EPI == kEpiResid) {
-        C[m * a.ldc + n] = a.resid[m * a.ldr + n] + acc[0][i][j];
+        const float v = acc[0][i][j] + (a.bias[0] ? a.bias[0][n] : 0.f);
+        C[m * a.ldc + n] = a.resid ? a.resid[m * a.ldr + n] + v : v;
       } else {
         const int s = n < a.seg_end[0] ? 0 : (n < a.seg_end[1] ? 1 : 2);
         const float b = a.bias[s] ? a.bias[s][n - (s == 0 ? 0 : a.seg_end[s - 1])] : 0.f;
-        C[m * a.ldc + n] = acc[0][i][j] + b;
+        const float v = acc[0][i][j] + b;
+        C[m * a.ldc + n] = a.act != kActNone ? act_fn(a.act, v) : v;
       }
     }
   }

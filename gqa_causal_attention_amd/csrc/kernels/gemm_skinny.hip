@@ -44,10 +44,6 @@ constexpr int SK_D = 2;              // weight chunks in flight per wave (regist
 constexpr int SK_KS = SK_KX / 32;    // MFMA k-steps per chunk
 constexpr int SK_MINW = 4, SK_MAXW = 8;  // waves per workgroup
 
-__device__ __forceinline__ float act_of(int act, float g) {
-  return act == kActGeluTanh ? gelu_tanh(g) : silu(g);
-}
-
 __device__ __forceinline__ int seg_index(const GemmArgs& a, int64_t n) {
   return n < a.seg_end[0] ? 0 : (n < a.seg_end[1] ? 1 : 2);
 }
@@ -206,6 +202,8 @@ __global__ __launch_bounds__(NWV * 64, 1) void gemm_skinny_kernel(GemmArgs a) {
   if constexpr (MODE == kModeGated && EPI == kEpiGated) {
     // gate rows 4 lg + e (lanes 0-31) and up rows 8 + 4 (lg - 2) + e (lanes
     // 32-63) are the same columns 8 g + 4 (lg & 1) + e: bring up to the gate lanes
+    with_act(a.act, [&](auto act_c) {
+    constexpr int ACT = decltype(act_c)::value;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       f32x4 up;
@@ -214,14 +212,20 @@ __global__ __launch_bounds__(NWV * 64, 1) void gemm_skinny_kernel(GemmArgs a) {
       const int m = 16 * t + lr;
       const int64_t col = 8 * g + 4 * (lg & 1);
       if (lane < 32 && m < a.M && col < a.N) {
+        f32x4 gv = acc[t];
+        if (a.bias[0]) gv += *reinterpret_cast<const f32x4*>(a.bias[0] + col);
+        if (a.bias[1]) up += *reinterpret_cast<const f32x4*>(a.bias[1] + col);
         bf16x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = from_f32<bf16>(act_of(a.act, acc[t][e]) * up[e]);
+        for (int e = 0; e < 4; ++e) o[e] = from_f32<bf16>(act_t<ACT>(gv[e]) * up[e]);
         *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.C) + (int64_t)m * a.ldc + col) = o;
       }
     }
+    });
     return;
   }
+  with_act(EPI == kEpiStore ? a.act : (int)kActNone, [&](auto act_c) {
+  constexpr int ACT = decltype(act_c)::value;
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int m = 16 * t + lr;
@@ -238,21 +242,25 @@ __global__ __launch_bounds__(NWV * 64, 1) void gemm_skinny_kernel(GemmArgs a) {
       if constexpr (EPI == kEpiPartial) {
         *reinterpret_cast<f32x4*>(a.partial + ((int64_t)z * a.M + m) * a.N + n) = v;
       } else if constexpr (EPI == kEpiResid) {
-        const f32x4 rv = *reinterpret_cast<const f32x4*>(a.resid + (int64_t)m * a.ldr + n);
-        *reinterpret_cast<f32x4*>(static_cast<float*>(a.C) + (int64_t)m * a.ldc + n) = rv + v;
-      } else {  // kEpiStore (+ bias); a segment boundary may fall inside the 4 columns
+        f32x4 r = v;
+        if (a.bias[0]) r += *reinterpret_cast<const f32x4*>(a.bias[0] + n);
+        if (a.resid) r = *reinterpret_cast<const f32x4*>(a.resid + (int64_t)m * a.ldr + n) + r;
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.C) + (int64_t)m * a.ldc + n) = r;
+      } else {  // kEpiStore (+ bias, act); a segment boundary may fall inside the 4 columns
         bf16x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int64_t col = n + e;
           const int s = seg_index(a, col);
           const float b = a.bias[s] ? a.bias[s][col - (s == 0 ? 0 : a.seg_end[s - 1])] : 0.f;
-          o[e] = from_f32<bf16>(v[e] + b);
+          const float x = v[e] + b;
+          o[e] = from_f32<bf16>(act_t<ACT>(x));
         }
         *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.C) + (int64_t)m * a.ldc + n) = o;
       }
     }
   }
+  });
 }
 
 template <int MT, int MODE, int EPI>

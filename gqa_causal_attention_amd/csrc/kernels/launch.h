@@ -15,25 +15,27 @@ enum GemmMode {
   kModeGated = 1,  // gate/up pair: output column n reads gate row n and up row n
 };
 enum GemmEpi {
-  kEpiStore = 0,    // C = acc (+ bias), stored in the activation type
-  kEpiResid = 1,    // C (float32) = resid + acc
-  kEpiGated = 2,    // C = act(acc_gate) * acc_up, stored in the activation type
+  kEpiStore = 0,    // C = act(acc + bias) (act kActNone: acc + bias), in the activation type
+  kEpiResid = 1,    // C (float32) = resid + (acc + bias[0]); resid and bias may be null
+  kEpiGated = 2,    // C = act(acc_gate + bias[0]) * (acc_up + bias[1]), in the activation type
   kEpiPartial = 3,  // float32 partial sums of one K split (split-K; raw B-row order)
 };
-enum ActKind { kActSilu = 0, kActGeluTanh = 1 };
+// MLP activations (the values act_fn in common.h switches on).
+enum ActKind { kActNone = 0, kActSilu = 1, kActGeluTanh = 2, kActGelu = 3 };
 
 struct GemmArgs {
   const void* A;           // [M, K] activations, row stride lda
   int64_t lda;
   const void* B[3];        // weight segments [rows_s, K] (row stride K)
   int64_t seg_end[3];      // cumulative row ends of the segments (kModeSeg)
-  const float* bias[3];    // per-segment bias (may be null)
+  const float* bias[3];    // kEpiStore: per-segment bias; kEpiResid: bias[0]; kEpiGated: gate, up
+                           // biases (each may be null)
   int M, N, K;             // N = output columns (kModeGated: IT)
   void* C;                 // output, row stride ldc
   int64_t ldc;
   const float* resid;      // kEpiResid: [M, N] float32, row stride ldr
   int64_t ldr;
-  int act;                 // ActKind for kEpiGated
+  int act;                 // ActKind (kEpiGated; kEpiStore when not kActNone)
   float* partial;          // kEpiPartial: [splits, M, NB] float32, NB = B rows
   int splits;              // number of K splits (grid z)
   int k_split;             // K elements per split (multiple of 64)
@@ -68,13 +70,31 @@ hipError_t launch_gemm_f32(const GemmArgs& a, int mode, int epi, hipStream_t s);
 // kEpiGated) writing a.C; `out_type` is the element type of a.C for Store/Gated.
 hipError_t launch_splitk_reduce(const GemmArgs& a, int mode, int epi, int out_type, hipStream_t s);
 
-hipError_t launch_rmsnorm(const float* x, const float* w, void* out, int out_type, int rows, int d,
-                          float eps, int offset, int* nonfinite_flag, hipStream_t s);
-// Fused K-split reduction + residual + RMSNorm: x1 = resid + sum over z < splits
-// of part[z, row, :] (written to x1, float32), then out = rmsnorm(x1).
-bool rmsnorm_fuses_reduce(int d);
-hipError_t launch_resid_rmsnorm(const float* part, int splits, const float* resid, float* x1, const float* w,
-                                void* out, int out_type, int rows, int d, float eps, int offset, hipStream_t s);
+// Row normalisation with its residual plumbing (norm.hip).
+enum NormKind { kNormRms = 0, kNormRmsOffset = 1, kNormLayer = 2 };
+struct NormSpec {
+  const float* w;          // gain [d]; null: this norm step is skipped
+  const float* b;          // LayerNorm bias [d] or null
+  int kind;                // NormKind
+};
+// Per row, each step optional: t = x + sum_z part[z] (+ bias); t = out_norm(t);
+// t = resid + t; x1 = t; out = norm(t).  x and part may not both be null.
+struct NormArgs {
+  const float* x;          // [rows, d] float32 (non-finite values set *flag)
+  const float* part;       // [splits, rows, d] K-split partial sums, or null
+  int splits;
+  const float* bias;       // [d] projection bias, or null
+  NormSpec out_norm;       // sandwich norm of a sublayer output
+  const float* resid;      // [rows, d] residual stream, or null
+  float* x1;               // [rows, d] float32 store of t after the residual add, or null
+  NormSpec norm;           // out = norm(t), written in out_type
+  void* out;
+  int d;
+  float eps;
+  int* flag;
+};
+bool norm_supported(int d);
+hipError_t launch_norm(const NormArgs& a, int out_type, int rows, hipStream_t s);
 
 struct RopeArgs {
   void* qkv;               // [T, ld] activations: q | k | v columns

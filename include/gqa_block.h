@@ -52,8 +52,16 @@ typedef enum {
 } gqa_status;
 
 typedef enum { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype;
-typedef enum { GQA_NORM_RMS = 0, GQA_NORM_RMS_OFFSET = 1 } gqa_norm_kind;
-typedef enum { GQA_MLP_SWIGLU = 0, GQA_MLP_GEGLU_TANH = 1 } gqa_mlp_kind;
+/* mojolearn ``norm``: RMSNorm with gain w, RMSNorm with gain 1 + w (Gemma), LayerNorm
+ * (DantinoX "Core Layers" page, Normalisation / LayerNorm: population variance,
+ * gain w, bias with norm_bias). */
+typedef enum { GQA_NORM_RMS = 0, GQA_NORM_RMS_OFFSET = 1, GQA_NORM_LAYER = 2 } gqa_norm_kind;
+/* mojolearn ``mlp``: gated down(act(gate(x)) * up(x)) with act = SiLU ('swiglu'),
+ * tanh-GELU ('geglu_tanh') or exact erf GELU ('geglu'); ungated down(act(up(x)))
+ * with exact ('gelu') or tanh ('gelu_tanh') GELU (no gate_proj). */
+typedef enum {
+  GQA_MLP_SWIGLU = 0, GQA_MLP_GEGLU_TANH = 1, GQA_MLP_GEGLU = 2, GQA_MLP_GELU = 3, GQA_MLP_GELU_TANH = 4
+} gqa_mlp_kind;
 /* RoPE frequency scaling (mojolearn ``rope_scaling``: None, "linear", "llama3"). */
 typedef enum { GQA_ROPE_PLAIN = 0, GQA_ROPE_LINEAR = 1, GQA_ROPE_LLAMA3 = 2 } gqa_rope_scaling;
 
@@ -71,9 +79,9 @@ typedef struct {
   float rope_theta;       /* RoPE base (``rope_theta``) */
   float norm_eps;         /* RMSNorm epsilon, inside the square root (``norm_eps``) */
   float attn_softcap;     /* 0: off; c > 0: scores become c*tanh(s/c) (``attn_softcap``) */
-  int32_t norm;           /* gqa_norm_kind: w or (1 + w) gain (``norm``) */
-  int32_t mlp;            /* gqa_mlp_kind: down(act(gate(x)) * up(x)), act = SiLU or
-                             tanh-GELU (``mlp`` = 'swiglu' / 'geglu_tanh') */
+  int32_t norm;           /* a gqa_norm_kind value: mojolearn ``norm``; every norm of the
+                             block but qk_norm */
+  int32_t mlp;            /* a gqa_mlp_kind value: mojolearn ``mlp`` */
   int32_t qkv_bias;       /* 1: q/k/v projection biases (``qkv_bias``) */
   int32_t qk_norm;        /* 1: per-head RMSNorm of q and k over head_dim before RoPE
                              (``qk_norm``); same eps and norm kind as the block */
@@ -97,6 +105,14 @@ typedef struct {
   float rope_low_freq_factor;     /* LLAMA3: > 0 and < rope_high_freq_factor */
   float rope_high_freq_factor;    /* LLAMA3 */
   int32_t rope_original_max_positions; /* LLAMA3: > 0 */
+  /* Bias and norm options (mojolearn ``o_bias``, ``mlp_bias``, ``norm_bias``) and
+   * Gemma 2/3's sandwich norms (the dew DecoderBlock page's output norms). */
+  int32_t o_bias;         /* 1: o_proj.bias (d) */
+  int32_t mlp_bias;       /* 1: up_proj.bias (IT), down_proj.bias (d) and, gated, gate_proj.bias (IT) */
+  int32_t norm_bias;      /* 1 (LayerNorm only): a bias (d) beside every norm weight */
+  int32_t sandwich_norms; /* 1: x1 = x + post_attention_layernorm(o_proj(attn)),
+                             y = x1 + post_feedforward_layernorm(mlp(pre_feedforward_layernorm(x1)));
+                             needs pre_/post_feedforward_layernorm.weight (d) */
 } gqa_block_config;
 
 /* One weight tensor, keyed by its Hugging Face parameter name, in torch's
@@ -104,10 +120,12 @@ typedef struct {
  * TransformerBlock class description.  Required: input_layernorm.weight (d),
  * post_attention_layernorm.weight (d), q_proj.weight (QW,d),
  * k_proj.weight (KW,d), v_proj.weight (KW,d), o_proj.weight (d,QW),
- * gate_proj.weight (IT,d), up_proj.weight (IT,d), down_proj.weight (d,IT).
- * With qkv_bias: q_proj.bias (QW), k_proj.bias (KW), v_proj.bias (KW).
- * With qk_norm: q_norm.weight (hd), k_norm.weight (hd).  Norm weights and
- * biases are float32; matrices are in weight_dtype.  Weights are BORROWED
+ * gate_proj.weight (IT,d; gated MLPs only), up_proj.weight (IT,d),
+ * down_proj.weight (d,IT).  With qkv_bias: q_proj.bias (QW), k_proj.bias (KW),
+ * v_proj.bias (KW).  With qk_norm: q_norm.weight (hd), k_norm.weight (hd).
+ * With o_bias / mlp_bias / sandwich_norms / norm_bias: the tensors named in
+ * the config fields above.  Norm weights and biases are float32; matrices are
+ * in weight_dtype.  Weights are BORROWED
  * device pointers: keep them alive and unchanged until gqa_block_destroy. */
 typedef struct {
   const char* name;

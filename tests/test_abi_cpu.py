@@ -90,6 +90,7 @@ def test_weight_table_errors(case, code):
                       "original_max_position_embeddings": 8192}, -1),
     ("rope_scaling", {"type": "llama3", "factor": 8.0, "low_freq_factor": 1.0, "high_freq_factor": 4.0,
                       "original_max_position_embeddings": 0}, -1),
+    ("norm_bias", True, -1),
 ])
 def test_config_errors(field, value, code):
     cfg, W = random_block(2)
@@ -112,6 +113,44 @@ def test_rope_scaling_kind_is_checked():
     assert "rope_scaling" in lib.gqa_last_error().decode()
 
 
+@pytest.mark.parametrize("case,code", [("gate_for_ungated", -2), ("missing_sandwich", -2),
+                                       ("missing_norm_bias", -2), ("norm_bias_unasked", -2)])
+def test_option_weight_tables(case, code):
+    if case == "gate_for_ungated":
+        cfg, W = random_block(5, mlp="gelu")
+        arr, n = _records(cfg, W, extra="gate_proj.weight")
+    elif case == "missing_sandwich":
+        cfg, W = random_block(5, sandwich_norms=True)
+        arr, n = _records(cfg, W, drop="post_feedforward_layernorm.weight")
+    elif case == "missing_norm_bias":
+        cfg, W = random_block(5, norm="layernorm", norm_bias=True)
+        arr, n = _records(cfg, W, drop="input_layernorm.bias")
+    else:
+        cfg, W = random_block(5, norm="layernorm")
+        arr, n = _records(cfg, W, extra="post_attention_layernorm.bias")
+    rc, msg = _create(cfg, arr, n)
+    assert rc == code, msg
+
+
+@pytest.mark.parametrize("field,value", [("o_bias", 2), ("sandwich_norms", -1), ("mlp", 5), ("norm", 3)])
+def test_option_fields_checked_by_the_library(field, value):
+    cfg, W = random_block(2)
+    c = make_config(cfg)
+    setattr(c, field, value)
+    lib = _lib()
+    arr, n = _records(cfg, W)
+    h = ctypes.c_void_p()
+    assert lib.gqa_block_create(ctypes.byref(c), arr, n, ctypes.byref(h)) == -1
+    assert lib.gqa_last_error().decode()
+
+
+def test_unknown_option_names():
+    for key, val in (("norm", "batchnorm"), ("mlp", "relu")):
+        cfg, _ = random_block(6, **{key: val})
+        with pytest.raises(ValueError):
+            make_config(cfg)
+
+
 def test_bf16_shape_rule():
     cfg, W = random_block(3, dtype="bf16", d_model=96, intermediate=128)
     arr, n = _records(cfg, W)
@@ -129,7 +168,11 @@ def test_valid_table_passes_validation():
     for over in ({}, dict(rope_dim=6, rope_scaling={"type": "linear", "factor": 4.0}),
                  dict(rope_dim=16, rope_scaling={"type": "llama3", "factor": 8.0, "low_freq_factor": 1.0,
                                                  "high_freq_factor": 4.0,
-                                                 "original_max_position_embeddings": 8192})):
+                                                 "original_max_position_embeddings": 8192}),
+                 dict(norm="layernorm", norm_bias=True, sandwich_norms=True, o_bias=True, mlp_bias=True,
+                      mlp="geglu"),
+                 dict(mlp="gelu_tanh", mlp_bias=True, sandwich_norms=True, norm="rmsnorm_offset"),
+                 dict(mlp="gelu")):
         cfg, W = random_block(4, qkv_bias=True, qk_norm=True, **over)
         arr, n = _records(cfg, W)
         rc, msg = _create(cfg, arr, n)

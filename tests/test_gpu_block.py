@@ -78,6 +78,23 @@ BF16_CASES = {
                                           rope_scaling={"type": "linear", "factor": 4.0}), 2, 90, 10, 3),
     "partial_rotary_rd20_hd64": (dict(d_model=256, n_heads=4, n_kv_heads=2, head_dim=64, intermediate=256,
                                       rope_dim=20, qk_norm=True), 1, 70, 6, 2),
+    # norm / MLP / bias options: Gemma 2 sandwich norms (128x128 tiles, then
+    # decode); LayerNorm with every bias and an ungated exact-GELU MLP on the
+    # pipelined large-M tiles; exact GeGLU with MLP biases under LayerNorm
+    # sandwich norms; ungated tanh-GELU; a 10240-wide row (register norm form)
+    "gemma2_sandwich": (dict(d_model=256, n_heads=4, n_kv_heads=2, head_dim=128, intermediate=384, window=64,
+                             attn_softcap=50.0, mlp="geglu_tanh", norm="rmsnorm_offset", sandwich_norms=True),
+                        2, 150, 20, 3),
+    "layernorm_biases_gelu": (dict(d_model=256, n_heads=4, n_kv_heads=2, head_dim=64, intermediate=512,
+                                   norm="layernorm", norm_bias=True, qkv_bias=True, o_bias=True, mlp_bias=True,
+                                   mlp="gelu"), 1, 600, 10, 3),
+    "geglu_sandwich_layernorm": (dict(d_model=512, n_heads=8, n_kv_heads=2, head_dim=64, intermediate=768,
+                                      mlp="geglu", mlp_bias=True, o_bias=True, sandwich_norms=True,
+                                      norm="layernorm", norm_bias=True), 1, 700, 0, 2),
+    "gelu_tanh_ungated": (dict(d_model=256, n_heads=4, n_kv_heads=1, head_dim=128, intermediate=256,
+                               mlp="gelu_tanh"), 2, 90, 0, 2),
+    "wide_row_10240": (dict(d_model=10240, n_heads=2, n_kv_heads=1, head_dim=128, intermediate=256,
+                            norm="layernorm"), 1, 40, 0, 1),
 }
 
 
@@ -139,6 +156,14 @@ DECODE_GEMM_BLOCKS = {
     # of rotated and pass-through columns alike
     "split_partial_rotary": dict(d_model=1024, n_heads=8, n_kv_heads=2, head_dim=128, intermediate=1280,
                                  qkv_bias=True, rope_dim=64, rope_theta=5e5, rope_scaling=LLAMA31_ROPE),
+    # sandwich norms with biases: the norm kernels sum the o_proj and down
+    # K-split partials (+ bias) before the output norm and the residual add
+    "split_sandwich_biases": dict(d_model=1024, n_heads=8, n_kv_heads=2, head_dim=128, intermediate=1280,
+                                  sandwich_norms=True, o_bias=True, mlp_bias=True, mlp="geglu",
+                                  norm="rmsnorm_offset"),
+    # ungated MLP: the up GEMM stores act(up + bias)
+    "ungated_biases": dict(d_model=1024, n_heads=8, n_kv_heads=2, head_dim=128, intermediate=1280,
+                           mlp="gelu_tanh", mlp_bias=True, o_bias=True, norm="layernorm", norm_bias=True),
 }
 
 
@@ -194,6 +219,13 @@ F32_CASES = {
                                             2, 19, 6, 5),
     "partial_rotary_odd_linear": (dict(d_model=50, n_heads=5, n_kv_heads=5, head_dim=10, intermediate=37,
                                        rope_dim=4, rope_scaling={"type": "linear", "factor": 2.5}), 1, 13, 3, 2),
+    "layernorm_sandwich_all_biases": (dict(norm="layernorm", norm_bias=True, sandwich_norms=True, o_bias=True,
+                                           mlp_bias=True, qkv_bias=True, mlp="geglu"), 2, 15, 5, 3),
+    "odd_dims_layernorm_gelu_sandwich": (dict(d_model=50, n_heads=5, n_kv_heads=5, head_dim=10, intermediate=37,
+                                              norm="layernorm", norm_bias=True, mlp="gelu",
+                                              sandwich_norms=True), 1, 13, 0, 2),
+    "odd_wide_row_9002": (dict(d_model=9002, n_heads=2, n_kv_heads=1, head_dim=8, intermediate=40,
+                               mlp="gelu_tanh", mlp_bias=True), 1, 6, 0, 1),
 }
 
 
