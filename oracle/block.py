@@ -74,6 +74,7 @@ import numpy as np
 __all__ = [
     "rms_norm", "layer_norm", "gelu_erf", "MLP_KINDS", "rope_inv_freq", "rope_cos_sin", "apply_rope", "silu", "gelu_tanh", "attention_row",
     "OracleState", "block_forward", "block_step", "block_forward_rows",
+    "BACKWARD_WEIGHTS", "backward_supported", "block_backward",
 ]
 
 
@@ -625,4 +626,140 @@ def block_forward_rows(cfg: dict, W: dict, x: np.ndarray, rows, state: OracleSta
         y = _mlp(cfg, w, x1, "batched")[0]
         for (i, _), yr in zip(items, y):
             out[i] = yr
+    return out
+
+
+# --------------------------------------------------------------------------
+# Backward of a zero-state prefill
+# --------------------------------------------------------------------------
+BACKWARD_WEIGHTS = ("input_layernorm.weight", "post_attention_layernorm.weight", "q_proj.weight",
+                    "k_proj.weight", "v_proj.weight", "o_proj.weight", "gate_proj.weight",
+                    "up_proj.weight", "down_proj.weight")
+
+
+def backward_supported(cfg: dict) -> bool:
+    """mojolearn ``TransformerBlock.backward``: the default block options only
+    (RMSNorm with gain w, SwiGLU, no biases, no q/k norm, no softcap, plain
+    RoPE over every dimension, no sandwich norms); the window is honoured."""
+    return (cfg.get("norm", "rmsnorm") == "rmsnorm" and cfg.get("mlp", "swiglu") == "swiglu"
+            and not cfg.get("qkv_bias") and not cfg.get("qk_norm") and not cfg.get("attn_softcap")
+            and not cfg.get("o_bias") and not cfg.get("mlp_bias") and not cfg.get("norm_bias")
+            and not cfg.get("sandwich_norms") and not cfg.get("rope_scaling")
+            and (cfg.get("rope_dim") or cfg["head_dim"]) == cfg["head_dim"])
+
+
+def _rms_backward(dy, xhat, r, w):
+    """RMSNorm y = x r w, r = (mean(x^2) + eps)^(-1/2), x^ = x r: with g = dy w,
+    dx = r (g - x^ mean(g x^)) (r depends on every x_j through the mean), and
+    dw = sum over tokens of dy x^."""
+    g = dy * w
+    dx = r * (g - xhat * np.mean(g * xhat, axis=-1, keepdims=True))
+    dw = np.sum((dy * xhat).reshape(-1, dy.shape[-1]), axis=0)
+    return dx, dw
+
+
+def block_backward(cfg: dict, W: dict, x: np.ndarray, dy: np.ndarray, *, dtype=np.float64) -> dict:
+    """Gradients of a zero-state prefill: mojolearn ``TransformerBlock.backward(x,
+    grad_output)``: the forward is recomputed from an empty cache at positions
+    [0, L) (window honoured) and grad_output = dL/dy is propagated back to x and
+    the nine weights, each weight gradient summed over the B * L tokens.
+    Returns {"x": [B, L, d], name: gradient in the tensor's shape}.
+
+    The chain rule through the block of ``block_forward`` (DantinoX "Core
+    Layers" page formulas), step by step in reverse: y = x1 + down(silu(g) u);
+    g, u = gate(h2), up(h2); h2 = RMSNorm(x1); x1 = x + o_proj(ctx); ctx =
+    softmax(q k^T / sqrt(hd) + mask) v per head (kv head h // G); q, k = RoPE
+    of the projections of h = RMSNorm(x).  The softmax backward is dS = P (dP -
+    rowsum(P dP)); RoPE's backward is the rotation by the opposite angle.
+    """
+    if not backward_supported(cfg):
+        raise ValueError("backward supports the default block options only")
+    dt = np.dtype(dtype)
+    x = np.asarray(x).astype(dt)
+    dy = np.asarray(dy).astype(dt)
+    B, L, d = x.shape
+    H, KV, hd = cfg["n_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    G = H // KV
+    window = int(cfg.get("window", 0))
+    if L > cfg["max_positions"]:
+        raise ValueError("position at or beyond max_positions")
+    eps = dt.type(cfg["norm_eps"])
+    w = {k: v.astype(dt) for k, v in W.items()}
+    scale = dt.type(1.0 / np.sqrt(hd))
+
+    # ---- forward, keeping what the backward reads ----
+    r1 = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    xh1 = x * r1
+    h = xh1 * w["input_layernorm.weight"]
+    q = (h @ w["q_proj.weight"].T).reshape(B, L, H, hd)
+    k = (h @ w["k_proj.weight"].T).reshape(B, L, KV, hd)
+    v = (h @ w["v_proj.weight"].T).reshape(B, L, KV, hd)
+    cos, sin = _rope(cfg, np.arange(L))                          # [L, hd/2]
+    c4, s4 = cos[None, :, None, :], sin[None, :, None, :]
+    qr, kr = apply_rope(q, c4, s4), apply_rope(k, c4, s4)
+    pos = np.arange(L)
+    allowed = pos[None, :] <= pos[:, None]
+    if window > 0:
+        allowed &= pos[None, :] >= pos[:, None] - (window - 1)
+    P = np.empty((B, H, L, L), dtype=dt)
+    ctx = np.empty((B, L, H, hd), dtype=dt)
+    for b in range(B):
+        for hh in range(H):
+            j = hh // G
+            s = (qr[b, :, hh, :] @ kr[b, :, j, :].T) * scale
+            s = np.where(allowed, s, -np.inf)
+            e = np.exp(s - np.max(s, axis=-1, keepdims=True))
+            P[b, hh] = e / np.sum(e, axis=-1, keepdims=True)
+            ctx[b, :, hh, :] = P[b, hh] @ v[b, :, j, :]
+    ctx2 = ctx.reshape(B, L, H * hd)
+    x1 = x + ctx2 @ w["o_proj.weight"].T
+    r2 = 1.0 / np.sqrt(np.mean(x1 * x1, axis=-1, keepdims=True) + eps)
+    xh2 = x1 * r2
+    h2 = xh2 * w["post_attention_layernorm.weight"]
+    g = h2 @ w["gate_proj.weight"].T
+    u = h2 @ w["up_proj.weight"].T
+    sg = 1.0 / (1.0 + np.exp(-g))
+    a = g * sg * u
+
+    T = B * L
+    flat = lambda t: t.reshape(T, t.shape[-1])
+    out = {}
+    # ---- y = x1 + a Wd^T ----
+    out["down_proj.weight"] = flat(dy).T @ flat(a)
+    da = dy @ w["down_proj.weight"]
+    # ---- a = silu(g) u: d silu(g)/dg = sg (1 + g (1 - sg)) ----
+    dg = da * u * sg * (1.0 + g * (1.0 - sg))
+    du = da * g * sg
+    out["gate_proj.weight"] = flat(dg).T @ flat(h2)
+    out["up_proj.weight"] = flat(du).T @ flat(h2)
+    dh2 = dg @ w["gate_proj.weight"] + du @ w["up_proj.weight"]
+    dx1, out["post_attention_layernorm.weight"] = _rms_backward(dh2, xh2, r2, w["post_attention_layernorm.weight"])
+    dx1 = dx1 + dy
+    # ---- x1 = x + ctx Wo^T ----
+    out["o_proj.weight"] = flat(dx1).T @ flat(ctx2)
+    dctx = (dx1 @ w["o_proj.weight"]).reshape(B, L, H, hd)
+    # ---- attention, per row and head ----
+    dqr = np.zeros_like(qr)
+    dkr = np.zeros_like(kr)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for hh in range(H):
+            j = hh // G
+            p = P[b, hh]
+            dO = dctx[b, :, hh, :]
+            dv[b, :, j, :] += p.T @ dO
+            dp = dO @ v[b, :, j, :].T
+            ds = p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
+            dqr[b, :, hh, :] = (ds @ kr[b, :, j, :]) * scale
+            dkr[b, :, j, :] += (ds.T @ qr[b, :, hh, :]) * scale
+    # ---- RoPE: rotation back by the opposite angle ----
+    dq = apply_rope(dqr, c4, -s4).reshape(B, L, H * hd)
+    dk = apply_rope(dkr, c4, -s4).reshape(B, L, KV * hd)
+    dv = dv.reshape(B, L, KV * hd)
+    out["q_proj.weight"] = flat(dq).T @ flat(h)
+    out["k_proj.weight"] = flat(dk).T @ flat(h)
+    out["v_proj.weight"] = flat(dv).T @ flat(h)
+    dh = dq @ w["q_proj.weight"] + dk @ w["k_proj.weight"] + dv @ w["v_proj.weight"]
+    dxn, out["input_layernorm.weight"] = _rms_backward(dh, xh1, r1, w["input_layernorm.weight"])
+    out["x"] = dx1 + dxn
     return out
