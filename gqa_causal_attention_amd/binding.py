@@ -22,7 +22,8 @@ STATUS = {0: "OK", -1: "ARG", -2: "SHAPE", -3: "DTYPE", -4: "NONFINITE", -5: "CA
 # Exported entry points declared in include/gqa_block.h.
 EXPORTS = ("gqa_block_create", "gqa_block_destroy", "gqa_state_bytes", "gqa_block_allocate_state",
            "gqa_state_set_lengths", "gqa_state_get_lengths", "gqa_state_free", "gqa_workspace_bytes",
-           "gqa_block_forward", "gqa_block_forward_ragged", "gqa_block_step", "gqa_block_status",
+           "gqa_block_forward", "gqa_block_forward_ragged", "gqa_backward_workspace_bytes", "gqa_block_backward",
+           "gqa_block_step", "gqa_block_status",
            "gqa_block_set_timing",
            "gqa_block_kernel_times", "gqa_last_error", "gqa_version")
 
@@ -79,6 +80,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gqa_workspace_bytes": ([P, I32, I32, ctypes.POINTER(SZ)], I32),
         "gqa_block_forward": ([P, P, P, P, I32, I32, P, SZ, P], I32),
         "gqa_block_forward_ragged": ([P, P, P, I32, I32, ctypes.POINTER(I32), P, SZ, P], I32),
+        "gqa_backward_workspace_bytes": ([P, I32, I32, ctypes.POINTER(SZ)], I32),
+        "gqa_block_backward": ([P, P, P, P, ctypes.POINTER(P), I32, I32, P, SZ, P], I32),
         "gqa_block_step": ([P, P, P, P, I32, P, SZ, P], I32),
         "gqa_block_status": ([P, P], I32),
         "gqa_block_set_timing": ([P, I32], I32),
@@ -232,6 +235,32 @@ class Block:
                                           B, L, ctypes.c_void_p(ws.data_ptr()), ws.numel(),
                                           _stream_ptr(stream)))
         return y
+
+    BACKWARD_WEIGHTS = ("input_layernorm.weight", "post_attention_layernorm.weight", "q_proj.weight",
+                        "k_proj.weight", "v_proj.weight", "o_proj.weight", "gate_proj.weight", "up_proj.weight",
+                        "down_proj.weight")
+
+    def backward(self, x, grad_output, stream=None, grads=None):
+        """mojolearn TransformerBlock.backward: gradients of a zero-state
+        prefill -> {"x": [B, L, d], weight name: gradient in its shape}, all
+        float32 torch tensors on the device (``grads`` may supply them)."""
+        import torch
+        assert x.dtype == torch.float32 and x.is_contiguous() and x.dim() == 3
+        assert grad_output.shape == x.shape and grad_output.dtype == torch.float32 and grad_output.is_contiguous()
+        B, L, _ = x.shape
+        nb = ctypes.c_size_t()
+        _check(self.lib.gqa_backward_workspace_bytes(self.handle, B, L, ctypes.byref(nb)))
+        ws = torch.empty(max(nb.value, 1), dtype=torch.uint8, device=self.device)
+        if grads is None:
+            grads = {"x": torch.empty_like(x)}
+            for name in self.BACKWARD_WEIGHTS:
+                grads[name] = torch.empty(tuple(self.tensors[name].shape), dtype=torch.float32, device=self.device)
+        table = (ctypes.c_void_p * 9)(*[grads[n].data_ptr() for n in self.BACKWARD_WEIGHTS])
+        _check(self.lib.gqa_block_backward(self.handle, ctypes.c_void_p(x.data_ptr()),
+                                           ctypes.c_void_p(grad_output.data_ptr()),
+                                           ctypes.c_void_p(grads["x"].data_ptr()), table, B, L,
+                                           ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream_ptr(stream)))
+        return grads
 
     def step(self, x, state: "State", out=None, stream=None):
         import torch

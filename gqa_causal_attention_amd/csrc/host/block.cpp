@@ -727,6 +727,280 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
   return GQA_OK;
 }
 
+// ---- backward of a zero-state prefill ----
+
+// mojolearn TransformerBlock.backward: the default block options only (the
+// window is honoured).
+bool backward_supported(const gqa_block_config& c) {
+  return c.norm == GQA_NORM_RMS && c.mlp == GQA_MLP_SWIGLU && !c.qkv_bias && !c.qk_norm && c.attn_softcap == 0.f &&
+         !c.o_bias && !c.mlp_bias && !c.norm_bias && !c.sandwich_norms && c.rope_scaling == GQA_ROPE_PLAIN &&
+         c.rope_dim == c.head_dim;
+}
+
+struct BwdLayout {
+  WsLayout fwd;  // the recomputed forward's workspace, at offset 0
+  size_t y, gu, lse, dsum, wdT, wguT, woT, wqkvT, dy_op, dyT, da, act, actT, dgu, dguT, h2T, dh2, dx1, dx1_op, dx1T,
+      wpart, cpart, ctxT, dctx, dq, dk, dv, dqkv, dqkvT, hT, dh, part, total;
+  int Tp;  // token count padded to 256: the depth of the weight-gradient GEMMs
+  int Kq;  // q | k | v width padded to 64: the depth of the dh GEMM
+};
+
+BwdLayout bwd_layout_for(const gqa_block* blk, int B, int L) {
+  const auto& c = blk->cfg;
+  BwdLayout w{};
+  w.fwd = layout_for(blk, B, L);
+  size_t off = w.fwd.total;
+  auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+  const size_t T = (size_t)B * L, es = blk->es;
+  const size_t d = c.d_model, QW = blk->QW, KW = blk->KW, IT = c.intermediate, H = c.n_heads;
+  w.Tp = (int)((T + 255) / 256 * 256);
+  w.Kq = (int)((QW + 2 * KW + 63) / 64 * 64);
+  const size_t Tp = w.Tp, Kq = w.Kq;
+  w.y = take(T * d * 4);
+  w.gu = take(T * 2 * IT * 4);
+  w.lse = take(T * H * 4);
+  w.dsum = take(T * H * 4);
+  w.wdT = take(IT * d * es);
+  w.wguT = take(d * 2 * IT * es);
+  w.woT = take(QW * d * es);
+  w.wqkvT = take(d * Kq * es);
+  w.dy_op = take(T * d * es);
+  w.dyT = take(d * Tp * es);
+  w.da = take(T * IT * 4);
+  w.act = take(T * IT * es);
+  w.actT = take(IT * Tp * es);
+  w.dgu = take(T * 2 * IT * es);
+  w.dguT = take(2 * IT * Tp * es);
+  w.h2T = take(d * Tp * es);
+  w.dh2 = take(T * d * 4);
+  w.dx1 = take(T * d * 4);
+  w.dx1_op = take(T * d * es);
+  w.dx1T = take(d * Tp * es);
+  w.wpart = take(T * d * 4);
+  w.cpart = take((size_t)colsum_chunks((int)T) * d * 4);
+  w.ctxT = take(QW * Tp * es);
+  w.dctx = take(T * QW * 4);
+  w.dq = take(T * QW * 4);
+  w.dk = take(T * KW * 4);
+  w.dv = take(T * KW * 4);
+  w.dqkv = take(T * Kq * es);
+  w.dqkvT = take(Kq * Tp * es);
+  w.hT = take(d * Tp * es);
+  w.dh = take(T * d * 4);
+  size_t part = 0;  // K-split partials of any product whose plan splits
+  if (is_bf16(blk)) {
+    auto need = [&](size_t M, size_t N, size_t K) {
+      const GemmPlan p = plan_gemm((int)M, (int)N, (int)K, false);
+      if (p.splits > 1) part = std::max(part, (size_t)p.splits * M * N * 4);
+    };
+    need(T, IT, d);       // da
+    need(d, IT, Tp);      // dWd
+    need(T, d, 2 * IT);   // dh2
+    need(IT, d, Tp);      // dWg, dWu
+    need(T, QW, d);       // dctx
+    need(d, QW, Tp);      // dWo
+    need(T, d, Kq);       // dh
+    need(QW, d, Tp);      // dWq
+    need(KW, d, Tp);      // dWk, dWv
+    need(T, IT, d);       // gate / up of the recompute
+  }
+  w.part = part ? take(part) : 0;
+  w.total = off;
+  return w;
+}
+
+int run_backward(gqa_block* blk, const float* x, const float* dy, float* dx, float* const* dw, int B, int L, void* ws,
+                 size_t wsb, hipStream_t s) {
+  if (!blk) return fail(GQA_ERR_ARG, "block is NULL");
+  const auto& c = blk->cfg;
+  if (!backward_supported(c))
+    return fail(GQA_ERR_UNSUPPORTED, "backward supports the default block options only (RMSNorm, SwiGLU, no "
+                                     "biases, q/k norm, softcap, RoPE scaling, partial rotary or sandwich norms)");
+  if (B < 0 || L < 0) return fail(GQA_ERR_ARG, "B and L must be >= 0");
+  if (L > c.max_positions)
+    return fail(GQA_ERR_POSITION, "position %d is at or beyond max_positions %d", L - 1, c.max_positions);
+  if (B == 0 || L == 0) return GQA_OK;
+  if (!x || !dy || !dx || !dw) return fail(GQA_ERR_ARG, "x, grad_output, grad_x or the gradient table is NULL");
+  for (int i = 0; i < 9; ++i)
+    if (!dw[i]) return fail(GQA_ERR_ARG, "gradient %d (%s) is NULL", i, kNames[i]);
+  const BwdLayout lay = bwd_layout_for(blk, B, L);
+  if (!ws || wsb < lay.total)
+    return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? wsb : (size_t)0, lay.total);
+
+  char* base = static_cast<char*>(ws);
+  float* y = reinterpret_cast<float*>(base + lay.y);
+  // 0. forward from an empty cache (positions 0 .. L-1), leaving its activations
+  if (int r = run_block(blk, nullptr, x, y, B, L, ws, lay.fwd.total, s)) return r;
+  BusyGuard guard(blk->busy);
+  if (!guard.ok) return fail(GQA_ERR_BUSY, "block is in use by another call");
+
+  const int T = B * L, d = c.d_model, QW = blk->QW, KW = blk->KW, IT = c.intermediate, H = c.n_heads;
+  const int Tp = lay.Tp, Kq = lay.Kq;
+  const bool bf = is_bf16(blk);
+  const int et = bf ? kBF16 : kF32;
+  const size_t es = blk->es;
+  KernelTimer* tm = &blk->timer;
+  auto at = [&](size_t off) { return static_cast<void*>(base + off); };
+  auto atf = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
+  const void* h = at(lay.fwd.h);
+  const void* qkv = at(lay.fwd.qkv);
+  const void* ctx = at(lay.fwd.ctx);
+  const float* x1 = atf(lay.fwd.x1);
+  const void* h2 = at(lay.fwd.h2);
+  float* part = lay.part ? atf(lay.part) : nullptr;
+  auto sub = [&](const void* p, size_t elems) { return static_cast<const void*>(static_cast<const char*>(p) + elems * es); };
+
+  // C[M, N] (float32, row stride ldc) = A[M, K] B[N, K]^T: the forward's GEMMs,
+  // K-split when their plan says so (partials summed in split order)
+  auto gemm = [&](const char* name, const void* A, int64_t lda, const void* Bm, int M, int N, int K, float* C,
+                  int64_t ldc) -> int {
+    GemmArgs a{};
+    a.A = A; a.lda = lda;
+    a.B[0] = a.B[1] = a.B[2] = Bm;
+    a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = N;
+    a.M = M; a.N = N; a.K = K;
+    a.C = C; a.ldc = ldc;
+    a.order = gemm_tile_order();
+    Scope sc(tm, name, s);
+    if (!bf) {
+      HIP_TRY(launch_gemm_f32(a, kModeSeg, kEpiResid, s));
+      return GQA_OK;
+    }
+    const GemmPlan p = plan_gemm(M, N, K, false);
+    a.wg_waves = p.waves;
+    if (p.splits <= 1) {
+      a.splits = 1;
+      a.k_split = K;
+      HIP_TRY(launch_gemm_bf16(a, kModeSeg, kEpiResid, p.tile, s));
+      return GQA_OK;
+    }
+    GemmArgs pa = a;
+    pa.splits = p.splits;
+    pa.k_split = K / p.splits;
+    pa.partial = part;
+    HIP_TRY(launch_gemm_bf16(pa, kModeSeg, kEpiPartial, p.tile, s));
+    a.splits = p.splits;
+    a.partial = part;
+    HIP_TRY(launch_splitk_reduce(a, kModeSeg, kEpiResid, kF32, s));
+    return GQA_OK;
+  };
+  auto tr = [&](const char* name, const void* in, int in_t, int64_t ld, int R, int C, void* out, int64_t ldo,
+                int Rp) -> int {
+    Scope sc(tm, name, s);
+    HIP_TRY(launch_transpose(in, in_t, ld, R, C, out, et, ldo, Rp, s));
+    return GQA_OK;
+  };
+#define BWD(expr) \
+  do {            \
+    if (int r_ = (expr)) return r_; \
+  } while (0)
+
+  // 1. gate and up pre-activations of the recomputed forward (float32, gate | up per row)
+  float* gu = atf(lay.gu);
+  BWD(gemm("bwd_gate", h2, d, blk->w[W_GATE], T, IT, d, gu, 2 * IT));
+  BWD(gemm("bwd_up", h2, d, blk->w[W_UP], T, IT, d, gu + IT, 2 * IT));
+  // 2. weights as the other product operand (transposed, K-contiguous)
+  void* wdT = at(lay.wdT);
+  void* wguT = at(lay.wguT);
+  void* woT = at(lay.woT);
+  void* wqkvT = at(lay.wqkvT);
+  BWD(tr("bwd_transpose_w", blk->w[W_DOWN], et, IT, d, IT, wdT, d, d));
+  BWD(tr("bwd_transpose_w", blk->w[W_GATE], et, d, IT, d, wguT, 2 * IT, IT));
+  BWD(tr("bwd_transpose_w", blk->w[W_UP], et, d, IT, d, static_cast<char*>(wguT) + (size_t)IT * es, 2 * IT, IT));
+  BWD(tr("bwd_transpose_w", blk->w[W_O], et, QW, d, QW, woT, d, d));
+  BWD(tr("bwd_transpose_w", blk->w[W_Q], et, d, QW, d, wqkvT, Kq, QW));
+  BWD(tr("bwd_transpose_w", blk->w[W_K], et, d, KW, d, static_cast<char*>(wqkvT) + (size_t)QW * es, Kq, KW));
+  BWD(tr("bwd_transpose_w", blk->w[W_V], et, d, KW, d, static_cast<char*>(wqkvT) + (size_t)(QW + KW) * es, Kq,
+         Kq - QW - KW));
+  // 3. down: da = dy Wd, dWd = dy^T a
+  const void* dy_op = dy;
+  if (bf) {
+    Scope sc(tm, "bwd_convert", s);
+    HIP_TRY(launch_convert(dy, at(lay.dy_op), et, (int64_t)T * d, s));
+    dy_op = at(lay.dy_op);
+  }
+  void* dyT = at(lay.dyT);
+  BWD(tr("bwd_transpose", dy, kF32, d, T, d, dyT, Tp, Tp));
+  float* da = atf(lay.da);
+  BWD(gemm("bwd_gemm_da", dy_op, d, wdT, T, IT, d, da, IT));
+  // 4. SwiGLU: a = silu(g) u (for dWd), dg | du
+  void* act = at(lay.act);
+  void* dgu = at(lay.dgu);
+  {
+    Scope sc(tm, "bwd_swiglu", s);
+    HIP_TRY(launch_swiglu_bwd(gu, da, T, IT, act, dgu, et, s));
+  }
+  void* actT = at(lay.actT);
+  BWD(tr("bwd_transpose", act, et, IT, T, IT, actT, Tp, Tp));
+  BWD(gemm("bwd_gemm_dw", dyT, Tp, actT, d, IT, Tp, dw[8], IT));
+  // 5. gate / up: dh2 = dg Wg + du Wu, dWg = dg^T h2, dWu = du^T h2
+  float* dh2 = atf(lay.dh2);
+  BWD(gemm("bwd_gemm_dh2", dgu, 2 * IT, wguT, T, d, 2 * IT, dh2, d));
+  void* dguT = at(lay.dguT);
+  void* h2T = at(lay.h2T);
+  BWD(tr("bwd_transpose", dgu, et, 2 * IT, T, 2 * IT, dguT, Tp, Tp));
+  BWD(tr("bwd_transpose", h2, et, d, T, d, h2T, Tp, Tp));
+  BWD(gemm("bwd_gemm_dw", dguT, Tp, h2T, IT, d, Tp, dw[6], d));
+  BWD(gemm("bwd_gemm_dw", sub(dguT, (size_t)IT * Tp), Tp, h2T, IT, d, Tp, dw[7], d));
+  // 6. post-attention RMSNorm backward + the residual: dx1 = dy + norm'(dh2)
+  float* dx1 = atf(lay.dx1);
+  void* dx1_op = bf ? at(lay.dx1_op) : static_cast<void*>(dx1);
+  float* wpart = atf(lay.wpart);
+  {
+    Scope sc(tm, "bwd_norm", s);
+    HIP_TRY(launch_rms_bwd(dh2, x1, static_cast<const float*>(blk->w[W_POST_NORM]), dy, T, d, c.norm_eps, dx1,
+                           bf ? dx1_op : nullptr, et, wpart, s));
+    HIP_TRY(launch_colsum(wpart, T, d, atf(lay.cpart), dw[1], s));
+  }
+  // 7. o_proj: dctx = dx1 Wo, dWo = dx1^T ctx
+  float* dctx = atf(lay.dctx);
+  BWD(gemm("bwd_gemm_dctx", dx1_op, d, woT, T, QW, d, dctx, QW));
+  void* dx1T = at(lay.dx1T);
+  void* ctxT = at(lay.ctxT);
+  BWD(tr("bwd_transpose", dx1, kF32, d, T, d, dx1T, Tp, Tp));
+  BWD(tr("bwd_transpose", ctx, et, QW, T, QW, ctxT, Tp, Tp));
+  BWD(gemm("bwd_gemm_dw", dx1T, Tp, ctxT, d, QW, Tp, dw[5], QW));
+  // 8. attention, then RoPE's backward, packed as the q/k/v GEMM's rows
+  BwdAttnArgs ba{};
+  ba.q = qkv; ba.ldq = QW + 2 * KW;
+  ba.k = at(lay.fwd.knew); ba.v = at(lay.fwd.vnew);
+  ba.o = ctx; ba.ldo = QW;
+  ba.dout = dctx;
+  ba.lse = atf(lay.lse); ba.dsum = atf(lay.dsum);
+  ba.dq = atf(lay.dq); ba.dk = atf(lay.dk); ba.dv = atf(lay.dv);
+  ba.cos_tab = blk->cos_tab; ba.sin_tab = blk->sin_tab;
+  ba.B = B; ba.L = L; ba.H = H; ba.KV = c.n_kv_heads; ba.hd = c.head_dim; ba.window = c.window;
+  ba.scale = 1.0f / std::sqrt((float)c.head_dim);
+  {
+    Scope sc(tm, "bwd_attention", s);
+    HIP_TRY(launch_attention_bwd(ba, et, s));
+  }
+  void* dqkv = at(lay.dqkv);
+  {
+    Scope sc(tm, "bwd_rope", s);
+    HIP_TRY(launch_rope_bwd_pack(ba, dqkv, Kq, et, s));
+  }
+  // 9. q/k/v: dh = [dq|dk|dv] [Wq;Wk;Wv], dW = d^T h
+  float* dh = atf(lay.dh);
+  BWD(gemm("bwd_gemm_dh", dqkv, Kq, wqkvT, T, d, Kq, dh, d));
+  void* dqkvT = at(lay.dqkvT);
+  void* hT = at(lay.hT);
+  BWD(tr("bwd_transpose", dqkv, et, Kq, T, Kq, dqkvT, Tp, Tp));
+  BWD(tr("bwd_transpose", h, et, d, T, d, hT, Tp, Tp));
+  BWD(gemm("bwd_gemm_dw", dqkvT, Tp, hT, QW, d, Tp, dw[2], d));
+  BWD(gemm("bwd_gemm_dw", sub(dqkvT, (size_t)QW * Tp), Tp, hT, KW, d, Tp, dw[3], d));
+  BWD(gemm("bwd_gemm_dw", sub(dqkvT, (size_t)(QW + KW) * Tp), Tp, hT, KW, d, Tp, dw[4], d));
+  // 10. input RMSNorm backward + the residual: dx = dx1 + norm'(dh)
+  {
+    Scope sc(tm, "bwd_norm", s);
+    HIP_TRY(launch_rms_bwd(dh, x, static_cast<const float*>(blk->w[W_IN_NORM]), dx1, T, d, c.norm_eps, dx, nullptr,
+                           et, wpart, s));
+    HIP_TRY(launch_colsum(wpart, T, d, atf(lay.cpart), dw[0], s));
+  }
+#undef BWD
+  return GQA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -901,6 +1175,18 @@ int gqa_block_forward_ragged(gqa_block* blk, const float* x, float* y, int32_t B
   if (B == 0 || L == 0) return GQA_OK;
   HIP_TRY(launch_zero_padding(y, lengths, B, L, blk->cfg.d_model, static_cast<hipStream_t>(stream)));
   return GQA_OK;
+}
+
+int gqa_backward_workspace_bytes(const gqa_block* blk, int32_t B, int32_t L, size_t* out) {
+  if (!blk || !out) return fail(GQA_ERR_ARG, "block or output is NULL");
+  if (B < 0 || L < 0) return fail(GQA_ERR_ARG, "B and L must be >= 0");
+  *out = (B == 0 || L == 0) ? 0 : bwd_layout_for(blk, B, L).total;
+  return GQA_OK;
+}
+
+int gqa_block_backward(gqa_block* blk, const float* x, const float* grad_out, float* grad_x, float* const* grad_w,
+                       int32_t B, int32_t L, void* ws, size_t wsb, void* stream) {
+  return run_backward(blk, x, grad_out, grad_x, grad_w, B, L, ws, wsb, static_cast<hipStream_t>(stream));
 }
 
 int gqa_block_step(gqa_block* blk, gqa_state* st, const float* x, float* y, int32_t B, void* ws, size_t wsb,

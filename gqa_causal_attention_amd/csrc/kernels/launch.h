@@ -150,6 +150,44 @@ int attention_decode_max_rows();
 int attention_decode_max_segments();
 int attention_decode_segments(int64_t total_keys, int keys_per_seg);
 
+// Backward of a zero-state prefill (backward.hip).
+struct BwdAttnArgs {
+  const void* q;           // post-RoPE queries [T, ldq] (head h at column h*hd)
+  int64_t ldq;
+  const void* k;           // post-RoPE keys [B, KV, L, hd]
+  const void* v;           // values [B, KV, L, hd]
+  const void* o;           // attention output [T, ldo]
+  int64_t ldo;
+  const float* dout;       // gradient of the attention output [T, ldo], float32
+  float* lse;              // [T, H] row log-sum-exp of the scaled scores, base 2 (written)
+  float* dsum;             // [T, H] rowsum(dO * O) (written)
+  float* dq;               // [T, H, hd] gradient of the post-RoPE queries
+  float* dk;               // [B, KV, L, hd] gradient of the post-RoPE keys
+  float* dv;               // [B, KV, L, hd]
+  const float* cos_tab;    // [max_positions, hd/2] (RoPE backward)
+  const float* sin_tab;
+  int B, L, H, KV, hd, window;
+  float scale;             // 1 / sqrt(hd)
+};
+// [R, C] (row stride ld) -> out[c * ldo + r] for r < Rp (zero for r >= R).
+hipError_t launch_transpose(const void* in, int in_type, int64_t ld, int R, int C, void* out, int out_type,
+                            int64_t ldo, int Rp, hipStream_t s);
+hipError_t launch_convert(const float* in, void* out, int elem, int64_t n, hipStream_t s);
+// gu [rows, 2 IT] float32 (gate | up), da [rows, IT] -> act = silu(g) u and dgu = dg | du.
+hipError_t launch_swiglu_bwd(const float* gu, const float* da, int64_t rows, int IT, void* act, void* dgu, int elem,
+                             hipStream_t s);
+// dx = resid + RMSNorm backward of dy at input x (gain w); dx_op: the same in elem (or null);
+// wpart = dy * x^ (the weight gradient's summands).
+hipError_t launch_rms_bwd(const float* dy, const float* x, const float* w, const float* resid, int rows, int d,
+                          float eps, float* dx, void* dx_op, int elem, float* wpart, hipStream_t s);
+int colsum_chunks(int R);  // rows of the `part` scratch of launch_colsum (times C floats)
+hipError_t launch_colsum(const float* a, int R, int C, float* part, float* out, hipStream_t s);
+// dq | dk | dv, RoPE undone on dq and dk, into the q/k/v GEMM's row layout [T, ld]
+// (ld >= (H + 2 KV) hd; the columns past that width are zero).
+hipError_t launch_rope_bwd_pack(const BwdAttnArgs& a, void* dqkv, int64_t ld, int elem, hipStream_t s);
+// lse, dsum, dq, dk, dv of the attention (causal, optional window).
+hipError_t launch_attention_bwd(const BwdAttnArgs& a, int elem, hipStream_t s);
+
 hipError_t launch_count_nonfinite(const void* p, int elem, int64_t n, int* flag, hipStream_t s);
 hipError_t launch_bump_lengths(int* lengths, int n, int by, hipStream_t s);
 // y [B, L, d] float32: positions t >= lengths_host[b] of row b set to +0.0.

@@ -199,6 +199,26 @@ int gqa_block_forward_ragged(gqa_block* blk, const float* x_dev, float* y_dev, i
                              const int32_t* lengths_host, void* workspace_dev, size_t workspace_bytes,
                              void* hip_stream);
 
+/* Workspace bytes gqa_block_backward needs for B rows x L tokens. */
+int gqa_backward_workspace_bytes(const gqa_block* blk, int32_t B, int32_t L, size_t* out);
+
+/* mojolearn TransformerBlock.backward(x, grad_output): gradients of a
+ * zero-state prefill.  The forward is recomputed from an empty cache at
+ * positions [0, L) (window honoured) and grad_out_dev (float32 [B, L, d],
+ * dL/dy) is propagated back: grad_x_dev (float32 [B, L, d]) receives dL/dx and
+ * grad_w_dev (a HOST array of 9 device pointers, float32, each in its tensor's
+ * shape, in the weight table's order: input_layernorm, post_attention_layernorm,
+ * q_proj, k_proj, v_proj, o_proj, gate_proj, up_proj, down_proj) the weight
+ * gradients, each summed over the B * L tokens (overwritten, not accumulated).
+ * The default block options only (RMSNorm with gain w, SwiGLU, no biases, q/k
+ * norm, softcap, RoPE scaling, partial rotary or sandwich norms); any window.
+ * bf16 blocks run the products in bf16 with float32 accumulation.  Errors:
+ * UNSUPPORTED (another option), ARG, POSITION (L > max_positions), WORKSPACE,
+ * BUSY, HIP. */
+int gqa_block_backward(gqa_block* blk, const float* x_dev, const float* grad_out_dev, float* grad_x_dev,
+                       float* const* grad_w_dev, int32_t B, int32_t L, void* workspace_dev, size_t workspace_bytes,
+                       void* hip_stream);
+
 /* mojolearn TransformerBlock.step: forward with L = 1 on a required state; x
  * is [B, d] or [B, 1, d] (the same memory).  Errors: as forward, STATE if st
  * is NULL. */
