@@ -250,6 +250,47 @@ def bench_prefill(args, torch):
                 breakdown=breakdown, wl=wl)
 
 
+def bench_backward(args, torch, wl):
+    """Gradients of a zero-state prefill on the prefill workload (x, and a seeded
+    N(0, 1) grad_output): the forward recompute plus the backward, timed over
+    eager launches (synchronised), with per-kernel HIP events in a second pass."""
+    from gqa_causal_attention_amd import Block
+    cfg, B, L = wl["cfg"], wl["batch"], wl["seq_len"]
+    blk = Block(cfg, wl["weights"])
+    x = torch.from_numpy(wl["x"]).cuda()
+    dy = torch.from_numpy(np.random.default_rng(7).standard_normal(wl["x"].shape, dtype=np.float32)).cuda()
+    grads = blk.backward(x, dy)
+    for _ in range(args.warmup):
+        blk.backward(x, dy, grads=grads)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        blk.backward(x, dy, grads=grads)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t1) * 1e3 / args.steps
+    blk.set_timing(True)
+    for _ in range(3):
+        blk.backward(x, dy, grads=grads)
+    torch.cuda.synchronize()
+    times = blk.kernel_times()
+    blk.set_timing(False)
+    gemm_f, attn_f = prefill_flops(cfg, B, L)
+    # recompute (gemm_f + attn_f), the dX and dW products (2 gemm_f), the
+    # attention backward (S again, dP, dV, dQ, dK: 2.5 attn_f)
+    flops = 3 * gemm_f + 3.5 * attn_f
+    per = {k: round(v[0] / max(v[1], 1), 4) for k, v in times.items()}
+    log(f"[backward] step {ms:.3f} ms, {flops / (ms * 1e-3) / 1e12:.1f} TFLOP/s algorithmic")
+    for k, v in sorted(per.items(), key=lambda kv: -kv[1] * times[kv[0]][1]):
+        log(f"   {k:20s} avg {v:.4f} ms x {times[k][1] // 3} per step")
+    del grads
+    return {"workload": "llama3-8b-shaped block backward of a zero-state prefill, B=1 L=4096 (x and nine weight "
+                        "gradients; forward recomputed)",
+            "step_ms": round(ms, 3), "algorithmic_tflop": round(flops / 1e12, 4),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "frac_of_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "attention_ms": round(per.get("bwd_attention", 0.0), 3)}
+
+
 def bench_decode(args, torch):
     from gqa_causal_attention_amd import Block
     from gqa_causal_attention_amd.workloads import make_workload
@@ -381,6 +422,7 @@ def main():
     ap.add_argument("--variant", choices=list(VARIANTS), default="plain",
                     help="block options on the same shapes (default: the plain Llama-shaped block)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="decode line only (profiling); no JSON headline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (scale for the --pmc byte counters)")
@@ -407,6 +449,7 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch)
     dec = None if args.no_decode else bench_decode(args, torch)
+    bwd = None if (args.no_backward or args.variant != "plain") else bench_backward(args, torch, pre["wl"])
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(pre)
@@ -438,6 +481,8 @@ def main():
                          "tokens_per_s": round(dec["tokens_per_s"], 1),
                          "algorithmic_bytes": dec["bytes"], "achieved_gbs": round(dec["gbs"], 1),
                          "frac_of_hbm_peak": round(dec["frac"], 4), "roofline": dec["roofline"]}
+    if bwd:
+        out["backward"] = bwd
     print(json.dumps(out), flush=True)
 
 
