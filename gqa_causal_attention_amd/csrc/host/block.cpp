@@ -460,7 +460,7 @@ struct BusyGuard {
 };
 
 int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, int L, void* ws, size_t wsb,
-              hipStream_t s) {
+              hipStream_t s, float* attn_lse = nullptr) {
   if (!blk) return fail(GQA_ERR_ARG, "block is NULL");
   const auto& c = blk->cfg;
   if (B < 0 || L < 0) return fail(GQA_ERR_ARG, "B and L must be >= 0");
@@ -629,6 +629,7 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
       Scope sc(tm, "attn_combine", s);
       HIP_TRY(launch_attention_decode_combine(a, s));
     } else if (bf && attention_prefill_bf16_supported(hd, blk->G)) {
+      a.lse = attn_lse;
       Scope sc(tm, "attn_prefill", s);
       HIP_TRY(launch_attention_prefill_bf16(a, s));
     } else {
@@ -740,7 +741,7 @@ bool backward_supported(const gqa_block_config& c) {
 struct BwdLayout {
   WsLayout fwd;  // the recomputed forward's workspace, at offset 0
   size_t y, gu, lse, dsum, wdT, wguT, woT, wqkvT, dy_op, dyT, da, act, actT, dgu, dguT, h2T, dh2, dx1, dx1_op, dx1T,
-      wpart, cpart, ctxT, dctx, dq, dk, dv, dqkv, dqkvT, hT, dh, part, total;
+      wpart, cpart, ctxT, dctx, dq, dk, dv, dob, dqkv, dqkvT, hT, dh, part, total;
   int Tp;  // token count padded to 256: the depth of the weight-gradient GEMMs
   int Kq;  // q | k | v width padded to 64: the depth of the dh GEMM
 };
@@ -781,8 +782,10 @@ BwdLayout bwd_layout_for(const gqa_block* blk, int B, int L) {
   w.ctxT = take(QW * Tp * es);
   w.dctx = take(T * QW * 4);
   w.dq = take(T * QW * 4);
-  w.dk = take(T * KW * 4);
-  w.dv = take(T * KW * 4);
+  const size_t parts = (size_t)blk->G;  // per-head partials of the matrix-core path
+  w.dk = take(parts * T * KW * 4);
+  w.dv = take(parts * T * KW * 4);
+  w.dob = take(T * QW * 2);
   w.dqkv = take(T * Kq * es);
   w.dqkvT = take(Kq * Tp * es);
   w.hT = take(d * Tp * es);
@@ -830,7 +833,13 @@ int run_backward(gqa_block* blk, const float* x, const float* dy, float* dx, flo
   char* base = static_cast<char*>(ws);
   float* y = reinterpret_cast<float*>(base + lay.y);
   // 0. forward from an empty cache (positions 0 .. L-1), leaving its activations
-  if (int r = run_block(blk, nullptr, x, y, B, L, ws, lay.fwd.total, s)) return r;
+  // (and, on the matrix-core attention path, each row's log-sum-exp)
+  const bool mfma_attn = is_bf16(blk) && !lay.fwd.decode_attn &&
+                         attention_prefill_bf16_supported(c.head_dim, blk->G) &&
+                         attention_bwd_mfma_supported(c.head_dim, blk->G);
+  if (int r = run_block(blk, nullptr, x, y, B, L, ws, lay.fwd.total, s,
+                        mfma_attn ? reinterpret_cast<float*>(base + lay.lse) : nullptr))
+    return r;
   BusyGuard guard(blk->busy);
   if (!guard.ok) return fail(GQA_ERR_BUSY, "block is in use by another call");
 
@@ -971,9 +980,14 @@ int run_backward(gqa_block* blk, const float* x, const float* dy, float* dx, flo
   ba.cos_tab = blk->cos_tab; ba.sin_tab = blk->sin_tab;
   ba.B = B; ba.L = L; ba.H = H; ba.KV = c.n_kv_heads; ba.hd = c.head_dim; ba.window = c.window;
   ba.scale = 1.0f / std::sqrt((float)c.head_dim);
+  ba.kv_parts = mfma_attn ? blk->G : 1;
+  ba.kv_part_stride = (int64_t)T * KW;
   {
     Scope sc(tm, "bwd_attention", s);
-    HIP_TRY(launch_attention_bwd(ba, et, s));
+    if (mfma_attn)
+      HIP_TRY(launch_attention_bwd_mfma(ba, at(lay.dob), s));
+    else
+      HIP_TRY(launch_attention_bwd(ba, et, s));
   }
   void* dqkv = at(lay.dqkv);
   {

@@ -40,6 +40,7 @@
 //    The softcap variant is a separate instantiation; masks are selects on
 //    tiles that cross the diagonal or the window edge only (wave-uniform
 //    tests), and tiles a wave cannot see are skipped.
+#include "attn_tile.h"
 #include "common.h"
 #include "launch.h"
 
@@ -68,29 +69,6 @@ struct PrefillCfg {
 };
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units: lazily rescale beyond 2^8
-
-// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
-// (lds is wave-uniform).  The builtin only exists for the device pass.
-__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-#endif
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
-#else
-  return s16x4{};
-#endif
-}
-
-__device__ __forceinline__ void lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // tanh(x) = 1 - 2 / (e^{2x} + 1) with the hardware reciprocal.
 __device__ __forceinline__ float tanh_rcp(float x) {
@@ -298,9 +276,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_kernel(AttnArgs a, in
     }
   }
 
-  // ---- normalise and write ctx[token, h*HD + d] ----
+  // ---- normalise and write ctx[token, h*HD + d] (and, when asked, the row's
+  // log-sum-exp of the scaled scores in base 2, for the backward) ----
   const int tok = qt0 + (lane & 31);
   const float lt = l_run + xor32(l_run);
+  if (a.lse && wave_valid && tok < L && lane < 32)
+    a.lse[((int64_t)b * L + tok) * a.H + h] = m_ref + __log2f(lt);
   if (wave_valid && tok < L) {
     const float inv = 1.0f / lt;
     bf16* out = static_cast<bf16*>(a.ctx) + ((int64_t)b * L + tok) * ((int64_t)a.H * HD) + (int64_t)h * HD;

@@ -137,20 +137,28 @@ __global__ __launch_bounds__(256) void rope_bwd_pack_kernel(BwdAttnArgs a, T* __
   }
   const int slot = c / hd, e = c % hd;
   const float* src;
+  int parts = 1;  // dk / dv: per-head partials, summed in order
   bool rot = true;
   if (slot < a.H) {
     src = a.dq + (tok * a.H + slot) * hd;
   } else if (slot < a.H + a.KV) {
     src = a.dk + (((int64_t)b * a.KV + (slot - a.H)) * a.L + t) * hd;
+    parts = a.kv_parts;
   } else {
     src = a.dv + (((int64_t)b * a.KV + (slot - a.H - a.KV)) * a.L + t) * hd;
+    parts = a.kv_parts;
     rot = false;
   }
-  float x = src[e];
+  auto val = [&](int i) {
+    float v = src[i];
+    for (int z = 1; z < parts; ++z) v += src[z * a.kv_part_stride + i];
+    return v;
+  };
+  float x = val(e);
   if (rot) {  // forward: y1 = x1 c - x2 s, y2 = x2 c + x1 s  ->  x = R(-angle) y
     const int p = e < half ? e : e - half;
     const float cs = a.cos_tab[(int64_t)t * half + p], sn = a.sin_tab[(int64_t)t * half + p];
-    const float y1 = src[p], y2 = src[p + half];
+    const float y1 = val(p), y2 = val(p + half);
     x = e < half ? y1 * cs + y2 * sn : y2 * cs - y1 * sn;
   }
   dqkv[i] = from_f32<T>(x);

@@ -138,6 +138,7 @@ struct AttnArgs {
   float softcap;           // 0 = off
   float* part;             // decode partials [H, rec_stride, hd + 2]: record s + b = row b's piece of segment s
   int nseg, rec_stride;    // decode: key segments per kv head; records per head (>= nseg + B)
+  float* lse;              // prefill (bf16 kernel): if set, [T, H] log2-sum-exp2 of the scaled scores
 };
 hipError_t launch_attention_generic(const AttnArgs& a, int elem, hipStream_t s);
 hipError_t launch_attention_prefill_bf16(const AttnArgs& a, hipStream_t s);
@@ -162,8 +163,10 @@ struct BwdAttnArgs {
   float* lse;              // [T, H] row log-sum-exp of the scaled scores, base 2 (written)
   float* dsum;             // [T, H] rowsum(dO * O) (written)
   float* dq;               // [T, H, hd] gradient of the post-RoPE queries
-  float* dk;               // [B, KV, L, hd] gradient of the post-RoPE keys
-  float* dv;               // [B, KV, L, hd]
+  float* dk;               // [kv_parts][B, KV, L, hd] gradient of the post-RoPE keys (partials summed
+  float* dv;               //   in part order by launch_rope_bwd_pack)
+  int kv_parts;            // 1, or G per-head partials (matrix-core path)
+  int64_t kv_part_stride;  // elements between partials: B * KV * L * hd
   const float* cos_tab;    // [max_positions, hd/2] (RoPE backward)
   const float* sin_tab;
   int B, L, H, KV, hd, window;
@@ -185,8 +188,12 @@ hipError_t launch_colsum(const float* a, int R, int C, float* part, float* out, 
 // dq | dk | dv, RoPE undone on dq and dk, into the q/k/v GEMM's row layout [T, ld]
 // (ld >= (H + 2 KV) hd; the columns past that width are zero).
 hipError_t launch_rope_bwd_pack(const BwdAttnArgs& a, void* dqkv, int64_t ld, int elem, hipStream_t s);
-// lse, dsum, dq, dk, dv of the attention (causal, optional window).
+// lse, dsum, dq, dk, dv of the attention (causal, optional window): wave kernels, any hd.
 hipError_t launch_attention_bwd(const BwdAttnArgs& a, int elem, hipStream_t s);
+// Matrix-core form (bf16, hd 64 / 128): needs the forward's lse, writes dsum, a bf16
+// copy of dout into dob [T, ldo], dq, and G per-head partials of dk and dv.
+bool attention_bwd_mfma_supported(int hd, int G);
+hipError_t launch_attention_bwd_mfma(const BwdAttnArgs& a, void* dob, hipStream_t s);
 
 hipError_t launch_count_nonfinite(const void* p, int elem, int64_t n, int* flag, hipStream_t s);
 hipError_t launch_bump_lengths(int* lengths, int n, int by, hipStream_t s);

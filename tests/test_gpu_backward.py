@@ -49,7 +49,8 @@ CASES = {
     "f32_tiny": ("f32", dict(), 2, 13),
     "f32_window": ("f32", dict(window=5), 2, 19),
     "f32_odd_dims": ("f32", dict(d_model=50, n_heads=5, n_kv_heads=5, head_dim=10, intermediate=37), 1, 9),
-    # bf16: 128x128 GEMM tiles over T = 300 (ragged), weight-gradient depth padded to 512
+    # bf16 (matrix-core attention backward for head_dim 64 / 128): 128x128 GEMM tiles over
+    # T = 300 (ragged), weight-gradient depth padded to 512
     "bf16_hd128_g4": ("bf16", dict(d_model=256, n_heads=8, n_kv_heads=2, head_dim=128, intermediate=512,
                                    rope_theta=5e5), 1, 300),
     # T = 40: decode-sized products (weight-streaming kernel, K split), window
@@ -57,6 +58,10 @@ CASES = {
                                          window=16), 2, 20),
     # T = 700: the pipelined large-M tiles; q/k/v width 640 + 2 * 64 padded to the GEMM depth
     "bf16_large_t": ("bf16", dict(d_model=512, n_heads=5, n_kv_heads=1, head_dim=128, intermediate=768), 1, 700),
+    # the attention backward's wave-kernel form: head_dim 256, and L = 1
+    "bf16_hd256_wave_form": ("bf16", dict(d_model=256, n_heads=2, n_kv_heads=1, head_dim=256, intermediate=256,
+                                          window=24), 1, 90),
+    "bf16_single_position": ("bf16", dict(d_model=256, n_heads=4, n_kv_heads=2, head_dim=64, intermediate=256), 3, 1),
 }
 
 
