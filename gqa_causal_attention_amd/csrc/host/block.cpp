@@ -459,8 +459,10 @@ struct BusyGuard {
   }
 };
 
+// recompute_only: stop after the MLP's input norm (h2), the activations the
+// backward reads (no MLP, no y).
 int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, int L, void* ws, size_t wsb,
-              hipStream_t s, float* attn_lse = nullptr) {
+              hipStream_t s, float* attn_lse = nullptr, bool recompute_only = false) {
   if (!blk) return fail(GQA_ERR_ARG, "block is NULL");
   const auto& c = blk->cfg;
   if (B < 0 || L < 0) return fail(GQA_ERR_ARG, "B and L must be >= 0");
@@ -674,6 +676,7 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
     na.out = h2;
     if (int r = norm(fuse_o || sandwich ? "resid_rmsnorm" : "rmsnorm", na)) return r;
   }
+  if (recompute_only) return GQA_OK;
   // 7. gate/up (+ biases) and act(gate) * up; ungated MLPs: act(up (+ bias))
   if (mlp_gated(c.mlp)) {
     GemmArgs a{};
@@ -838,7 +841,7 @@ int run_backward(gqa_block* blk, const float* x, const float* dy, float* dx, flo
                          attention_prefill_bf16_supported(c.head_dim, blk->G) &&
                          attention_bwd_mfma_supported(c.head_dim, blk->G);
   if (int r = run_block(blk, nullptr, x, y, B, L, ws, lay.fwd.total, s,
-                        mfma_attn ? reinterpret_cast<float*>(base + lay.lse) : nullptr))
+                        mfma_attn ? reinterpret_cast<float*>(base + lay.lse) : nullptr, true))
     return r;
   BusyGuard guard(blk->busy);
   if (!guard.ok) return fail(GQA_ERR_BUSY, "block is in use by another call");
@@ -904,10 +907,24 @@ int run_backward(gqa_block* blk, const float* x, const float* dy, float* dx, flo
     if (int r_ = (expr)) return r_; \
   } while (0)
 
-  // 1. gate and up pre-activations of the recomputed forward (float32, gate | up per row)
+  // 1. gate and up pre-activations of the recomputed forward (float32, gate | up
+  // per row): one gated GEMM whose single-split partial epilogue writes exactly
+  // that layout, else two plain products
   float* gu = atf(lay.gu);
-  BWD(gemm("bwd_gate", h2, d, blk->w[W_GATE], T, IT, d, gu, 2 * IT));
-  BWD(gemm("bwd_up", h2, d, blk->w[W_UP], T, IT, d, gu + IT, 2 * IT));
+  const GemmPlan pgu = bf ? plan_gemm(T, IT, d, true) : GemmPlan{0, 0, 0};
+  if (bf && pgu.tile != kTileSkinny) {
+    GemmArgs a{};
+    a.A = h2; a.lda = d;
+    a.B[0] = blk->w[W_GATE]; a.B[1] = blk->w[W_UP]; a.B[2] = nullptr;
+    a.M = T; a.N = IT; a.K = d;
+    a.splits = 1; a.k_split = d; a.partial = gu;
+    a.order = gemm_tile_order();
+    Scope sc(tm, "bwd_gate_up", s);
+    HIP_TRY(launch_gemm_bf16(a, kModeGated, kEpiPartial, pgu.tile, s));
+  } else {
+    BWD(gemm("bwd_gate", h2, d, blk->w[W_GATE], T, IT, d, gu, 2 * IT));
+    BWD(gemm("bwd_up", h2, d, blk->w[W_UP], T, IT, d, gu + IT, 2 * IT));
+  }
   // 2. weights as the other product operand (transposed, K-contiguous)
   void* wdT = at(lay.wdT);
   void* wguT = at(lay.wguT);
