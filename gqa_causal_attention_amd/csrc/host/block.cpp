@@ -762,8 +762,9 @@ BwdLayout bwd_layout_for(const gqa_block* blk, int B, int L) {
   const size_t Tp = w.Tp, Kq = w.Kq;
   w.y = take(T * d * 4);
   w.gu = take(T * 2 * IT * 4);
-  w.lse = take(T * H * 4);
-  w.dsum = take(T * H * 4);
+  const size_t lse_n = (size_t)B * H * (((size_t)L + 3) & ~(size_t)3);  // [B, H, L padded to 4] (>= T * H)
+  w.lse = take(lse_n * 4);
+  w.dsum = take(lse_n * 4);
   w.wdT = take(IT * d * es);
   w.wguT = take(d * 2 * IT * es);
   w.woT = take(QW * d * es);
@@ -997,6 +998,7 @@ int run_backward(gqa_block* blk, const float* x, const float* dy, float* dx, flo
   ba.cos_tab = blk->cos_tab; ba.sin_tab = blk->sin_tab;
   ba.B = B; ba.L = L; ba.H = H; ba.KV = c.n_kv_heads; ba.hd = c.head_dim; ba.window = c.window;
   ba.scale = 1.0f / std::sqrt((float)c.head_dim);
+  ba.lse_ld = (L + 3) & ~3;
   ba.kv_parts = mfma_attn ? blk->G : 1;
   ba.kv_part_stride = (int64_t)T * KW;
   {

@@ -6,8 +6,9 @@
 // log-sum-exp instead of storing them): with S = q k^T / sqrt(hd) (masked),
 // P = exp(S - lse), dP = dO v^T, D = rowsum(dO * O):
 //   dS = P * (dP - D),  dq = dS k / sqrt(hd),  dk = dS^T q / sqrt(hd),  dv = P^T dO.
-// The forward kernel leaves lse (base 2) per (token, head); a prep kernel forms D
-// and a bf16 copy of dO.
+// The forward kernel leaves lse (base 2) per (row, head, token) with each
+// head's tokens contiguous; a prep kernel forms D in the same layout and a bf16
+// copy of dO.
 //
 // Both kernels use the forward kernel's product shapes on
 // v_mfma_f32_32x32x16_bf16 and its LDS conventions (direct-to-LDS tile loads,
@@ -135,8 +136,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq_kernel(BwdAttnArgs a, 
       df[ks] = *reinterpret_cast<const bf16x8*>(dr + ks * 16);
     }
   }
-  const float lse2 = a.lse[trow * a.H + h];
-  const float dsum = a.dsum[trow * a.H + h];
+  const int64_t hrow = ((int64_t)b * a.H + h) * a.lse_ld + tokc;  // [B, H, lse_ld]
+  const float lse2 = a.lse[hrow];
+  const float dsum = a.dsum[hrow];
   const bf16* kbase = static_cast<const bf16*>(a.k) + ((int64_t)b * a.KV + j) * L * HD;
   const bf16* vbase = static_cast<const bf16*>(a.v) + ((int64_t)b * a.KV + j) * L * HD;
 
@@ -246,8 +248,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdAttnArgs a, con
   }
   const bf16* qbase = static_cast<const bf16*>(a.q) + (int64_t)b * L * a.ldq + (int64_t)h * HD;
   const bf16* dbase = dob + (int64_t)b * L * a.ldo + (int64_t)h * HD;
-  const float* lse = a.lse + (int64_t)b * L * a.H + h;
-  const float* dsm = a.dsum + (int64_t)b * L * a.H + h;
+  const float* lse = a.lse + ((int64_t)b * a.H + h) * a.lse_ld;  // this head's queries contiguous
+  const float* dsm = a.dsum + ((int64_t)b * a.H + h) * a.lse_ld;
 
   auto issue = [&](int t, int stage) {
     const int qb = qlo + t * 32;
@@ -281,17 +283,25 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdAttnArgs a, con
     // some query of the tile sees some key of the wave
     const bool use = wave_valid && qb + 31 >= kw0 && !(W > 0 && qb > kw_hi + W - 1);
     if (use) {
+      // this lane's rows are 4 runs of 4 consecutive queries: (e/4)*8 + (lane/32)*4 + e%4
+      f32x4 l4[4], d4[4];
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        // clamped into the padded row (entries past L only feed masked rows); 16-byte aligned
+        const int q4 = min(qb + e4 * 8 + (lane >> 5) * 4, a.lse_ld - 4);
+        l4[e4] = *reinterpret_cast<const f32x4*>(lse + q4);
+        d4[e4] = *reinterpret_cast<const f32x4*>(dsm + q4);
+      }
       const f32x16 s = rows_x_cols<HD>(sQ, kf, lane);               // S [queries][keys]
       const f32x16 dp = rows_x_cols<HD>(sQ + C::TILE, vf, lane);    // dP
       f32x16 p, ds;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int q = qb + acc_row(e, lane);
-        const int qc = min(q, L - 1);
         const bool ok = q < L && q >= my_k && (W == 0 || q - my_k < W);
-        const float pv = ok ? exp2_fast(s[e] * s_log2 - lse[(int64_t)qc * a.H]) : 0.f;
+        const float pv = ok ? exp2_fast(s[e] * s_log2 - l4[e / 4][e % 4]) : 0.f;
         p[e] = pv;
-        ds[e] = pv * (dp[e] - dsm[(int64_t)qc * a.H]);
+        ds[e] = ok ? pv * (dp[e] - d4[e / 4][e % 4]) : 0.f;  // (padding entries of D are not written)
       }
       tr_acc<HD>(sQ + 3 * C::TILE, p, dv, lane);                    // dV^T += dO^T P
       tr_acc<HD>(sQ + 2 * C::TILE, ds, dk, lane);                   // dK^T += Q^T dS
@@ -338,7 +348,8 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdAttnArgs a, bf16*
     db[e] = from_f32<bf16>(d);
   }
   s = wave_sum(s);
-  if (lane == 0) a.dsum[wid] = s;
+  const int64_t b = tok / a.L, t = tok % a.L;
+  if (lane == 0) a.dsum[(b * a.H + h) * a.lse_ld + t] = s;
 }
 
 int dq_waves(int G) { return G * (G >= 5 ? 1 : 8 / G); }  // as the forward: G heads x 32-query waves

@@ -281,7 +281,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_kernel(AttnArgs a, in
   const int tok = qt0 + (lane & 31);
   const float lt = l_run + xor32(l_run);
   if (a.lse && wave_valid && tok < L && lane < 32)
-    a.lse[((int64_t)b * L + tok) * a.H + h] = m_ref + __log2f(lt);
+    a.lse[((int64_t)b * a.H + h) * ((L + 3) & ~3) + tok] = m_ref + __log2f(lt);
   if (wave_valid && tok < L) {
     const float inv = 1.0f / lt;
     bf16* out = static_cast<bf16*>(a.ctx) + ((int64_t)b * L + tok) * ((int64_t)a.H * HD) + (int64_t)h * HD;

@@ -138,7 +138,8 @@ struct AttnArgs {
   float softcap;           // 0 = off
   float* part;             // decode partials [H, rec_stride, hd + 2]: record s + b = row b's piece of segment s
   int nseg, rec_stride;    // decode: key segments per kv head; records per head (>= nseg + B)
-  float* lse;              // prefill (bf16 kernel): if set, [T, H] log2-sum-exp2 of the scaled scores
+  float* lse;              // prefill (bf16 kernel): if set, [B, H, Lp] log2-sum-exp2 of the scaled scores,
+                           //   Lp = L rounded up to a multiple of 4
 };
 hipError_t launch_attention_generic(const AttnArgs& a, int elem, hipStream_t s);
 hipError_t launch_attention_prefill_bf16(const AttnArgs& a, hipStream_t s);
@@ -160,8 +161,9 @@ struct BwdAttnArgs {
   const void* o;           // attention output [T, ldo]
   int64_t ldo;
   const float* dout;       // gradient of the attention output [T, ldo], float32
-  float* lse;              // [T, H] row log-sum-exp of the scaled scores, base 2 (written)
-  float* dsum;             // [T, H] rowsum(dO * O) (written)
+  float* lse;              // row log-sum-exp of the scaled scores, base 2: [T, H] (wave kernels, written)
+                           //   or [B, H, lse_ld] (matrix-core kernels, from the forward)
+  float* dsum;             // rowsum(dO * O), same layout as lse (written)
   float* dq;               // [T, H, hd] gradient of the post-RoPE queries
   float* dk;               // [kv_parts][B, KV, L, hd] gradient of the post-RoPE keys (partials summed
   float* dv;               //   in part order by launch_rope_bwd_pack)
@@ -170,6 +172,7 @@ struct BwdAttnArgs {
   const float* cos_tab;    // [max_positions, hd/2] (RoPE backward)
   const float* sin_tab;
   int B, L, H, KV, hd, window;
+  int lse_ld;              // matrix-core layout: L rounded up to a multiple of 4
   float scale;             // 1 / sqrt(hd)
 };
 // [R, C] (row stride ld) -> out[c * ldo + r] for r < Rp (zero for r >= R).
