@@ -414,13 +414,14 @@ hipError_t launch_rms_bwd(const float* dy, const float* x, const float* w, const
   return hipGetLastError();
 }
 
-int colsum_chunks(int R) { return (R + 255) / 256; }
+constexpr int kColsumRows = 32;  // rows per chunk: enough chunks to fill the GPU at 4k tokens
+int colsum_chunks(int R) { return (R + kColsumRows - 1) / kColsumRows; }
 
 hipError_t launch_colsum(const float* a, int R, int C, float* part, float* out, hipStream_t s) {
   if (C <= 0) return hipSuccess;
   const int nz = R > 0 ? colsum_chunks(R) : 0;
   if (nz > 0)
-    hipLaunchKernelGGL(colsum_part_kernel, dim3((C + 255) / 256, nz), dim3(256), 0, s, a, R, C, 256, part);
+    hipLaunchKernelGGL(colsum_part_kernel, dim3((C + 255) / 256, nz), dim3(256), 0, s, a, R, C, kColsumRows, part);
   hipLaunchKernelGGL(colsum_final_kernel, dim3((C + 255) / 256), dim3(256), 0, s, part, nz, C, out);
   return hipGetLastError();
 }
