@@ -27,6 +27,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <cstdint>
+
 namespace gqa {
 namespace {
 
@@ -54,6 +56,91 @@ __global__ __launch_bounds__(256) void transpose_kernel(const TI* __restrict__ i
   for (int i = ty; i < 64; i += 4) {
     const int c = c0 + i, r = r0 + tx;
     if (c < C && r < Rp) out[(int64_t)c * ldo + r] = from_f32<TO>(tile[tx][i]);
+  }
+}
+
+// Vector form: 16-byte accesses on both sides (8 elements per thread along the
+// input row when loading, along the output row when storing); needs ld, ldo
+// and C multiples of 8 and 16-byte aligned bases.
+template <typename T>
+struct Vec8;
+template <>
+struct Vec8<bf16> {
+  typedef bf16x8 type;
+};
+template <>
+struct Vec8<float> {
+  struct type {
+    f32x4 lo, hi;
+  };
+};
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&v)[8]);
+template <>
+__device__ __forceinline__ void load8<bf16>(const bf16* p, float (&v)[8]) {
+  const bf16x8 x = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = to_f32(x[e]);
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[e] = a[e];
+    v[4 + e] = b[e];
+  }
+}
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float (&v)[8]);
+template <>
+__device__ __forceinline__ void store8<bf16>(bf16* p, const float (&v)[8]) {
+  bf16x8 x;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = from_f32<bf16>(v[e]);
+  *reinterpret_cast<bf16x8*>(p) = x;
+}
+template <>
+__device__ __forceinline__ void store8<float>(float* p, const float (&v)[8]) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+
+template <typename TI, typename TO>
+__global__ __launch_bounds__(256) void transpose_vec_kernel(const TI* __restrict__ in, int64_t ld, int R, int C,
+                                                           TO* __restrict__ out, int64_t ldo, int Rp) {
+  __shared__ float tile[64][65];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int idx = threadIdx.x + 256 * pass;
+    const int r = idx >> 3, c8 = (idx & 7) * 8;
+    float v[8];
+    if (r0 + r < R && c0 + c8 < C) {  // C % 8 == 0: the 8 columns are all in or all out
+      load8<TI>(in + (int64_t)(r0 + r) * ld + c0 + c8, v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[r][c8 + e] = v[e];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int idx = threadIdx.x + 256 * pass;
+    const int oc = idx >> 3, r8 = (idx & 7) * 8;
+    const int c = c0 + oc, r = r0 + r8;
+    if (c >= C || r >= Rp) continue;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = tile[r8 + e][oc];
+    TO* o = out + (int64_t)c * ldo + r;
+    if (r + 8 <= Rp) {
+      store8<TO>(o, v);
+    } else {
+      for (int e = 0; e < Rp - r; ++e) o[e] = from_f32<TO>(v[e]);
+    }
   }
 }
 
@@ -374,6 +461,23 @@ hipError_t launch_transpose(const void* in, int in_type, int64_t ld, int R, int 
   if (Rp <= 0 || C <= 0) return hipSuccess;
   if (Rp < R || ldo < Rp) return hipErrorInvalidValue;
   dim3 grid((C + 63) / 64, (Rp + 63) / 64);
+  const size_t ie = in_type == kF32 ? 4 : 2, oe = out_type == kF32 ? 4 : 2;
+  const bool vec = ld % 8 == 0 && ldo % 8 == 0 && C % 8 == 0 && reinterpret_cast<uintptr_t>(in) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(out) % 16 == 0 && ie * 8 % 16 == 0 && oe * 8 % 16 == 0;
+  if (vec) {
+    if (in_type == kF32 && out_type == kF32)
+      hipLaunchKernelGGL((transpose_vec_kernel<float, float>), grid, dim3(256), 0, s, static_cast<const float*>(in),
+                         ld, R, C, static_cast<float*>(out), ldo, Rp);
+    else if (in_type == kF32 && out_type == kBF16)
+      hipLaunchKernelGGL((transpose_vec_kernel<float, bf16>), grid, dim3(256), 0, s, static_cast<const float*>(in),
+                         ld, R, C, static_cast<bf16*>(out), ldo, Rp);
+    else if (in_type == kBF16 && out_type == kBF16)
+      hipLaunchKernelGGL((transpose_vec_kernel<bf16, bf16>), grid, dim3(256), 0, s, static_cast<const bf16*>(in),
+                         ld, R, C, static_cast<bf16*>(out), ldo, Rp);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   if (in_type == kF32 && out_type == kF32)
     hipLaunchKernelGGL((transpose_kernel<float, float>), grid, dim3(256), 0, s, static_cast<const float*>(in), ld, R, C,
                        static_cast<float*>(out), ldo, Rp);
