@@ -879,7 +879,10 @@ int run_backward(gqa_block* blk, const float* x, const float* dy, float* dx, flo
       HIP_TRY(launch_gemm_f32(a, kModeSeg, kEpiResid, s));
       return GQA_OK;
     }
-    const GemmPlan p = plan_gemm(M, N, K, false);
+    GemmPlan p = plan_gemm(M, N, K, false);
+    // a grid of 256x256 tiles well short of the 256 CUs (the k/v weight
+    // gradients: 64 tiles) takes 128x128 tiles instead
+    if (gemm_dma_tile(p.tile) && (long)((M + 255) / 256) * ((N + 255) / 256) < 192) p = GemmPlan{kTile128x128, 1, 0};
     a.wg_waves = p.waves;
     if (p.splits <= 1) {
       a.splits = 1;

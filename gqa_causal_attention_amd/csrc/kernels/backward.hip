@@ -185,6 +185,63 @@ __global__ __launch_bounds__(256) void rms_bwd_kernel(const float* __restrict__ 
   }
 }
 
+// Register form (d % 4 == 0, d <= 1024 * MAXV): each row read once, 16-byte
+// accesses at clamped columns, out-of-row pieces zeroed by selects.
+template <typename T, int MAXV>
+__global__ __launch_bounds__(256) void rms_bwd_vec_kernel(const float* __restrict__ dy, const float* __restrict__ x,
+                                                         const float* __restrict__ w,
+                                                         const float* __restrict__ resid, int d, float eps,
+                                                         float* __restrict__ dx, T* __restrict__ dx_op,
+                                                         float* __restrict__ wpart) {
+  __shared__ float red[4];
+  const int64_t off = (int64_t)blockIdx.x * d;
+  const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+  int ci[MAXV];
+  bool in[MAXV];
+  f32x4 xv[MAXV], gv[MAXV];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int idx = (threadIdx.x + i * 256) * 4;
+    in[i] = idx < d;
+    ci[i] = in[i] ? idx : d - 4;
+    const f32x4 xx = *reinterpret_cast<const f32x4*>(x + off + ci[i]);
+    const f32x4 yy = *reinterpret_cast<const f32x4*>(dy + off + ci[i]);
+    const f32x4 ww = *reinterpret_cast<const f32x4*>(w + ci[i]);
+    xv[i] = in[i] ? xx : zero;
+    gv[i] = in[i] ? yy * ww : zero;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss += xv[i][e] * xv[i][e];
+  }
+  const float r = 1.0f / sqrtf(block_sum<256>(ss, red) / (float)d + eps);
+  float gx = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) gx += gv[i][e] * xv[i][e];
+  const float m = block_sum<256>(gx, red) * r / (float)d;  // mean(g x^)
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    if (!in[i]) continue;
+    const f32x4 rs = *reinterpret_cast<const f32x4*>(resid + off + ci[i]);
+    const f32x4 yy = *reinterpret_cast<const f32x4*>(dy + off + ci[i]);
+    f32x4 v, wp;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float xh = xv[i][e] * r;
+      v[e] = rs[e] + r * (gv[i][e] - xh * m);
+      wp[e] = yy[e] * xh;
+    }
+    *reinterpret_cast<f32x4*>(dx + off + ci[i]) = v;
+    *reinterpret_cast<f32x4*>(wpart + off + ci[i]) = wp;
+    if (dx_op) {
+      T* o = dx_op + off + ci[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = from_f32<T>(v[e]);
+    }
+  }
+}
+
 // Column sums of a [R, C] float32 matrix: chunk z of rows -> part[z, c], then
 // out[c] = sum over chunks in order.
 __global__ __launch_bounds__(256) void colsum_part_kernel(const float* __restrict__ a, int R, int C, int rows_per,
@@ -249,6 +306,74 @@ __global__ __launch_bounds__(256) void rope_bwd_pack_kernel(BwdAttnArgs a, T* __
     x = e < half ? y1 * cs + y2 * sn : y2 * cs - y1 * sn;
   }
   dqkv[i] = from_f32<T>(x);
+}
+
+// Vector form (hd % 8 == 0): a thread per 4 rotate-half pairs of one head slot
+// (two 4-element stores), then threads that zero the padding 8 columns at a time.
+template <typename T>
+__device__ __forceinline__ void store4v(T* p, const f32x4& v) {
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<bf16x4*>(p) = bf16x4{from_f32<bf16>(v[0]), from_f32<bf16>(v[1]), from_f32<bf16>(v[2]),
+                                          from_f32<bf16>(v[3])};
+  } else {
+    *reinterpret_cast<f32x4*>(p) = v;
+  }
+}
+template <typename T>
+__global__ __launch_bounds__(256) void rope_bwd_pack4_kernel(BwdAttnArgs a, T* __restrict__ dqkv, int64_t ld) {
+  const int hd = a.hd, half = hd / 2, ng = half / 4;
+  const int slots = a.H + 2 * a.KV;
+  const int width = slots * hd;
+  const int64_t T_ = (int64_t)a.B * a.L;
+  const int64_t n_main = T_ * slots * ng;
+  const int pad8 = (int)((ld - width) / 8);
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_main) {
+    const int64_t k = i - n_main;
+    if (k >= T_ * pad8) return;
+    const int64_t tok = k / pad8;
+    T* o = dqkv + tok * ld + width + (k % pad8) * 8;
+    store4v<T>(o, f32x4{0.f, 0.f, 0.f, 0.f});
+    store4v<T>(o + 4, f32x4{0.f, 0.f, 0.f, 0.f});
+    return;
+  }
+  const int g = (int)(i % ng);
+  const int64_t hs = i / ng;
+  const int slot = (int)(hs % slots);
+  const int64_t tok = hs / slots;
+  const int b = (int)(tok / a.L), t = (int)(tok % a.L);
+  const int p = 4 * g;
+  const float* src;
+  int parts = 1;
+  bool rot = true;
+  if (slot < a.H) {
+    src = a.dq + (tok * a.H + slot) * hd;
+  } else if (slot < a.H + a.KV) {
+    src = a.dk + (((int64_t)b * a.KV + (slot - a.H)) * a.L + t) * hd;
+    parts = a.kv_parts;
+  } else {
+    src = a.dv + (((int64_t)b * a.KV + (slot - a.H - a.KV)) * a.L + t) * hd;
+    parts = a.kv_parts;
+    rot = false;
+  }
+  f32x4 y1 = *reinterpret_cast<const f32x4*>(src + p), y2 = *reinterpret_cast<const f32x4*>(src + p + half);
+  for (int z = 1; z < parts; ++z) {
+    y1 += *reinterpret_cast<const f32x4*>(src + z * a.kv_part_stride + p);
+    y2 += *reinterpret_cast<const f32x4*>(src + z * a.kv_part_stride + p + half);
+  }
+  f32x4 x1 = y1, x2 = y2;
+  if (rot) {  // x = R(-angle) y
+    const f32x4 c = *reinterpret_cast<const f32x4*>(a.cos_tab + (int64_t)t * half + p);
+    const f32x4 sn = *reinterpret_cast<const f32x4*>(a.sin_tab + (int64_t)t * half + p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x1[e] = y1[e] * c[e] + y2[e] * sn[e];
+      x2[e] = y2[e] * c[e] - y1[e] * sn[e];
+    }
+  }
+  T* o = dqkv + tok * ld + slot * hd + p;
+  store4v<T>(o, x1);
+  store4v<T>(o + half, x2);
 }
 
 // Elementwise float32 -> operand type.
@@ -506,9 +631,25 @@ hipError_t launch_swiglu_bwd(const float* gu, const float* da, int64_t rows, int
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t rms_bwd_vec(const float* dy, const float* x, const float* w, const float* resid, int rows, int d, float eps,
+                       float* dx, T* dx_op, float* wpart, hipStream_t s) {
+#define GQA_RMS_BWD(MV) \
+  hipLaunchKernelGGL((rms_bwd_vec_kernel<T, MV>), dim3(rows), dim3(256), 0, s, dy, x, w, resid, d, eps, dx, dx_op, wpart)
+  if (d <= 1024 * 2) GQA_RMS_BWD(2);
+  else if (d <= 1024 * 4) GQA_RMS_BWD(4);
+  else if (d <= 1024 * 8) GQA_RMS_BWD(8);
+  else GQA_RMS_BWD(16);
+#undef GQA_RMS_BWD
+  return hipGetLastError();
+}
+
 hipError_t launch_rms_bwd(const float* dy, const float* x, const float* w, const float* resid, int rows, int d,
                           float eps, float* dx, void* dx_op, int elem, float* wpart, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  if (d % 4 == 0 && d <= 1024 * 16)
+    return elem == kBF16 ? rms_bwd_vec<bf16>(dy, x, w, resid, rows, d, eps, dx, static_cast<bf16*>(dx_op), wpart, s)
+                         : rms_bwd_vec<float>(dy, x, w, resid, rows, d, eps, dx, static_cast<float*>(dx_op), wpart, s);
   if (elem == kBF16)
     hipLaunchKernelGGL(rms_bwd_kernel<bf16>, dim3(rows), dim3(256), 0, s, dy, x, w, resid, d, eps, dx,
                        static_cast<bf16*>(dx_op), wpart);
@@ -534,6 +675,16 @@ hipError_t launch_rope_bwd_pack(const BwdAttnArgs& a, void* dqkv, int64_t ld, in
   const int64_t n = (int64_t)a.B * a.L * ld;
   if (n == 0) return hipSuccess;
   if (ld < (int64_t)(a.H + 2 * a.KV) * a.hd) return hipErrorInvalidValue;
+  const int width = (a.H + 2 * a.KV) * a.hd;
+  if (a.hd % 8 == 0 && (ld - width) % 8 == 0 && ld % 4 == 0) {
+    const int64_t n4 = (int64_t)a.B * a.L * ((a.H + 2 * a.KV) * (a.hd / 8) + (ld - width) / 8);
+    dim3 g4((unsigned)((n4 + 255) / 256));
+    if (elem == kBF16)
+      hipLaunchKernelGGL(rope_bwd_pack4_kernel<bf16>, g4, dim3(256), 0, s, a, static_cast<bf16*>(dqkv), ld);
+    else
+      hipLaunchKernelGGL(rope_bwd_pack4_kernel<float>, g4, dim3(256), 0, s, a, static_cast<float*>(dqkv), ld);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((n + 255) / 256));
   if (elem == kBF16)
     hipLaunchKernelGGL(rope_bwd_pack_kernel<bf16>, grid, dim3(256), 0, s, a, static_cast<bf16*>(dqkv), ld);
