@@ -449,18 +449,23 @@ int check_weights(const gqa_block_config* c, const gqa_tensor* ws, int n, const 
 
 struct BusyGuard {
   std::atomic<int>& f;
-  bool ok;
-  explicit BusyGuard(std::atomic<int>& f_) : f(f_) {
+  bool ok, held = false;
+  // take = false: the caller already holds the guard (nothing to take or release)
+  explicit BusyGuard(std::atomic<int>& f_, bool take = true) : f(f_) {
+    if (!take) {
+      ok = true;
+      return;
+    }
     int z = 0;
-    ok = f.compare_exchange_strong(z, 1);
+    ok = held = f.compare_exchange_strong(z, 1);
   }
   ~BusyGuard() {
-    if (ok) f.store(0);
+    if (held) f.store(0);
   }
 };
 
 // recompute_only: stop after the MLP's input norm (h2), the activations the
-// backward reads (no MLP, no y).
+// backward reads (no MLP, no y); the backward holds the busy guard itself.
 int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, int L, void* ws, size_t wsb,
               hipStream_t s, float* attn_lse = nullptr, bool recompute_only = false) {
   if (!blk) return fail(GQA_ERR_ARG, "block is NULL");
@@ -484,7 +489,7 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
   const WsLayout lay = layout_for(blk, B, L);
   if (!ws || wsb < lay.total)
     return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? wsb : (size_t)0, lay.total);
-  BusyGuard guard(blk->busy);
+  BusyGuard guard(blk->busy, !recompute_only);
   if (!guard.ok) return fail(GQA_ERR_BUSY, "block is in use by another call");
 
   char* base = static_cast<char*>(ws);
@@ -834,6 +839,8 @@ int run_backward(gqa_block* blk, const float* x, const float* dy, float* dx, flo
   if (!ws || wsb < lay.total)
     return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? wsb : (size_t)0, lay.total);
 
+  BusyGuard guard(blk->busy);
+  if (!guard.ok) return fail(GQA_ERR_BUSY, "block is in use by another call");
   char* base = static_cast<char*>(ws);
   float* y = reinterpret_cast<float*>(base + lay.y);
   // 0. forward from an empty cache (positions 0 .. L-1), leaving its activations
@@ -844,8 +851,6 @@ int run_backward(gqa_block* blk, const float* x, const float* dy, float* dx, flo
   if (int r = run_block(blk, nullptr, x, y, B, L, ws, lay.fwd.total, s,
                         mfma_attn ? reinterpret_cast<float*>(base + lay.lse) : nullptr, true))
     return r;
-  BusyGuard guard(blk->busy);
-  if (!guard.ok) return fail(GQA_ERR_BUSY, "block is in use by another call");
 
   const int T = B * L, d = c.d_model, QW = blk->QW, KW = blk->KW, IT = c.intermediate, H = c.n_heads;
   const int Tp = lay.Tp, Kq = lay.Kq;
