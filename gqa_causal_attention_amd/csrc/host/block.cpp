@@ -746,8 +746,38 @@ bool backward_supported(const gqa_block_config& c) {
          c.rope_dim == c.head_dim;
 }
 
+// Backward products that read K-major operands in place (the pipelined
+// kernel's transposed-operand mode, 256x256 tiles): the input-gradient
+// products take the weights [out, in] as they are (tr_dx), the
+// weight-gradient products take the activations and their gradients
+// [tokens, features] as they are, K = tokens (tr_dw).  Otherwise those
+// operands are first transposed into K-contiguous copies.
+bool bwd_trans_dx(const gqa_block* blk, int T) {
+  const auto& c = blk->cfg;
+  const int d = c.d_model, IT = c.intermediate, QW = blk->QW, KW = blk->KW;
+  for (int i : {W_DOWN, W_GATE, W_UP, W_O, W_Q, W_K, W_V})
+    if (reinterpret_cast<uintptr_t>(blk->w[i]) % 16 != 0) return false;
+  return is_bf16(blk) && T > 512 && gemm_dma_tile(plan_gemm(T, d, 2 * IT, false).tile) && d % 8 == 0 &&
+         IT % 64 == 0 && QW % 64 == 0 && KW % 64 == 0;
+}
+bool bwd_trans_dw(const gqa_block* blk, int T) {
+  const auto& c = blk->cfg;
+  const int d = c.d_model, IT = c.intermediate, QW = blk->QW, KW = blk->KW;
+  return is_bf16(blk) && T >= 256 && T % 64 == 0 && d % 8 == 0 && IT % 8 == 0 && QW % 8 == 0 && KW % 8 == 0;
+}
+// K splits of a transposed-operand product: enough to bring a small grid of
+// 256x256 tiles near the CU count, keeping each split 64-aligned and at least
+// 256 deep.
+int trans_splits(int M, int N, int K) {
+  const long tiles = (long)((M + 255) / 256) * ((N + 255) / 256);
+  int sp = 1;
+  while (sp < 8 && tiles * sp < 192 && K % (128 * sp) == 0 && K / (2 * sp) >= 256) sp *= 2;
+  return sp;
+}
+
 struct BwdLayout {
   WsLayout fwd;  // the recomputed forward's workspace, at offset 0
+  bool tr_dx, tr_dw;
   size_t y, gu, lse, dsum, wdT, wguT, woT, wqkvT, dy_op, dyT, da, act, actT, dgu, dguT, h2T, dh2, dx1, dx1_op, dx1T,
       wpart, cpart, ctxT, dctx, dq, dk, dv, dob, dqkv, dqkvT, hT, dh, part, total;
   int Tp;  // token count padded to 256: the depth of the weight-gradient GEMMs
@@ -764,31 +794,34 @@ BwdLayout bwd_layout_for(const gqa_block* blk, int B, int L) {
   const size_t d = c.d_model, QW = blk->QW, KW = blk->KW, IT = c.intermediate, H = c.n_heads;
   w.Tp = (int)((T + 255) / 256 * 256);
   w.Kq = (int)((QW + 2 * KW + 63) / 64 * 64);
+  w.tr_dx = bwd_trans_dx(blk, (int)T);
+  w.tr_dw = bwd_trans_dw(blk, (int)T);
+  const bool cx = !w.tr_dx, cw = !w.tr_dw;  // transposed copies needed
   const size_t Tp = w.Tp, Kq = w.Kq;
   w.y = take(T * d * 4);
   w.gu = take(T * 2 * IT * 4);
   const size_t lse_n = (size_t)B * H * (((size_t)L + 3) & ~(size_t)3);  // [B, H, L padded to 4] (>= T * H)
   w.lse = take(lse_n * 4);
   w.dsum = take(lse_n * 4);
-  w.wdT = take(IT * d * es);
-  w.wguT = take(d * 2 * IT * es);
-  w.woT = take(QW * d * es);
-  w.wqkvT = take(d * Kq * es);
+  w.wdT = cx ? take(IT * d * es) : 0;
+  w.wguT = cx ? take(d * 2 * IT * es) : 0;
+  w.woT = cx ? take(QW * d * es) : 0;
+  w.wqkvT = cx ? take(d * Kq * es) : 0;
   w.dy_op = take(T * d * es);
-  w.dyT = take(d * Tp * es);
+  w.dyT = cw ? take(d * Tp * es) : 0;
   w.da = take(T * IT * 4);
   w.act = take(T * IT * es);
-  w.actT = take(IT * Tp * es);
+  w.actT = cw ? take(IT * Tp * es) : 0;
   w.dgu = take(T * 2 * IT * es);
-  w.dguT = take(2 * IT * Tp * es);
-  w.h2T = take(d * Tp * es);
+  w.dguT = cw ? take(2 * IT * Tp * es) : 0;
+  w.h2T = cw ? take(d * Tp * es) : 0;
   w.dh2 = take(T * d * 4);
   w.dx1 = take(T * d * 4);
   w.dx1_op = take(T * d * es);
-  w.dx1T = take(d * Tp * es);
+  w.dx1T = cw ? take(d * Tp * es) : 0;
   w.wpart = take(T * d * 4);
   w.cpart = take((size_t)colsum_chunks((int)T) * d * 4);
-  w.ctxT = take(QW * Tp * es);
+  w.ctxT = cw ? take(QW * Tp * es) : 0;
   w.dctx = take(T * QW * 4);
   w.dq = take(T * QW * 4);
   const size_t parts = (size_t)blk->G;  // per-head partials of the matrix-core path
@@ -796,8 +829,8 @@ BwdLayout bwd_layout_for(const gqa_block* blk, int B, int L) {
   w.dv = take(parts * T * KW * 4);
   w.dob = take(T * QW * 2);
   w.dqkv = take(T * Kq * es);
-  w.dqkvT = take(Kq * Tp * es);
-  w.hT = take(d * Tp * es);
+  w.dqkvT = cw ? take(Kq * Tp * es) : 0;
+  w.hT = cw ? take(d * Tp * es) : 0;
   w.dh = take(T * d * 4);
   size_t part = 0;  // K-split partials of any product whose plan splits
   if (is_bf16(blk)) {
@@ -805,15 +838,21 @@ BwdLayout bwd_layout_for(const gqa_block* blk, int B, int L) {
       const GemmPlan p = plan_gemm((int)M, (int)N, (int)K, false);
       if (p.splits > 1) part = std::max(part, (size_t)p.splits * M * N * 4);
     };
-    need(T, IT, d);       // da
-    need(d, IT, Tp);      // dWd
-    need(T, d, 2 * IT);   // dh2
-    need(IT, d, Tp);      // dWg, dWu
-    need(T, QW, d);       // dctx
-    need(d, QW, Tp);      // dWo
-    need(T, d, Kq);       // dh
-    need(QW, d, Tp);      // dWq
-    need(KW, d, Tp);      // dWk, dWv
+    auto need_t = [&](size_t M, size_t N, size_t K) {
+      const int sp = trans_splits((int)M, (int)N, (int)K);
+      if (sp > 1) part = std::max(part, (size_t)sp * M * N * 4);
+    };
+    auto dx = [&](size_t M, size_t N, size_t K) { w.tr_dx ? need_t(M, N, K) : need(M, N, K); };
+    auto dw = [&](size_t M, size_t N) { w.tr_dw ? need_t(M, N, T) : need(M, N, Tp); };
+    dx(T, IT, d);         // da
+    dw(d, IT);            // dWd
+    dx(T, d, 2 * IT);     // dh2
+    dw(IT, d);            // dWg, dWu
+    dx(T, QW, d);         // dctx
+    dw(d, QW);            // dWo
+    dx(T, d, Kq);         // dh
+    dw(QW, d);            // dWq
+    dw(KW, d);            // dWk, dWv
     need(T, IT, d);       // gate / up of the recompute
   }
   w.part = part ? take(part) : 0;
@@ -905,6 +944,39 @@ int run_backward(gqa_block* blk, const float* x, const float* dy, float* dx, flo
     HIP_TRY(launch_splitk_reduce(a, kModeSeg, kEpiResid, kF32, s));
     return GQA_OK;
   };
+  // C[M, N] (float32) = A B^T with B given K-major (B^T[K, N], row stride ldb,
+  // rows from up to three segments b0 | b1 | b2 ending at K rows e0, e1, e2)
+  // and A given K-major too when ta (A^T[K, M], row stride lda)
+  auto gemm_t = [&](const char* name, const void* A, int64_t lda, bool ta, const void* b0, const void* b1,
+                    const void* b2, int64_t e0, int64_t e1, int64_t e2, int64_t ldb, int M, int N, int K, float* C,
+                    int64_t ldc) -> int {
+    GemmArgs a{};
+    a.A = A; a.lda = lda;
+    a.B[0] = b0; a.B[1] = b1; a.B[2] = b2;
+    a.seg_end[0] = e0; a.seg_end[1] = e1; a.seg_end[2] = e2;
+    a.ldb = ldb;
+    a.trans = (ta ? 1 : 0) | 2;
+    a.M = M; a.N = N; a.K = K;
+    a.C = C; a.ldc = ldc;
+    a.order = gemm_tile_order();
+    Scope sc(tm, name, s);
+    const int sp = trans_splits(M, N, K);
+    if (sp <= 1) {
+      a.splits = 1;
+      a.k_split = K;
+      HIP_TRY(launch_gemm_bf16(a, kModeSeg, kEpiResid, kTileDma256x256, s));
+      return GQA_OK;
+    }
+    GemmArgs pa = a;
+    pa.splits = sp;
+    pa.k_split = K / sp;
+    pa.partial = part;
+    HIP_TRY(launch_gemm_bf16(pa, kModeSeg, kEpiPartial, kTileDma256x256, s));
+    a.splits = sp;
+    a.partial = part;
+    HIP_TRY(launch_splitk_reduce(a, kModeSeg, kEpiResid, kF32, s));
+    return GQA_OK;
+  };
   auto tr = [&](const char* name, const void* in, int in_t, int64_t ld, int R, int C, void* out, int64_t ldo,
                 int Rp) -> int {
     Scope sc(tm, name, s);
@@ -939,14 +1011,23 @@ int run_backward(gqa_block* blk, const float* x, const float* dy, float* dx, flo
   void* wguT = at(lay.wguT);
   void* woT = at(lay.woT);
   void* wqkvT = at(lay.wqkvT);
-  BWD(tr("bwd_transpose_w", blk->w[W_DOWN], et, IT, d, IT, wdT, d, d));
-  BWD(tr("bwd_transpose_w", blk->w[W_GATE], et, d, IT, d, wguT, 2 * IT, IT));
-  BWD(tr("bwd_transpose_w", blk->w[W_UP], et, d, IT, d, static_cast<char*>(wguT) + (size_t)IT * es, 2 * IT, IT));
-  BWD(tr("bwd_transpose_w", blk->w[W_O], et, QW, d, QW, woT, d, d));
-  BWD(tr("bwd_transpose_w", blk->w[W_Q], et, d, QW, d, wqkvT, Kq, QW));
-  BWD(tr("bwd_transpose_w", blk->w[W_K], et, d, KW, d, static_cast<char*>(wqkvT) + (size_t)QW * es, Kq, KW));
-  BWD(tr("bwd_transpose_w", blk->w[W_V], et, d, KW, d, static_cast<char*>(wqkvT) + (size_t)(QW + KW) * es, Kq,
-         Kq - QW - KW));
+  if (!lay.tr_dx) {
+    BWD(tr("bwd_transpose_w", blk->w[W_DOWN], et, IT, d, IT, wdT, d, d));
+    BWD(tr("bwd_transpose_w", blk->w[W_GATE], et, d, IT, d, wguT, 2 * IT, IT));
+    BWD(tr("bwd_transpose_w", blk->w[W_UP], et, d, IT, d, static_cast<char*>(wguT) + (size_t)IT * es, 2 * IT, IT));
+    BWD(tr("bwd_transpose_w", blk->w[W_O], et, QW, d, QW, woT, d, d));
+    BWD(tr("bwd_transpose_w", blk->w[W_Q], et, d, QW, d, wqkvT, Kq, QW));
+    BWD(tr("bwd_transpose_w", blk->w[W_K], et, d, KW, d, static_cast<char*>(wqkvT) + (size_t)QW * es, Kq, KW));
+    BWD(tr("bwd_transpose_w", blk->w[W_V], et, d, KW, d, static_cast<char*>(wqkvT) + (size_t)(QW + KW) * es, Kq,
+           Kq - QW - KW));
+  }
+  // weight gradient dW[M, N] = sum over tokens of g[t, m] x[t, n]: g and x
+  // read in place when tr_dw, else from their transposed copies
+  auto gemm_dw = [&](const void* g, int64_t ldg, const void* gT, const void* xx, int64_t ldx, const void* xT, int M,
+                     int N, float* C) -> int {
+    if (lay.tr_dw) return gemm_t("bwd_gemm_dw", g, ldg, true, xx, xx, xx, T, T, T, ldx, M, N, T, C, N);
+    return gemm("bwd_gemm_dw", gT, Tp, xT, M, N, Tp, C, N);
+  };
   // 3. down: da = dy Wd, dWd = dy^T a
   const void* dy_op = dy;
   if (bf) {
@@ -955,9 +1036,14 @@ int run_backward(gqa_block* blk, const float* x, const float* dy, float* dx, flo
     dy_op = at(lay.dy_op);
   }
   void* dyT = at(lay.dyT);
-  BWD(tr("bwd_transpose", dy, kF32, d, T, d, dyT, Tp, Tp));
+  if (!lay.tr_dw) BWD(tr("bwd_transpose", dy, kF32, d, T, d, dyT, Tp, Tp));
   float* da = atf(lay.da);
-  BWD(gemm("bwd_gemm_da", dy_op, d, wdT, T, IT, d, da, IT));
+  if (lay.tr_dx) {
+    const void* wd = blk->w[W_DOWN];
+    BWD(gemm_t("bwd_gemm_da", dy_op, d, false, wd, wd, wd, d, d, d, IT, T, IT, d, da, IT));
+  } else {
+    BWD(gemm("bwd_gemm_da", dy_op, d, wdT, T, IT, d, da, IT));
+  }
   // 4. SwiGLU: a = silu(g) u (for dWd), dg | du
   void* act = at(lay.act);
   void* dgu = at(lay.dgu);
@@ -966,17 +1052,23 @@ int run_backward(gqa_block* blk, const float* x, const float* dy, float* dx, flo
     HIP_TRY(launch_swiglu_bwd(gu, da, T, IT, act, dgu, et, s));
   }
   void* actT = at(lay.actT);
-  BWD(tr("bwd_transpose", act, et, IT, T, IT, actT, Tp, Tp));
-  BWD(gemm("bwd_gemm_dw", dyT, Tp, actT, d, IT, Tp, dw[8], IT));
+  if (!lay.tr_dw) BWD(tr("bwd_transpose", act, et, IT, T, IT, actT, Tp, Tp));
+  BWD(gemm_dw(dy_op, d, dyT, act, IT, actT, d, IT, dw[8]));
   // 5. gate / up: dh2 = dg Wg + du Wu, dWg = dg^T h2, dWu = du^T h2
   float* dh2 = atf(lay.dh2);
-  BWD(gemm("bwd_gemm_dh2", dgu, 2 * IT, wguT, T, d, 2 * IT, dh2, d));
+  if (lay.tr_dx)
+    BWD(gemm_t("bwd_gemm_dh2", dgu, 2 * IT, false, blk->w[W_GATE], blk->w[W_UP], blk->w[W_UP], IT, 2 * IT, 2 * IT,
+               d, T, d, 2 * IT, dh2, d));
+  else
+    BWD(gemm("bwd_gemm_dh2", dgu, 2 * IT, wguT, T, d, 2 * IT, dh2, d));
   void* dguT = at(lay.dguT);
   void* h2T = at(lay.h2T);
-  BWD(tr("bwd_transpose", dgu, et, 2 * IT, T, 2 * IT, dguT, Tp, Tp));
-  BWD(tr("bwd_transpose", h2, et, d, T, d, h2T, Tp, Tp));
-  BWD(gemm("bwd_gemm_dw", dguT, Tp, h2T, IT, d, Tp, dw[6], d));
-  BWD(gemm("bwd_gemm_dw", sub(dguT, (size_t)IT * Tp), Tp, h2T, IT, d, Tp, dw[7], d));
+  if (!lay.tr_dw) {
+    BWD(tr("bwd_transpose", dgu, et, 2 * IT, T, 2 * IT, dguT, Tp, Tp));
+    BWD(tr("bwd_transpose", h2, et, d, T, d, h2T, Tp, Tp));
+  }
+  BWD(gemm_dw(dgu, 2 * IT, dguT, h2, d, h2T, IT, d, dw[6]));
+  BWD(gemm_dw(sub(dgu, IT), 2 * IT, lay.tr_dw ? nullptr : sub(dguT, (size_t)IT * Tp), h2, d, h2T, IT, d, dw[7]));
   // 6. post-attention RMSNorm backward + the residual: dx1 = dy + norm'(dh2)
   float* dx1 = atf(lay.dx1);
   void* dx1_op = bf ? at(lay.dx1_op) : static_cast<void*>(dx1);
@@ -989,12 +1081,19 @@ int run_backward(gqa_block* blk, const float* x, const float* dy, float* dx, flo
   }
   // 7. o_proj: dctx = dx1 Wo, dWo = dx1^T ctx
   float* dctx = atf(lay.dctx);
-  BWD(gemm("bwd_gemm_dctx", dx1_op, d, woT, T, QW, d, dctx, QW));
+  if (lay.tr_dx) {
+    const void* wo = blk->w[W_O];
+    BWD(gemm_t("bwd_gemm_dctx", dx1_op, d, false, wo, wo, wo, d, d, d, QW, T, QW, d, dctx, QW));
+  } else {
+    BWD(gemm("bwd_gemm_dctx", dx1_op, d, woT, T, QW, d, dctx, QW));
+  }
   void* dx1T = at(lay.dx1T);
   void* ctxT = at(lay.ctxT);
-  BWD(tr("bwd_transpose", dx1, kF32, d, T, d, dx1T, Tp, Tp));
-  BWD(tr("bwd_transpose", ctx, et, QW, T, QW, ctxT, Tp, Tp));
-  BWD(gemm("bwd_gemm_dw", dx1T, Tp, ctxT, d, QW, Tp, dw[5], QW));
+  if (!lay.tr_dw) {
+    BWD(tr("bwd_transpose", dx1, kF32, d, T, d, dx1T, Tp, Tp));
+    BWD(tr("bwd_transpose", ctx, et, QW, T, QW, ctxT, Tp, Tp));
+  }
+  BWD(gemm_dw(dx1_op, d, dx1T, ctx, QW, ctxT, d, QW, dw[5]));
   // 8. attention, then RoPE's backward, packed as the q/k/v GEMM's rows
   BwdAttnArgs ba{};
   ba.q = qkv; ba.ldq = QW + 2 * KW;
@@ -1023,14 +1122,22 @@ int run_backward(gqa_block* blk, const float* x, const float* dy, float* dx, flo
   }
   // 9. q/k/v: dh = [dq|dk|dv] [Wq;Wk;Wv], dW = d^T h
   float* dh = atf(lay.dh);
-  BWD(gemm("bwd_gemm_dh", dqkv, Kq, wqkvT, T, d, Kq, dh, d));
+  if (lay.tr_dx)
+    BWD(gemm_t("bwd_gemm_dh", dqkv, Kq, false, blk->w[W_Q], blk->w[W_K], blk->w[W_V], QW, QW + KW, QW + 2 * KW, d,
+               T, d, Kq, dh, d));
+  else
+    BWD(gemm("bwd_gemm_dh", dqkv, Kq, wqkvT, T, d, Kq, dh, d));
   void* dqkvT = at(lay.dqkvT);
   void* hT = at(lay.hT);
-  BWD(tr("bwd_transpose", dqkv, et, Kq, T, Kq, dqkvT, Tp, Tp));
-  BWD(tr("bwd_transpose", h, et, d, T, d, hT, Tp, Tp));
-  BWD(gemm("bwd_gemm_dw", dqkvT, Tp, hT, QW, d, Tp, dw[2], d));
-  BWD(gemm("bwd_gemm_dw", sub(dqkvT, (size_t)QW * Tp), Tp, hT, KW, d, Tp, dw[3], d));
-  BWD(gemm("bwd_gemm_dw", sub(dqkvT, (size_t)(QW + KW) * Tp), Tp, hT, KW, d, Tp, dw[4], d));
+  if (!lay.tr_dw) {
+    BWD(tr("bwd_transpose", dqkv, et, Kq, T, Kq, dqkvT, Tp, Tp));
+    BWD(tr("bwd_transpose", h, et, d, T, d, hT, Tp, Tp));
+  }
+  const bool tw = lay.tr_dw;
+  BWD(gemm_dw(dqkv, Kq, dqkvT, h, d, hT, QW, d, dw[2]));
+  BWD(gemm_dw(sub(dqkv, QW), Kq, tw ? nullptr : sub(dqkvT, (size_t)QW * Tp), h, d, hT, KW, d, dw[3]));
+  BWD(gemm_dw(sub(dqkv, (size_t)QW + KW), Kq, tw ? nullptr : sub(dqkvT, (size_t)(QW + KW) * Tp), h, d, hT, KW, d,
+              dw[4]));
   // 10. input RMSNorm backward + the residual: dx = dx1 + norm'(dh)
   {
     Scope sc(tm, "bwd_norm", s);

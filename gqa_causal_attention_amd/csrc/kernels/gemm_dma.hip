@@ -26,6 +26,21 @@
 // Each wave owns a (BM/WGM) x (BN/WGN) sub-tile of 32x32 accumulators fed by
 // v_mfma_f32_32x32x16_bf16; fragment registers are double-buffered across the
 // 16-deep k-steps of a slice.
+//
+// Transposed operands (TR bit 0: A, bit 1: B; 256-wide tiles, 16x16x32 MFMA):
+// the operand is stored K-major, X^T[k][x] (a weight [out, in] read as the
+// product's right operand along `out`, or activations [tokens, features] read
+// along the token axis), so the backward's products need no transposed copies.
+// Its slice is staged as BK rows of 256 consecutive x (512 bytes; a load
+// instruction moves two rows), XOR-swizzled on 16-byte chunks with a key of
+// the row, and the MFMA operand (8 consecutive k of one x per lane) comes from
+// two transposing reads ds_read_b64_tr_b16 (within a 16-lane group lane i
+// receives element i % 4 of the 8-byte pieces addressed by lanes 4e + i / 4,
+// e = 0..3, i.e. 4 consecutive k of one x).  Those reads are issued through
+// inline asm (the builtin makes the compiler wait for every outstanding global
+// load first, the next slice's direct-to-LDS loads included), and their
+// results are waited for explicitly with counts derived from the fixed issue
+// order below.
 #include "common.h"
 #include "launch.h"
 
@@ -76,6 +91,44 @@ __device__ __forceinline__ int seg_of(const GemmArgs& a, int64_t n) {
   return n < a.seg_end[0] ? 0 : (n < a.seg_end[1] ? 1 : 2);
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// 32-bit LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+// ds_read_b64_tr_b16 at LDS byte address addr + OFF.  The result is not
+// tracked by the compiler's wait-count insertion: wait (lgkm_wait) and tie()
+// it before use.
+template <int OFF>
+__device__ __forceinline__ s16x4 lds_read_tr16_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset is 16 bits");
+  s16x4 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
+  return v;
+}
+// Wait until at most N LDS / scalar-memory operations of this wave are
+// outstanding (LDS operations complete in issue order).
+template <int N>
+__device__ __forceinline__ void lgkm_wait() {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N));
+}
+// Makes v look redefined here, so its uses stay behind a preceding lgkm_wait.
+__device__ __forceinline__ void tie(bf16x8& v) { asm volatile("" : "+v"(v)); }
+
+// XOR key (in 16-byte chunks) of k-row r of a transposed slice: rows r and
+// r + 1..3, r + 8 land in different 32-byte slots of 256 bytes.
+__device__ __forceinline__ int tkey(int r) { return 2 * ((r & 3) + 4 * ((r >> 3) & 1)); }
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(IntC<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 
 // Global row pointer of B-tile row r (K offset k0) for tile column tn.  Gated
 // mode: each wave's WTN B rows are WTN/2 gate rows then the WTN/2 up rows of
@@ -120,7 +173,7 @@ template <> struct Mfma<16> {
 // SCHED 1: B fragments double-buffered (read one or two per A row), each A
 //          fragment re-read for the next k-step as soon as its row of MFMAs
 //          has issued (fewer live registers, reads spread over the step).
-template <int BM, int BN, int BK, int ST, int WGM, int WGN, int MF, int SCHED, int MODE, int EPI>
+template <int BM, int BN, int BK, int ST, int WGM, int WGN, int MF, int SCHED, int MODE, int EPI, int TR>
 __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) {
   typedef Mfma<MF> MM;
   typedef typename MM::acc_t acc_t;
@@ -131,7 +184,11 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
   constexpr int CPR = BK / 8;            // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;          // rows per load instruction
   constexpr int RP = 128 / BK;           // rows per 256 bytes of LDS
-  constexpr int IA = BM / RPI / NW, IB = BN / RPI / NW;  // load instructions per wave per slice
+  constexpr bool TA = (TR & 1) != 0, TB = (TR & 2) != 0;
+  constexpr int RBA = BM * 2, RBB = BN * 2;         // bytes per k-row of a transposed slice
+  constexpr int TPR = 1024 / RBA;                   // k-rows per load instruction (transposed)
+  // load instructions per wave per slice
+  constexpr int IA = TA ? BK / TPR / NW : BM / RPI / NW, IB = TB ? BK / TPR / NW : BN / RPI / NW;
   constexpr int NLD = IA + IB;
   constexpr int A_BYTES = BM * BK * 2, STAGE_BYTES = (BM + BN) * BK * 2;
   constexpr int KS = BK / MM::KD;        // MFMA k-steps per slice
@@ -144,6 +201,9 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
   static_assert(MODE != kModeGated || FN % 2 == 0, "gated wave tiles hold gate and up halves");
   static_assert(ST >= 2 && ST <= 6 && (ST - 1) * NLD < 64, "pipeline depth");
   static_assert(KS % 2 == 0 || SCHED == 1, "fragment slots alternate across slices");
+  static_assert(TR == 0 || (MF == 16 && SCHED == 1 && MODE == kModeSeg && BM == 256 && BN == 256 && BK == 64 &&
+                            (BK / TPR) % NW == 0),
+                "transposed operands: 256x256 tiles, 64-deep slices, 16x16x32 MFMA, A re-read schedule");
   __shared__ __attribute__((aligned(1024))) char smem[ST * STAGE_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -181,34 +241,75 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
   const int nk = (int)((min((int64_t)a.K, kbeg + a.k_split) - kbeg) / BK);
 
   // ---- this lane's global source of every load instruction it issues ----
+  // (transposed: lane l of instruction i fetches k-row i * TPR + l / 32, 16-byte
+  // chunk (l % 32) ^ tkey(row); columns past M or N clamp to the last whole
+  // chunk, whose products land in discarded outputs)
   const int lrow = lane / CPR, lslot = lane % CPR;
+  const int trw = lane / (64 / TPR), tsl = lane % (64 / TPR);
   const bf16* gA[IA];
   const bf16* gB[IB];
   {
     const bf16* A = static_cast<const bf16*>(a.A);
 #pragma unroll
     for (int j = 0; j < IA; ++j) {
-      const int r = (wave + NW * j) * RPI + lrow;
-      const int chunk = lslot ^ ((r / RP) % CPR);
-      const int m = min(m0 + r, a.M - 1);
-      gA[j] = A + (int64_t)m * a.lda + kbeg + chunk * 8;
+      if constexpr (TA) {
+        const int r = (wave + NW * j) * TPR + trw;
+        const int m = min(m0 + (tsl ^ tkey(r)) * 8, a.M - 8);
+        gA[j] = A + (kbeg + r) * a.lda + m;
+      } else {
+        const int r = (wave + NW * j) * RPI + lrow;
+        const int chunk = lslot ^ ((r / RP) % CPR);
+        const int m = min(m0 + r, a.M - 1);
+        gA[j] = A + (int64_t)m * a.lda + kbeg + chunk * 8;
+      }
     }
 #pragma unroll
     for (int j = 0; j < IB; ++j) {
-      const int r = (wave + NW * j) * RPI + lrow;
-      const int chunk = lslot ^ ((r / RP) % CPR);
-      gB[j] = b_row_ptr<MODE, BN, WTN>(a, tn, r, kbeg) + chunk * 8;
+      if constexpr (TB) {
+        gB[j] = nullptr;  // per slice, from the K segment (issue)
+      } else {
+        const int r = (wave + NW * j) * RPI + lrow;
+        const int chunk = lslot ^ ((r / RP) % CPR);
+        gB[j] = b_row_ptr<MODE, BN, WTN>(a, tn, r, kbeg) + chunk * 8;
+      }
     }
   }
-  auto issue = [&](int kt, int stage) {
+  // The segment table as the first entry plus increments: a choice between
+  // two captured values becomes a data-dependent offset into the lambda's
+  // captures, which keeps every captured variable in scratch memory; adding
+  // an increment or zero does not.
+  const uint64_t tb_u0 = (uint64_t)(uintptr_t)a.B[0];
+  const uint64_t tb_d1 = (uint64_t)(uintptr_t)a.B[1] - tb_u0, tb_d2 = (uint64_t)(uintptr_t)a.B[2] - (uint64_t)(uintptr_t)a.B[1];
+  const int64_t tb_e0 = a.seg_end[0], tb_g1 = a.seg_end[1] - a.seg_end[0], tb_g2 = a.seg_end[2] - a.seg_end[1];
+  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
     char* sA = smem + stage * STAGE_BYTES;
     char* sB = sA + A_BYTES;
+    const int64_t kk = kbeg + (int64_t)kt * BK;
 #pragma unroll
     for (int j = 0; j < IA; ++j)
-      load_lds16(gA[j] + (int64_t)kt * BK, sA + (wave + NW * j) * 1024);
+      load_lds16(gA[j] + (TA ? kk - kbeg : 0) * a.lda + (TA ? 0 : (int64_t)kt * BK), sA + (wave + NW * j) * 1024);
+    if constexpr (TB) {
+      // B^T rows come from up to three segments along K (slice-aligned
+      // boundaries); rows past the last one (K padding) repeat it
+      const int64_t e1 = tb_e0 + tb_g1, e2 = e1 + tb_g2;
+      const int64_t kq = min(kk, e2 - 1);
+      const bool past0 = kq >= tb_e0, past1 = kq >= e1;
+      const int64_t start = (past0 ? tb_e0 : 0) + (past1 ? tb_g1 : 0);
+      const int64_t avail = tb_e0 + (past0 ? tb_g1 : 0) + (past1 ? tb_g2 : 0) - kk;  // rows of the slice in the segment
+      const uint64_t base = tb_u0 + (past0 ? tb_d1 : 0) + (past1 ? tb_d2 : 0);
+      const bf16* Bs = reinterpret_cast<const bf16*>((uintptr_t)base) + (kk - start) * a.ldb;
+      const int last = (int)min(avail, (int64_t)BK) - 1;
 #pragma unroll
-    for (int j = 0; j < IB; ++j)
-      load_lds16(gB[j] + (int64_t)kt * BK, sB + (wave + NW * j) * 1024);
+      for (int j = 0; j < IB; ++j) {
+        const int r = (wave + NW * j) * TPR + trw;
+        const int col = min(tn * BN + (tsl ^ tkey(r)) * 8, a.N - 8);
+        load_lds16(Bs + (min(r, last) * (int)a.ldb + col), sB + (wave + NW * j) * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < IB; ++j)
+        load_lds16(gB[j] + (int64_t)kt * BK, sB + (wave + NW * j) * 1024);
+    }
   };
 
   // ---- fragment addressing: row lane % MF of an MF-row block, chunk CPF ks + lane / MF ----
@@ -220,6 +321,24 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
   int koff[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) koff[ks] = ((CPF * ks + fhi) ^ fsw) * 16;
+  // transposed fragments (16x16x32): lane l of group g = l / 16, j = l % 16
+  // addresses k-row 8 g + j / 4 (+ 4 for the second read) and the 8 bytes of
+  // columns xb + 4 (j % 4) .. + 3 of its 16-column block xb
+  const int tg = lane >> 4, tj = lane & 15;
+  const int tkl = 2 * ((tj >> 2) + 4 * (tg & 1));  // = tkey of every row this lane reads
+  const int trow = 8 * tg + (tj >> 2);
+  uint32_t ta_off[TA ? FM : 1], tb_off[TB ? FN : 1];
+#pragma unroll
+  for (int i = 0; i < (TA ? FM : 0); ++i) {
+    const int xb = wm * WTM + i * 16;
+    ta_off[i] = trow * RBA + ((((xb >> 3) ^ tkl) | ((tj & 3) >> 1)) * 16) + (tj & 1) * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < (TB ? FN : 0); ++j) {
+    const int xb = wn * WTN + j * 16;
+    tb_off[j] = A_BYTES + trow * RBB + ((((xb >> 3) ^ tkl) | ((tj & 3) >> 1)) * 16) + (tj & 1) * 8;
+  }
+  const uint32_t smem_lds = lds_addr(smem);
 
   acc_t acc[FM][FN];
 #pragma unroll
@@ -233,15 +352,58 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
   // read; the reads of the next k-step (possibly of the next slice) go to the
   // other slot (SCHED 0) or, for A under SCHED 1, to slot 0 after its row.
   bf16x8 fa[2][FM], fb[2][FN];
-  auto rd = [&](int stage, int ks, int slot, int r) {
-    const char* s = smem + stage * STAGE_BYTES + koff[ks];
-    if (r < FM) fa[slot][r] = *reinterpret_cast<const bf16x8*>(s + a_off + r * MF * (BK * 2));
-    else fb[slot][r - FM] = *reinterpret_cast<const bf16x8*>(s + b_off + (r - FM) * MF * (BK * 2));
+  auto rd_tr = [&](uint32_t ad, auto ks_c, int rb) __attribute__((always_inline)) {
+    constexpr int KSN = decltype(ks_c)::value;
+    s16x4 lo, hi;
+    if (rb == RBA) {
+      lo = lds_read_tr16_at<KSN * 32 * RBA>(ad);
+      hi = lds_read_tr16_at<KSN * 32 * RBA + 4 * RBA>(ad);
+    } else {
+      lo = lds_read_tr16_at<KSN * 32 * RBB>(ad);
+      hi = lds_read_tr16_at<KSN * 32 * RBB + 4 * RBB>(ad);
+    }
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  auto step = [&](int cur, int stage, int ks) {
+  auto rd = [&](int stage, auto ks_c, int slot, int r) __attribute__((always_inline)) {
+    constexpr int KSN = decltype(ks_c)::value;
+    const char* s = smem + stage * STAGE_BYTES + koff[KSN];
+    if (r < FM) {
+      if constexpr (TA) fa[slot][r] = rd_tr(smem_lds + stage * STAGE_BYTES + ta_off[r], ks_c, RBA);
+      else fa[slot][r] = *reinterpret_cast<const bf16x8*>(s + a_off + r * MF * (BK * 2));
+    } else {
+      if constexpr (TB) fb[slot][r - FM] = rd_tr(smem_lds + stage * STAGE_BYTES + tb_off[r - FM], ks_c, RBB);
+      else fb[slot][r - FM] = *reinterpret_cast<const bf16x8*>(s + b_off + (r - FM) * MF * (BK * 2));
+    }
+  };
+  // Waits for the asm reads (TR != 0), from the issue order of a step (A
+  // re-read schedule): row r issues its MFMAs, after the first one the next
+  // step's B fragment r (r < FN), and after the row the next step's A
+  // fragment r; a fragment read takes NA / NB instructions.  A fragment r is
+  // therefore followed by P - ops(r) instructions when row r of the next
+  // step starts, and the last B fragment by NA * (FM - FN + 1) when row 0
+  // starts.  (After the prologue and after each barrier nothing is pending.)
+  constexpr int NA = TA ? 2 : 1, NB = TB ? 2 : 1;
+  constexpr int P_OPS = FM * NA + (FN < FM ? FN : FM) * NB;
+  auto row_wait = [&](auto i_c) {
+    constexpr int I = decltype(i_c)::value;
+    constexpr int OPS_I = NA + (I < FN ? NB : 0);
+    constexpr int NW_A = TA ? P_OPS - OPS_I : 64;
+    constexpr int NW_B = (TB && I == 0) ? NA * (FM - FN + 1) : 64;
+    constexpr int NWT = NW_A < NW_B ? NW_A : NW_B;
+    if constexpr (NWT < 64) lgkm_wait<(NWT < 15 ? NWT : 15)>();
+  };
+  auto step = [&](int cur, int stage, auto ks) __attribute__((always_inline)) {
     if constexpr (SCHED == 1) {
+      static_for<0, FM>([&](auto i_c) {
+        constexpr int i = decltype(i_c)::value;
+        if constexpr (TR != 0) {
+          row_wait(i_c);
+          if constexpr (TA) tie(fa[0][i]);
+          if constexpr (TB && i == 0) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
+            for (int j = 0; j < FN; ++j) tie(fb[cur][j]);
+          }
+        }
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           acc[i][j] = MM::run(fa[0][i], fb[cur][j], acc[i][j]);
@@ -250,7 +412,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
         }
         rd(stage, ks, 0, i);
         __builtin_amdgcn_sched_barrier(0);
-      }
+      });
     } else {
 #pragma unroll
       for (int t = 0; t < FM * FN; ++t) {
@@ -272,22 +434,27 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
     wait_slices<NLD, ST - 1>(min(ST - 1, nk - 1));
     lds_sync();
 #pragma unroll
-    for (int r = 0; r < FM + FN; ++r) rd(0, 0, 0, r);
+    for (int r = 0; r < FM + FN; ++r) rd(0, IntC<0>{}, 0, r);
+    if constexpr (TR != 0) lgkm_wait<0>();
   }
   for (int kt = 0; kt < nk; ++kt) {
     const int stage = kt % ST;
-#pragma unroll
-    for (int ks = 0; ks + 1 < KS; ++ks) step(ks & 1, stage, ks + 1);
+    static_for<0, KS - 1>([&](auto ks_c) {
+      constexpr int ks = decltype(ks_c)::value;
+      step(ks & 1, stage, IntC<ks + 1>{});
+    });
     if (kt + 1 < nk) {
       // slice kt + 1 has landed once at most min(ST - 2, nk - 2 - kt) later slices are pending
       wait_slices<NLD, ST - 2>(min(ST - 2, nk - 2 - kt));
+      if constexpr (TR != 0) lgkm_wait<0>();
       lds_sync();  // publishes slice kt + 1; every wave is done reading stage `stage`
       if (kt + ST < nk) issue(kt + ST, stage);
     }
     // (after the last slice these reads fetch an unused stage: harmless, and it
     // keeps a single copy of the MFMA sequence in the loop)
-    step((KS - 1) & 1, (kt + 1) % ST, 0);
+    step((KS - 1) & 1, (kt + 1) % ST, IntC<0>{});
   }
+  if constexpr (TR != 0) lgkm_wait<0>();  // the last step's reads, before LDS is reused
 
   // The activation (gated and store epilogues) and the presence of gate/up
   // biases are resolved once here, so each epilogue loop below is compiled
@@ -451,18 +618,47 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
   }
 }
 
-template <int BM, int BN, int BK, int ST, int WGM, int WGN, int MF, int SCHED, int MODE, int EPI>
+template <int BM, int BN, int BK, int ST, int WGM, int WGN, int MF, int SCHED, int MODE, int EPI, int TR = 0>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   if (a.k_split % BK != 0) return hipErrorInvalidValue;
   const int cols = MODE == kModeGated ? BN / 2 : BN;
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + cols - 1) / cols);
-  hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, BK, ST, WGM, WGN, MF, SCHED, MODE, EPI>), dim3(tiles, a.splits),
+  hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, BK, ST, WGM, WGN, MF, SCHED, MODE, EPI, TR>), dim3(tiles, a.splits),
                      dim3(WGM * WGN * 64), 0, s, a);
   return hipGetLastError();
 }
 
+// Transposed operands: 256x256 tiles only.  Whole 16-byte chunks of the
+// stored K-major rows (M for a transposed A, N for a transposed B: multiples
+// of 8, at least 8), 16-byte aligned rows, B's K segments ending on slice
+// boundaries except the last.
+template <int EPI>
+hipError_t launch_trans(const GemmArgs& a, hipStream_t s) {
+  const bool ta = (a.trans & 1) != 0, tb = (a.trans & 2) != 0;
+  if (a.M < 1 || a.lda % 8 != 0 || (uintptr_t)a.A % 16 != 0) return hipErrorInvalidValue;
+  if (ta && (a.M < 8 || a.M % 8 != 0)) return hipErrorInvalidValue;
+  if (tb && (a.N < 8 || a.N % 8 != 0)) return hipErrorInvalidValue;
+  if (tb) {
+    if (a.ldb % 8 != 0 || a.ldb < a.N || a.seg_end[0] % 64 != 0 || a.seg_end[1] % 64 != 0 ||
+        a.seg_end[0] > a.seg_end[1] || a.seg_end[1] > a.seg_end[2] || a.seg_end[2] < 1)
+      return hipErrorInvalidValue;
+    for (int i = 0; i < 3; ++i)
+      if ((uintptr_t)a.B[i] % 16 != 0) return hipErrorInvalidValue;
+  }
+  if (ta && a.lda < a.M) return hipErrorInvalidValue;
+  if (a.trans == 2) return launch_cfg<256, 256, 64, 2, 2, 4, 16, 1, kModeSeg, EPI, 2>(a, s);
+  if (a.trans == 3) return launch_cfg<256, 256, 64, 2, 2, 4, 16, 1, kModeSeg, EPI, 3>(a, s);
+  return hipErrorInvalidValue;
+}
+
 template <int MODE, int EPI>
 hipError_t dispatch(const GemmArgs& a, int tile, hipStream_t s) {
+  if (a.trans != 0) {
+    if constexpr (MODE == kModeSeg && (EPI == kEpiResid || EPI == kEpiPartial))
+      return tile == kTileDma256x256 ? launch_trans<EPI>(a, s) : hipErrorInvalidValue;
+    else
+      return hipErrorInvalidValue;
+  }
   switch (tile) {
     case kTileDma256x256: return launch_cfg<256, 256, 64, 2, 2, 4, 16, 1, MODE, EPI>(a, s);
     case kTileDma256x256n: return launch_cfg<256, 256, 64, 2, 4, 2, 16, 0, MODE, EPI>(a, s);

@@ -43,6 +43,13 @@ struct GemmArgs {
   int bump_n, bump_by;
   int order;               // tile order of the pipelined kernel (0 = XCD-aware groups; others for tuning)
   int wg_waves;            // weight-streaming kernel: waves (16-row weight groups) per workgroup
+  // Transposed operands (pipelined kernel, 256x256 tiles, kModeSeg, residual or
+  // partial epilogue): bit 0: A is stored K-major, A^T[K, M] with row stride
+  // lda; bit 1: B is stored K-major, B^T[K, N] with row stride ldb, its rows
+  // taken from the segments B[s] along K (seg_end = cumulative K ends; rows
+  // past seg_end[2] repeat the last one and must meet zero A columns).
+  int trans;
+  int64_t ldb;
 };
 
 // Tile shapes of the bf16 MFMA GEMM.

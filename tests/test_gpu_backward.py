@@ -62,6 +62,13 @@ CASES = {
     "bf16_hd256_wave_form": ("bf16", dict(d_model=256, n_heads=2, n_kv_heads=1, head_dim=256, intermediate=256,
                                           window=24), 1, 90),
     "bf16_single_position": ("bf16", dict(d_model=256, n_heads=4, n_kv_heads=2, head_dim=64, intermediate=256), 3, 1),
+    # T = 768 (a multiple of 64, above 512): every product reads its operands in
+    # place (weights K-major for the input gradients, activations along the
+    # token axis for the weight gradients), the small grids split along K
+    "bf16_in_place_t768": ("bf16", dict(d_model=256, n_heads=4, n_kv_heads=2, head_dim=64, intermediate=512), 2, 384),
+    # the same with head_dim 128, a window and weight gradients of 64-row segments
+    "bf16_in_place_window": ("bf16", dict(d_model=512, n_heads=8, n_kv_heads=2, head_dim=128, intermediate=1024,
+                                          window=100), 1, 640),
 }
 
 
@@ -75,15 +82,17 @@ def test_backward_parity(torch_cuda, name):
     _check(cfg, W, x, dy, dtype, name)
 
 
-def test_backward_llama3_8b_widths_short_sequence(torch_cuda):
-    """The 8B block's widths (d 4096, 32/8 heads of 128, IT 14336) at L = 128."""
+@pytest.mark.parametrize("L", [128, 256])
+def test_backward_llama3_8b_widths_short_sequence(torch_cuda, L):
+    """The 8B block's widths (d 4096, 32/8 heads of 128, IT 14336) at L = 128
+    (transposed copies) and L = 256 (weight gradients read in place)."""
     from gqa_causal_attention_amd.workloads import LLAMA3_8B_BLOCK, draw_weights
     cfg = dict(LLAMA3_8B_BLOCK)
     W = draw_weights(cfg, np.random.default_rng(402))
     rng = np.random.default_rng(403)
-    x = rng.standard_normal((1, 128, 4096), dtype=np.float32)
-    dy = rng.standard_normal((1, 128, 4096), dtype=np.float32)
-    _check(cfg, W, x, dy, "bf16", "llama3_8b_L128")
+    x = rng.standard_normal((1, L, 4096), dtype=np.float32)
+    dy = rng.standard_normal((1, L, 4096), dtype=np.float32)
+    _check(cfg, W, x, dy, "bf16", f"llama3_8b_L{L}")
 
 
 def test_backward_deterministic_and_overwrites(torch_cuda):
