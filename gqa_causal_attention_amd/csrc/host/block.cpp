@@ -778,6 +778,7 @@ int trans_splits(int M, int N, int K) {
 struct BwdLayout {
   WsLayout fwd;  // the recomputed forward's workspace, at offset 0
   bool tr_dx, tr_dw;
+  bool fuse_swiglu;  // SwiGLU's backward in the epilogue of the da product (no da buffer)
   size_t y, gu, lse, dsum, wdT, wguT, woT, wqkvT, dy_op, dyT, da, act, actT, dgu, dguT, h2T, dh2, dx1, dx1_op, dx1T,
       wpart, cpart, ctxT, dctx, dq, dk, dv, dob, dqkv, dqkvT, hT, dh, part, total;
   int Tp;  // token count padded to 256: the depth of the weight-gradient GEMMs
@@ -796,6 +797,7 @@ BwdLayout bwd_layout_for(const gqa_block* blk, int B, int L) {
   w.Kq = (int)((QW + 2 * KW + 63) / 64 * 64);
   w.tr_dx = bwd_trans_dx(blk, (int)T);
   w.tr_dw = bwd_trans_dw(blk, (int)T);
+  w.fuse_swiglu = w.tr_dx && trans_splits((int)T, (int)IT, (int)d) == 1;
   const bool cx = !w.tr_dx, cw = !w.tr_dw;  // transposed copies needed
   const size_t Tp = w.Tp, Kq = w.Kq;
   w.y = take(T * d * 4);
@@ -809,7 +811,7 @@ BwdLayout bwd_layout_for(const gqa_block* blk, int B, int L) {
   w.wqkvT = cx ? take(d * Kq * es) : 0;
   w.dy_op = take(T * d * es);
   w.dyT = cw ? take(d * Tp * es) : 0;
-  w.da = take(T * IT * 4);
+  w.da = w.fuse_swiglu ? 0 : take(T * IT * 4);
   w.act = take(T * IT * es);
   w.actT = cw ? take(IT * Tp * es) : 0;
   w.dgu = take(T * 2 * IT * es);
@@ -1037,17 +1039,34 @@ int run_backward(gqa_block* blk, const float* x, const float* dy, float* dx, flo
   }
   void* dyT = at(lay.dyT);
   if (!lay.tr_dw) BWD(tr("bwd_transpose", dy, kF32, d, T, d, dyT, Tp, Tp));
-  float* da = atf(lay.da);
-  if (lay.tr_dx) {
-    const void* wd = blk->w[W_DOWN];
-    BWD(gemm_t("bwd_gemm_da", dy_op, d, false, wd, wd, wd, d, d, d, IT, T, IT, d, da, IT));
-  } else {
-    BWD(gemm("bwd_gemm_da", dy_op, d, wdT, T, IT, d, da, IT));
-  }
-  // 4. SwiGLU: a = silu(g) u (for dWd), dg | du
+  // 4. SwiGLU: a = silu(g) u (for dWd), dg | du -- in the da product's
+  // epilogue when it runs as one K split on the pipelined kernel
   void* act = at(lay.act);
   void* dgu = at(lay.dgu);
-  {
+  if (lay.fuse_swiglu) {
+    const void* wd = blk->w[W_DOWN];
+    GemmArgs a{};
+    a.A = dy_op; a.lda = d;
+    a.B[0] = a.B[1] = a.B[2] = wd;
+    a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = d;
+    a.ldb = IT;
+    a.trans = 2;
+    a.M = T; a.N = IT; a.K = d;
+    a.splits = 1; a.k_split = d;
+    a.resid = gu; a.ldr = 2 * (int64_t)IT;
+    a.C = act; a.ldc = IT;
+    a.C2 = dgu; a.ldc2 = 2 * (int64_t)IT;
+    a.order = gemm_tile_order();
+    Scope sc(tm, "bwd_gemm_da_swiglu", s);
+    HIP_TRY(launch_gemm_bf16(a, kModeSeg, kEpiSwigluBwd, kTileDma256x256, s));
+  } else {
+    float* da = atf(lay.da);
+    if (lay.tr_dx) {
+      const void* wd = blk->w[W_DOWN];
+      BWD(gemm_t("bwd_gemm_da", dy_op, d, false, wd, wd, wd, d, d, d, IT, T, IT, d, da, IT));
+    } else {
+      BWD(gemm("bwd_gemm_da", dy_op, d, wdT, T, IT, d, da, IT));
+    }
     Scope sc(tm, "bwd_swiglu", s);
     HIP_TRY(launch_swiglu_bwd(gu, da, T, IT, act, dgu, et, s));
   }

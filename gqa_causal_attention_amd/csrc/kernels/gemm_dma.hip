@@ -477,7 +477,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
   // epilogue with 16-byte loads and stores, whole rows per wave.  (The gated
   // gate/up epilogue stays direct: its tiles are many per CU, so their
   // stores overlap other tiles' main loops, and measured slower staged.) ----
-  if constexpr (MF == 16 && (EPI == kEpiResid || EPI == kEpiStore)) {
+  if constexpr (MF == 16 && (EPI == kEpiResid || EPI == kEpiStore || EPI == kEpiSwigluBwd)) {
     constexpr int COLS = MODE == kModeGated ? BN / 2 : BN;  // output columns of the tile
     constexpr int SW = COLS + 4;                            // staging row stride (floats): 4 rows per
                                                             // write land 16 banks apart
@@ -515,7 +515,26 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
         const int n = col0 + c;
         if (m >= a.M || n >= a.N) continue;
         const f32x4 v = *reinterpret_cast<const f32x4*>(stg + r * SW + c);
-        if constexpr (EPI == kEpiResid) {
+        if constexpr (EPI == kEpiSwigluBwd) {
+          // v = da; the recomputed gate / up pre-activations of the same columns
+          const float* gu = a.resid + (int64_t)m * a.ldr + n;
+          const f32x4 g4 = *reinterpret_cast<const f32x4*>(gu);
+          const f32x4 u4 = *reinterpret_cast<const f32x4*>(gu + a.N);
+          bf16x4 ov, og, ou;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float g = g4[e], u = u4[e];
+            const float sg = 1.0f / (1.0f + __expf(-g));
+            const float sl = g * sg;
+            ov[e] = from_f32<bf16>(sl * u);
+            og[e] = from_f32<bf16>(v[e] * u * sg * (1.0f + g * (1.0f - sg)));
+            ou[e] = from_f32<bf16>(v[e] * sl);
+          }
+          bf16* c2 = static_cast<bf16*>(a.C2) + (int64_t)m * a.ldc2 + n;
+          *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.C) + (int64_t)m * a.ldc + n) = ov;
+          *reinterpret_cast<bf16x4*>(c2) = og;
+          *reinterpret_cast<bf16x4*>(c2 + a.N) = ou;
+        } else if constexpr (EPI == kEpiResid) {
           f32x4 t = v;
           if (a.bias[0]) t += *reinterpret_cast<const f32x4*>(a.bias[0] + n);
           if (a.resid) t = *reinterpret_cast<const f32x4*>(a.resid + (int64_t)m * a.ldr + n) + t;
@@ -647,27 +666,35 @@ hipError_t launch_trans(const GemmArgs& a, hipStream_t s) {
   }
   if (ta && a.lda < a.M) return hipErrorInvalidValue;
   if (a.trans == 2) return launch_cfg<256, 256, 64, 2, 2, 4, 16, 1, kModeSeg, EPI, 2>(a, s);
-  if (a.trans == 3) return launch_cfg<256, 256, 64, 2, 2, 4, 16, 1, kModeSeg, EPI, 3>(a, s);
+  if constexpr (EPI != kEpiSwigluBwd)
+    if (a.trans == 3) return launch_cfg<256, 256, 64, 2, 2, 4, 16, 1, kModeSeg, EPI, 3>(a, s);
   return hipErrorInvalidValue;
 }
 
 template <int MODE, int EPI>
 hipError_t dispatch(const GemmArgs& a, int tile, hipStream_t s) {
-  if (a.trans != 0) {
-    if constexpr (MODE == kModeSeg && (EPI == kEpiResid || EPI == kEpiPartial))
-      return tile == kTileDma256x256 ? launch_trans<EPI>(a, s) : hipErrorInvalidValue;
-    else
+  if constexpr (EPI == kEpiSwigluBwd) {
+    if (MODE != kModeSeg || a.trans != 2 || tile != kTileDma256x256 || a.splits != 1 || a.N % 4 != 0 ||
+        a.ldr % 4 != 0 || !a.resid || !a.C || !a.C2)
       return hipErrorInvalidValue;
+    return launch_trans<EPI>(a, s);
+  } else {
+    if (a.trans != 0) {
+      if constexpr (MODE == kModeSeg && (EPI == kEpiResid || EPI == kEpiPartial))
+        return tile == kTileDma256x256 ? launch_trans<EPI>(a, s) : hipErrorInvalidValue;
+      else
+        return hipErrorInvalidValue;
+    }
+    switch (tile) {
+      case kTileDma256x256: return launch_cfg<256, 256, 64, 2, 2, 4, 16, 1, MODE, EPI>(a, s);
+      case kTileDma256x256n: return launch_cfg<256, 256, 64, 2, 4, 2, 16, 0, MODE, EPI>(a, s);
+      case kTileDma256x256m32: return launch_cfg<256, 256, 64, 2, 2, 4, 32, 0, MODE, EPI>(a, s);
+      case kTileDma256x192:
+        if constexpr (MODE == kModeGated) return hipErrorInvalidValue;
+        else return launch_cfg<256, 192, 64, 2, 4, 2, 16, 1, MODE, EPI>(a, s);
+    }
+    return hipErrorInvalidValue;
   }
-  switch (tile) {
-    case kTileDma256x256: return launch_cfg<256, 256, 64, 2, 2, 4, 16, 1, MODE, EPI>(a, s);
-    case kTileDma256x256n: return launch_cfg<256, 256, 64, 2, 4, 2, 16, 0, MODE, EPI>(a, s);
-    case kTileDma256x256m32: return launch_cfg<256, 256, 64, 2, 2, 4, 32, 0, MODE, EPI>(a, s);
-    case kTileDma256x192:
-      if constexpr (MODE == kModeGated) return hipErrorInvalidValue;
-      else return launch_cfg<256, 192, 64, 2, 4, 2, 16, 1, MODE, EPI>(a, s);
-  }
-  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -684,6 +711,7 @@ hipError_t launch_gemm_dma(const GemmArgs& a, int mode, int epi, int tile, hipSt
     case kEpiStore: return dispatch<kModeSeg, kEpiStore>(a, tile, s);
     case kEpiResid: return dispatch<kModeSeg, kEpiResid>(a, tile, s);
     case kEpiPartial: return dispatch<kModeSeg, kEpiPartial>(a, tile, s);
+    case kEpiSwigluBwd: return dispatch<kModeSeg, kEpiSwigluBwd>(a, tile, s);
   }
   return hipErrorInvalidValue;
 }

@@ -19,6 +19,11 @@ enum GemmEpi {
   kEpiResid = 1,    // C (float32) = resid + (acc + bias[0]); resid and bias may be null
   kEpiGated = 2,    // C = act(acc_gate + bias[0]) * (acc_up + bias[1]), in the activation type
   kEpiPartial = 3,  // float32 partial sums of one K split (split-K; raw B-row order)
+  // SwiGLU's backward on the product da (pipelined kernel, B transposed, one
+  // K split): with g = resid[m, n], u = resid[m, N + n] (float32, row stride
+  // ldr), C[m, n] = silu(g) u, C2[m, n] = da u silu'(g), C2[m, N + n] = da silu(g)
+  // (activation type; row strides ldc, ldc2)
+  kEpiSwigluBwd = 4,
 };
 // MLP activations (the values act_fn in common.h switches on).
 enum ActKind { kActNone = 0, kActSilu = 1, kActGeluTanh = 2, kActGelu = 3 };
@@ -50,6 +55,8 @@ struct GemmArgs {
   // past seg_end[2] repeat the last one and must meet zero A columns).
   int trans;
   int64_t ldb;
+  void* C2;                // kEpiSwigluBwd: second output, row stride ldc2
+  int64_t ldc2;
 };
 
 // Tile shapes of the bf16 MFMA GEMM.

@@ -66,8 +66,10 @@ CASES = {
     # place (weights K-major for the input gradients, activations along the
     # token axis for the weight gradients), the small grids split along K
     "bf16_in_place_t768": ("bf16", dict(d_model=256, n_heads=4, n_kv_heads=2, head_dim=64, intermediate=512), 2, 384),
-    # the same with head_dim 128, a window and weight gradients of 64-row segments
-    "bf16_in_place_window": ("bf16", dict(d_model=512, n_heads=8, n_kv_heads=2, head_dim=128, intermediate=1024,
+    # the same with head_dim 128 (q width 1024 != d), a window, and the dk / dv
+    # weight gradients split along K; both cases run SwiGLU's backward in the
+    # epilogue of the da product (a single K split)
+    "bf16_in_place_window": ("bf16", dict(d_model=256, n_heads=8, n_kv_heads=2, head_dim=128, intermediate=1024,
                                           window=100), 1, 640),
 }
 
