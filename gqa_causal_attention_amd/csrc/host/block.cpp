@@ -821,8 +821,9 @@ BwdLayout bwd_layout_for(const gqa_block* blk, int B, int L) {
   w.dx1 = take(T * d * 4);
   w.dx1_op = take(T * d * es);
   w.dx1T = cw ? take(d * Tp * es) : 0;
-  w.wpart = take(T * d * 4);
-  w.cpart = take((size_t)colsum_chunks((int)T) * d * 4);
+  const int wparts = rms_bwd_parts((int)T, (int)d);  // RMSNorm weight-gradient partial rows
+  w.wpart = take((size_t)wparts * d * 4);
+  w.cpart = take((size_t)colsum_chunks(wparts) * d * 4);
   w.ctxT = cw ? take(QW * Tp * es) : 0;
   w.dctx = take(T * QW * 4);
   w.dq = take(T * QW * 4);
@@ -1096,7 +1097,7 @@ int run_backward(gqa_block* blk, const float* x, const float* dy, float* dx, flo
     Scope sc(tm, "bwd_norm", s);
     HIP_TRY(launch_rms_bwd(dh2, x1, static_cast<const float*>(blk->w[W_POST_NORM]), dy, T, d, c.norm_eps, dx1,
                            bf ? dx1_op : nullptr, et, wpart, s));
-    HIP_TRY(launch_colsum(wpart, T, d, atf(lay.cpart), dw[1], s));
+    HIP_TRY(launch_colsum(wpart, rms_bwd_parts(T, d), d, atf(lay.cpart), dw[1], s));
   }
   // 7. o_proj: dctx = dx1 Wo, dWo = dx1^T ctx
   float* dctx = atf(lay.dctx);
@@ -1162,7 +1163,7 @@ int run_backward(gqa_block* blk, const float* x, const float* dy, float* dx, flo
     Scope sc(tm, "bwd_norm", s);
     HIP_TRY(launch_rms_bwd(dh, x, static_cast<const float*>(blk->w[W_IN_NORM]), dx1, T, d, c.norm_eps, dx, nullptr,
                            et, wpart, s));
-    HIP_TRY(launch_colsum(wpart, T, d, atf(lay.cpart), dw[0], s));
+    HIP_TRY(launch_colsum(wpart, rms_bwd_parts(T, d), d, atf(lay.cpart), dw[0], s));
   }
 #undef BWD
   return GQA_OK;

@@ -187,24 +187,37 @@ __global__ __launch_bounds__(256) void rms_bwd_kernel(const float* __restrict__ 
 
 // Register form (d % 4 == 0, d <= 1024 * MAXV): each row read once, 16-byte
 // accesses at clamped columns, out-of-row pieces zeroed by selects.
+// A workgroup takes kRmsBwdRows consecutive rows and sums the weight
+// gradient's summands dy * x^ of its rows per column in registers (rows in
+// order), writing one partial row per chunk: the column sums then read
+// rows / kRmsBwdRows partial rows instead of a [rows, d] array.
+constexpr int kRmsBwdRows = 4;
+
 template <typename T, int MAXV>
 __global__ __launch_bounds__(256) void rms_bwd_vec_kernel(const float* __restrict__ dy, const float* __restrict__ x,
                                                          const float* __restrict__ w,
-                                                         const float* __restrict__ resid, int d, float eps,
+                                                         const float* __restrict__ resid, int rows, int d, float eps,
                                                          float* __restrict__ dx, T* __restrict__ dx_op,
                                                          float* __restrict__ wpart) {
   __shared__ float red[4];
-  const int64_t off = (int64_t)blockIdx.x * d;
   const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
   int ci[MAXV];
   bool in[MAXV];
-  f32x4 xv[MAXV], gv[MAXV];
-  float ss = 0.f;
+  f32x4 wacc[MAXV];
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
     const int idx = (threadIdx.x + i * 256) * 4;
     in[i] = idx < d;
     ci[i] = in[i] ? idx : d - 4;
+    wacc[i] = zero;
+  }
+  const int row0 = blockIdx.x * kRmsBwdRows, row1 = min(rows, row0 + kRmsBwdRows);
+  for (int row = row0; row < row1; ++row) {
+  const int64_t off = (int64_t)row * d;
+  f32x4 xv[MAXV], gv[MAXV];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
     const f32x4 xx = *reinterpret_cast<const f32x4*>(x + off + ci[i]);
     const f32x4 yy = *reinterpret_cast<const f32x4*>(dy + off + ci[i]);
     const f32x4 ww = *reinterpret_cast<const f32x4*>(w + ci[i]);
@@ -225,21 +238,25 @@ __global__ __launch_bounds__(256) void rms_bwd_vec_kernel(const float* __restric
     if (!in[i]) continue;
     const f32x4 rs = *reinterpret_cast<const f32x4*>(resid + off + ci[i]);
     const f32x4 yy = *reinterpret_cast<const f32x4*>(dy + off + ci[i]);
-    f32x4 v, wp;
+    f32x4 v;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float xh = xv[i][e] * r;
       v[e] = rs[e] + r * (gv[i][e] - xh * m);
-      wp[e] = yy[e] * xh;
+      wacc[i][e] += yy[e] * xh;
     }
     *reinterpret_cast<f32x4*>(dx + off + ci[i]) = v;
-    *reinterpret_cast<f32x4*>(wpart + off + ci[i]) = wp;
     if (dx_op) {
       T* o = dx_op + off + ci[i];
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = from_f32<T>(v[e]);
     }
   }
+  }  // row
+  float* wp = wpart + (int64_t)blockIdx.x * d;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i)
+    if (in[i]) *reinterpret_cast<f32x4*>(wp + ci[i]) = wacc[i];
 }
 
 // Column sums of a [R, C] float32 matrix: chunk z of rows -> part[z, c], then
@@ -631,11 +648,14 @@ hipError_t launch_swiglu_bwd(const float* gu, const float* da, int64_t rows, int
   return hipGetLastError();
 }
 
+bool rms_bwd_vec_ok(int d) { return d % 4 == 0 && d <= 1024 * 16; }
+
 template <typename T>
 hipError_t rms_bwd_vec(const float* dy, const float* x, const float* w, const float* resid, int rows, int d, float eps,
                        float* dx, T* dx_op, float* wpart, hipStream_t s) {
+  const dim3 grid((unsigned)((rows + kRmsBwdRows - 1) / kRmsBwdRows));
 #define GQA_RMS_BWD(MV) \
-  hipLaunchKernelGGL((rms_bwd_vec_kernel<T, MV>), dim3(rows), dim3(256), 0, s, dy, x, w, resid, d, eps, dx, dx_op, wpart)
+  hipLaunchKernelGGL((rms_bwd_vec_kernel<T, MV>), grid, dim3(256), 0, s, dy, x, w, resid, rows, d, eps, dx, dx_op, wpart)
   if (d <= 1024 * 2) GQA_RMS_BWD(2);
   else if (d <= 1024 * 4) GQA_RMS_BWD(4);
   else if (d <= 1024 * 8) GQA_RMS_BWD(8);
@@ -647,7 +667,7 @@ hipError_t rms_bwd_vec(const float* dy, const float* x, const float* w, const fl
 hipError_t launch_rms_bwd(const float* dy, const float* x, const float* w, const float* resid, int rows, int d,
                           float eps, float* dx, void* dx_op, int elem, float* wpart, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (d % 4 == 0 && d <= 1024 * 16)
+  if (rms_bwd_vec_ok(d))
     return elem == kBF16 ? rms_bwd_vec<bf16>(dy, x, w, resid, rows, d, eps, dx, static_cast<bf16*>(dx_op), wpart, s)
                          : rms_bwd_vec<float>(dy, x, w, resid, rows, d, eps, dx, static_cast<float*>(dx_op), wpart, s);
   if (elem == kBF16)
@@ -658,6 +678,8 @@ hipError_t launch_rms_bwd(const float* dy, const float* x, const float* w, const
                        static_cast<float*>(dx_op), wpart);
   return hipGetLastError();
 }
+
+int rms_bwd_parts(int rows, int d) { return rms_bwd_vec_ok(d) ? (rows + kRmsBwdRows - 1) / kRmsBwdRows : rows; }
 
 constexpr int kColsumRows = 32;  // rows per chunk: enough chunks to fill the GPU at 4k tokens
 int colsum_chunks(int R) { return (R + kColsumRows - 1) / kColsumRows; }

@@ -197,9 +197,12 @@ hipError_t launch_convert(const float* in, void* out, int elem, int64_t n, hipSt
 hipError_t launch_swiglu_bwd(const float* gu, const float* da, int64_t rows, int IT, void* act, void* dgu, int elem,
                              hipStream_t s);
 // dx = resid + RMSNorm backward of dy at input x (gain w); dx_op: the same in elem (or null);
-// wpart = dy * x^ (the weight gradient's summands).
+// wpart [rms_bwd_parts(rows, d), d]: the weight gradient's summands dy * x^,
+// summed in row order over consecutive chunks of rows (their column sums are
+// the weight gradient).
 hipError_t launch_rms_bwd(const float* dy, const float* x, const float* w, const float* resid, int rows, int d,
                           float eps, float* dx, void* dx_op, int elem, float* wpart, hipStream_t s);
+int rms_bwd_parts(int rows, int d);
 int colsum_chunks(int R);  // rows of the `part` scratch of launch_colsum (times C floats)
 hipError_t launch_colsum(const float* a, int R, int C, float* part, float* out, hipStream_t s);
 // dq | dk | dv, RoPE undone on dq and dk, into the q/k/v GEMM's row layout [T, ld]
