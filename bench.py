@@ -139,7 +139,7 @@ def ingest_pmc(fetch_dir, write_dir):
             raise SystemExit(f"no {counter} records under {d}")
         return out
 
-    gu = re.compile(r"gemm_dma_kernel<256, 256, 64, 2, 2, 4, 16, 1, 1, 2>")
+    gu = re.compile(r"gemm_dma_kernel<256, 256, 64, 2, 2, 4, 16, 1, 1, 2, 0>")
     res = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rr = rows(d, counter)
