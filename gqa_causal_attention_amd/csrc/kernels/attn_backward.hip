@@ -68,7 +68,9 @@ __device__ __forceinline__ f32x16 rows_x_cols(const char* tile, const bf16x8 (&b
   return s;
 }
 
-template <int HD>
+// NOWAIT: the transposing reads go through inline asm (no compiler wait for
+// outstanding global loads), waited for explicitly before each 16-key step.
+template <int HD, bool NOWAIT = false>
 __device__ __forceinline__ void tr_acc(const char* tile, const f32x16& w, f32x16 (&acc)[BwdTile<HD>::RT],
                                        int lane) {
   using C = BwdTile<HD>;
@@ -82,14 +84,36 @@ __device__ __forceinline__ void tr_acc(const char* tile, const f32x16& w, f32x16
 #pragma unroll
     for (int e = 0; e < 8; ++e) pf[e] = from_f32<bf16>(w[k16 * 8 + e]);
     const int row = k16 * 16 + vrow;
+    if constexpr (NOWAIT) {
+      s16x4 lo[C::RT], hi[C::RT];
 #pragma unroll
-    for (int r = 0; r < C::RT; ++r) {
-      const int d = r * 32 + vdim;
-      const int off = ((d >> 3) ^ vk) * 16 + (d & 7) * 2;
-      const s16x4 lo = lds_read_tr16(tile + row * C::RB + off);
-      const s16x4 hi = lds_read_tr16(tile + (row + 8) * C::RB + off);
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[r], 0, 0, 0);
+      for (int r = 0; r < C::RT; ++r) {
+        const int d = r * 32 + vdim;
+        const int off = ((d >> 3) ^ vk) * 16 + (d & 7) * 2;
+        lo[r] = lds_read_tr16_nowait(tile + row * C::RB + off);
+        hi[r] = lds_read_tr16_nowait(tile + (row + 8) * C::RB + off);
+      }
+      lgkm_wait<0>();
+#pragma unroll
+      for (int r = 0; r < C::RT; ++r) {
+        tie(lo[r]);
+        tie(hi[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < C::RT; ++r) {
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[r], hi[r], 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[r], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < C::RT; ++r) {
+        const int d = r * 32 + vdim;
+        const int off = ((d >> 3) ^ vk) * 16 + (d & 7) * 2;
+        const s16x4 lo = lds_read_tr16(tile + row * C::RB + off);
+        const s16x4 hi = lds_read_tr16(tile + (row + 8) * C::RB + off);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[r], 0, 0, 0);
+      }
     }
   }
 }
@@ -215,7 +239,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdAttnArgs a, con
                                                              float* __restrict__ dkp, float* __restrict__ dvp) {
   using C = BwdTile<HD>;
   constexpr int NW = 4, KS = C::KS, RT = C::RT;
-  constexpr int STAGE = 4 * C::TILE;  // Q (row swizzle), dO (row), Q (column), dO (column)
+  // Q (row swizzle), dO (row), Q (column), dO (column), then the tile's 32
+  // log-sum-exp and 32 D values (float32)
+  constexpr int STAGE = 4 * C::TILE + 256;
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -268,6 +294,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdAttnArgs a, con
       load_lds16(qr + (sl ^ C::vkey(r)) * 8, sQ + 2 * C::TILE + i * 1024);
       load_lds16(dr + (sl ^ C::vkey(r)) * 8, sQ + 3 * C::TILE + i * 1024);
     }
+    // lanes 0-7 of wave 0: lse[qb .. qb + 31], lanes 8-15: D (16 bytes each;
+    // starts past the padded row clamp back, their entries only feed masked rows)
+    if (w == 0 && lane < 16) {
+      const float* src = (lane < 8 ? lse : dsm) + min(qb + 4 * (lane & 7), a.lse_ld - 4);
+      load_lds16(src, sQ + 4 * C::TILE);
+    }
   };
 
   f32x16 dk[RT], dv[RT];
@@ -288,13 +320,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdAttnArgs a, con
     const bool use = wave_valid && qb + 31 >= kw0 && !(W > 0 && qb > kw_hi + W - 1);
     if (use) {
       // this lane's rows are 4 runs of 4 consecutive queries: (e/4)*8 + (lane/32)*4 + e%4;
-      // their lse / D entries are 16-byte loads, clamped into the padded row (entries
+      // their lse / D entries are 16-byte reads of the tile's copies in LDS (entries
       // past L only feed masked rows)
-      auto q4 = [&](int e4) { return min(qb + e4 * 8 + (lane >> 5) * 4, a.lse_ld - 4); };
+      const float* sl = reinterpret_cast<const float*>(sQ + 4 * C::TILE);  // lse, then D at + 32
+      auto q4 = [&](int e4) { return e4 * 8 + (lane >> 5) * 4; };
       f32x16 p = rows_x_cols<HD>(sQ, kf, lane);                     // S [queries][keys] -> P
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse + q4(e4));
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + q4(e4));
 #pragma unroll
         for (int e = 4 * e4; e < 4 * e4 + 4; ++e) {
           const int q = qb + acc_row(e, lane);
@@ -302,16 +335,16 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_kernel(BwdAttnArgs a, con
           p[e] = ok ? exp2_fast(p[e] * s_log2 - l4[e % 4]) : 0.f;
         }
       }
-      tr_acc<HD>(sQ + 3 * C::TILE, p, dv, lane);                    // dV^T += dO^T P
+      tr_acc<HD, true>(sQ + 3 * C::TILE, p, dv, lane);              // dV^T += dO^T P
       f32x16 ds = rows_x_cols<HD>(sQ + C::TILE, vf, lane);          // dP -> dS
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dsm + q4(e4));
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + 32 + q4(e4));
 #pragma unroll
         for (int e = 4 * e4; e < 4 * e4 + 4; ++e)  // (p = 0 on masked rows; D's padding is unwritten)
           ds[e] = p[e] != 0.f ? p[e] * (ds[e] - d4[e % 4]) : 0.f;
       }
-      tr_acc<HD>(sQ + 2 * C::TILE, ds, dk, lane);                   // dK^T += Q^T dS
+      tr_acc<HD, true>(sQ + 2 * C::TILE, ds, dk, lane);             // dK^T += Q^T dS
     }
     if (t + 1 < ntiles) {
       __builtin_amdgcn_s_waitcnt(0x0f70);
