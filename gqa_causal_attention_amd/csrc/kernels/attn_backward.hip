@@ -206,7 +206,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bwd_dq_kernel(BwdAttnArgs a, 
         const float p = ok ? exp2_fast(s[e] * s_log2 - lse2) : 0.f;
         ds[e] = p * (dp[e] - dsum);
       }
-      tr_acc<HD>(sK + 2 * C::TILE, ds, acc, lane);                  // dQ^T += K^T dS^T
+      tr_acc<HD, true>(sK + 2 * C::TILE, ds, acc, lane);            // dQ^T += K^T dS^T
     }
     if (t + 1 < ntiles) {
       __builtin_amdgcn_s_waitcnt(0x0f70);
