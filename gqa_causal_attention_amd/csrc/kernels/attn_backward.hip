@@ -392,6 +392,50 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdAttnArgs a, bf16*
   if (lane == 0) a.dsum[(b * a.H + h) * a.lse_ld + t] = s;
 }
 
+// The same for head_dim 64 / 128: 16 lanes per (token, head), hd / 16
+// consecutive dims per lane (16-byte loads and stores), group-of-16 sum.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_bwd_prep_vec_kernel(BwdAttnArgs a, bf16* __restrict__ dob) {
+  constexpr int DPL = HD / 16;
+  const int sub = threadIdx.x & 15;
+  const int64_t n = (int64_t)a.B * a.L * a.H;
+  const int64_t pair = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+  const bool ok = pair < n;
+  const int64_t pc = ok ? pair : n - 1;  // every lane stays in the group sum
+  const int64_t tok = pc / a.H;
+  const int h = (int)(pc % a.H);
+  const int64_t off = tok * a.ldo + (int64_t)h * HD + sub * DPL;
+  const float* dr = a.dout + off;
+  const bf16* orow = static_cast<const bf16*>(a.o) + off;
+  float s = 0.f;
+  bf16 ob[DPL];
+#pragma unroll
+  for (int c = 0; c < DPL / 4; ++c) {
+    const f32x4 d4 = reinterpret_cast<const f32x4*>(dr)[c];
+    const bf16x4 o4 = reinterpret_cast<const bf16x4*>(orow)[c];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s += d4[e] * to_f32(o4[e]);
+      ob[4 * c + e] = from_f32<bf16>(d4[e]);
+    }
+  }
+  if (ok) {
+#pragma unroll
+    for (int c = 0; c < DPL / 4; ++c) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = ob[4 * c + e];
+      reinterpret_cast<bf16x4*>(dob + off)[c] = v;
+    }
+  }
+  s += __shfl_xor(s, 1, WAVE);
+  s += __shfl_xor(s, 2, WAVE);
+  s += __shfl_xor(s, 4, WAVE);
+  s += __shfl_xor(s, 8, WAVE);
+  const int64_t b = tok / a.L, t = tok % a.L;
+  if (ok && sub == 0) a.dsum[(b * a.H + h) * a.lse_ld + t] = s;
+}
+
 int dq_waves(int G) { return G * (G >= 5 ? 1 : 8 / G); }  // as the forward: G heads x 32-query waves
 
 template <int HD>
@@ -426,7 +470,16 @@ hipError_t launch_attention_bwd_mfma(const BwdAttnArgs& a, void* dob, hipStream_
   if (n == 0) return hipSuccess;
   if (!attention_bwd_mfma_supported(a.hd, a.H / a.KV) || a.kv_parts != a.H / a.KV || !a.lse)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_bwd_prep_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, s, a, static_cast<bf16*>(dob));
+  if (a.ldo % 8 == 0 && (uintptr_t)a.dout % 16 == 0 && (uintptr_t)a.o % 16 == 0 && (uintptr_t)dob % 16 == 0) {
+    const dim3 g((unsigned)((n + 15) / 16));
+    if (a.hd == 64)
+      hipLaunchKernelGGL(attn_bwd_prep_vec_kernel<64>, g, dim3(256), 0, s, a, static_cast<bf16*>(dob));
+    else
+      hipLaunchKernelGGL(attn_bwd_prep_vec_kernel<128>, g, dim3(256), 0, s, a, static_cast<bf16*>(dob));
+  } else {
+    hipLaunchKernelGGL(attn_bwd_prep_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, s, a,
+                       static_cast<bf16*>(dob));
+  }
   if (a.hd == 64) return launch_hd<64>(a, static_cast<bf16*>(dob), a.dk, a.dv, s);
   return launch_hd<128>(a, static_cast<bf16*>(dob), a.dk, a.dv, s);
 }

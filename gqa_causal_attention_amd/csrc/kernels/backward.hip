@@ -399,6 +399,22 @@ __global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ 
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) out[i] = from_f32<T>(in[i]);
 }
+// 8 elements per thread (n a multiple of 8, 16-byte aligned buffers): two
+// 16-byte loads, one 16-byte store.
+__global__ __launch_bounds__(256) void convert8_bf16_kernel(const float* __restrict__ in, bf16* __restrict__ out,
+                                                           int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const f32x4 a = reinterpret_cast<const f32x4*>(in)[2 * i];
+  const f32x4 b = reinterpret_cast<const f32x4*>(in)[2 * i + 1];
+  bf16x8 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    o[e] = from_f32<bf16>(a[e]);
+    o[4 + e] = from_f32<bf16>(b[e]);
+  }
+  reinterpret_cast<bf16x8*>(out)[i] = o;
+}
 
 // ---- attention backward ----
 constexpr int kMaxDpl = 16;  // head dims per lane (hd <= 256)
@@ -717,6 +733,12 @@ hipError_t launch_rope_bwd_pack(const BwdAttnArgs& a, void* dqkv, int64_t ld, in
 
 hipError_t launch_convert(const float* in, void* out, int elem, int64_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
+  if (elem == kBF16 && n % 8 == 0 && (uintptr_t)in % 16 == 0 && (uintptr_t)out % 16 == 0) {
+    const int64_t n8 = n / 8;
+    hipLaunchKernelGGL(convert8_bf16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, in,
+                       static_cast<bf16*>(out), n8);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((n + 255) / 256));
   if (elem == kBF16)
     hipLaunchKernelGGL(convert_kernel<bf16>, grid, dim3(256), 0, s, in, static_cast<bf16*>(out), n);
