@@ -267,6 +267,8 @@ __global__ __launch_bounds__(256) void colsum_part_kernel(const float* __restric
   if (c >= C) return;
   const int r0 = blockIdx.y * rows_per, r1 = min(R, r0 + rows_per);
   float s = 0.f;
+  // (unrolled so the loads are in flight together; the adds stay in row order)
+#pragma unroll 8
   for (int r = r0; r < r1; ++r) s += a[(int64_t)r * C + c];
   part[(int64_t)blockIdx.y * C + c] = s;
 }
@@ -275,6 +277,7 @@ __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restri
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= C) return;
   float s = 0.f;
+#pragma unroll 8
   for (int z = 0; z < nz; ++z) s += part[(int64_t)z * C + c];
   out[c] = s;
 }
