@@ -247,6 +247,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a) {
   const int64_t m = idx / N4, n = (idx % N4) * 4;
   const int64_t NB = MODE == kModeGated ? 2 * (int64_t)a.N : a.N;
   f32x4 s = {0.f, 0.f, 0.f, 0.f}, su = {0.f, 0.f, 0.f, 0.f};
+  // (unrolled so the splits' loads are in flight together; the adds stay in split order)
+#pragma unroll 8
   for (int z = 0; z < a.splits; ++z) {
     const float* p = a.partial + ((int64_t)z * a.M + m) * NB;
     s += *reinterpret_cast<const f32x4*>(p + n);
