@@ -64,7 +64,8 @@ CASES = {
     "bf16_single_position": ("bf16", dict(d_model=256, n_heads=4, n_kv_heads=2, head_dim=64, intermediate=256), 3, 1),
     # T = 768 (a multiple of 64, above 512): every product reads its operands in
     # place (weights K-major for the input gradients, activations along the
-    # token axis for the weight gradients), the small grids split along K
+    # token axis for the weight gradients), the small grids split along K; the
+    # dk / dv weight gradients have M = 128 rows (a ragged 256-row tile)
     "bf16_in_place_t768": ("bf16", dict(d_model=256, n_heads=4, n_kv_heads=2, head_dim=64, intermediate=512), 2, 384),
     # the same with head_dim 128 (q width 1024 != d), a window, and the dk / dv
     # weight gradients split along K; both cases run SwiGLU's backward in the
