@@ -24,7 +24,7 @@ EXPORTS = ("gqa_block_create", "gqa_block_destroy", "gqa_state_bytes", "gqa_bloc
            "gqa_state_set_lengths", "gqa_state_get_lengths", "gqa_state_free", "gqa_workspace_bytes",
            "gqa_block_forward", "gqa_block_forward_ragged", "gqa_backward_workspace_bytes", "gqa_block_backward",
            "gqa_block_step", "gqa_block_status",
-           "gqa_block_set_timing",
+           "gqa_block_describe_plan", "gqa_block_set_timing",
            "gqa_block_kernel_times", "gqa_last_error", "gqa_version")
 
 
@@ -84,6 +84,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gqa_block_backward": ([P, P, P, P, ctypes.POINTER(P), I32, I32, P, SZ, P], I32),
         "gqa_block_step": ([P, P, P, P, I32, P, SZ, P], I32),
         "gqa_block_status": ([P, P], I32),
+        "gqa_block_describe_plan": ([P, I32, I32, I32, ctypes.c_char_p, SZ, ctypes.POINTER(SZ)], I32),
         "gqa_block_set_timing": ([P, I32], I32),
         "gqa_block_kernel_times": ([P, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_int64), I32], I32),
@@ -148,6 +149,23 @@ def _stream_ptr(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _require(t, name: str, shape: tuple, device) -> None:
+    """Raise ValueError unless t is a contiguous float32 tensor of `shape` on
+    `device` (checked before any pointer reaches the library, so a mis-shaped
+    or host tensor never becomes an out-of-bounds device access)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the block is on {device}")
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
 _MATRICES = ("q_proj.weight", "k_proj.weight", "v_proj.weight", "o_proj.weight", "gate_proj.weight",
              "up_proj.weight", "down_proj.weight")
 
@@ -165,6 +183,8 @@ class Block:
         self.lib = load_library()
         self.cfg = dict(cfg)
         self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         self.ccfg = make_config(cfg)
         self.bf16 = self.ccfg.weight_dtype == GQA_BF16
         self.tensors = {}
@@ -185,6 +205,8 @@ class Block:
         _check(self.lib.gqa_block_create(ctypes.byref(self.ccfg), arr, len(recs), ctypes.byref(h)))
         self.handle = h
         self._ws = None
+        self._ws_captured = False
+        self._retired = []   # workspaces a captured graph may still use
 
     def close(self):
         if getattr(self, "handle", None):
@@ -203,11 +225,19 @@ class Block:
         return torch.bfloat16 if self.bf16 else torch.float32
 
     def workspace(self, B: int, L: int):
+        """The block's device workspace, grown on demand.  A buffer used while
+        a HIP graph is being captured stays alive with the block (a replay
+        keeps using it), so growing it later never frees memory a graph holds."""
         import torch
         n = ctypes.c_size_t()
         _check(self.lib.gqa_workspace_bytes(self.handle, B, L, ctypes.byref(n)))
         if self._ws is None or self._ws.numel() < n.value:
+            if self._ws is not None and self._ws_captured:
+                self._retired.append(self._ws)
             self._ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device=self.device)
+            self._ws_captured = False
+        if torch.cuda.is_current_stream_capturing():
+            self._ws_captured = True
         return self._ws, n.value
 
     def allocate_state(self, batch: int, max_tokens: int) -> "State":
@@ -217,13 +247,21 @@ class Block:
         """mojolearn TransformerBlock.forward; `lengths` (B ints in [1, L], no
         state) makes the batch ragged: padding positions output +0.0."""
         import torch
-        assert x.dtype == torch.float32 and x.is_contiguous() and x.dim() == 3
+        if not isinstance(x, torch.Tensor) or x.dim() != 3:
+            raise ValueError("x must be a [B, L, d_model] tensor")
         B, L, _ = x.shape
+        _require(x, "x", (B, L, self.cfg["d_model"]), self.device)
         y = torch.empty_like(x) if out is None else out
-        ws, nb = self.workspace(B, L)
+        _require(y, "out", tuple(x.shape), self.device)
+        if state is not None:
+            self._check_state(state)
         if lengths is not None:
             if state is not None:
                 raise ValueError("lengths is not allowed together with state")
+            if len(lengths) != B:
+                raise ValueError(f"lengths holds {len(lengths)} values, x has {B} rows")
+        ws, nb = self.workspace(B, L)
+        if lengths is not None:
             lens = (ctypes.c_int32 * B)(*[int(v) for v in lengths])
             _check(self.lib.gqa_block_forward_ragged(self.handle, ctypes.c_void_p(x.data_ptr()),
                                                      ctypes.c_void_p(y.data_ptr()), B, L, lens,
@@ -245,9 +283,15 @@ class Block:
         prefill -> {"x": [B, L, d], weight name: gradient in its shape}, all
         float32 torch tensors on the device (``grads`` may supply them)."""
         import torch
-        assert x.dtype == torch.float32 and x.is_contiguous() and x.dim() == 3
-        assert grad_output.shape == x.shape and grad_output.dtype == torch.float32 and grad_output.is_contiguous()
+        if not isinstance(x, torch.Tensor) or x.dim() != 3:
+            raise ValueError("x must be a [B, L, d_model] tensor")
         B, L, _ = x.shape
+        _require(x, "x", (B, L, self.cfg["d_model"]), self.device)
+        _require(grad_output, "grad_output", tuple(x.shape), self.device)
+        if grads is not None:
+            _require(grads.get("x"), "grads['x']", tuple(x.shape), self.device)
+            for name in self.BACKWARD_WEIGHTS:
+                _require(grads.get(name), f"grads[{name!r}]", tuple(self.tensors[name].shape), self.device)
         nb = ctypes.c_size_t()
         _check(self.lib.gqa_backward_workspace_bytes(self.handle, B, L, ctypes.byref(nb)))
         ws = torch.empty(max(nb.value, 1), dtype=torch.uint8, device=self.device)
@@ -264,17 +308,37 @@ class Block:
 
     def step(self, x, state: "State", out=None, stream=None):
         import torch
-        assert x.dtype == torch.float32 and x.is_contiguous()
+        d = self.cfg["d_model"]
+        if not isinstance(x, torch.Tensor) or x.dim() not in (2, 3) or (x.dim() == 3 and x.shape[1] != 1):
+            raise ValueError("x must be a [B, d_model] or [B, 1, d_model] tensor")
         B = x.shape[0]
-        y = torch.empty((B, 1, x.shape[-1]), dtype=torch.float32, device=x.device) if out is None else out
+        _require(x, "x", (B, d) if x.dim() == 2 else (B, 1, d), self.device)
+        if state is not None:
+            self._check_state(state)
+        y = torch.empty((B, 1, d), dtype=torch.float32, device=x.device) if out is None else out
+        if not isinstance(y, torch.Tensor) or y.numel() != B * d:
+            raise ValueError(f"out must hold B * d_model = {B * d} values")
+        _require(y, "out", tuple(y.shape), self.device)
         ws, nb = self.workspace(B, 1)
         _check(self.lib.gqa_block_step(self.handle, state.handle if state else None,
                                        ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()), B,
                                        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream_ptr(stream)))
         return y
 
+    def _check_state(self, state):
+        if not isinstance(state, State) or state.block is not self:
+            raise ValueError("state was not allocated by this block")
+
     def status(self, stream=None):
         _check(self.lib.gqa_block_status(self.handle, _stream_ptr(stream)))
+
+    def describe_plan(self, B: int, L: int, backward: bool = False) -> str:
+        """The library's launch plan for a forward (or backward) of B x L tokens."""
+        n = ctypes.c_size_t()
+        _check(self.lib.gqa_block_describe_plan(self.handle, int(backward), B, L, None, 0, ctypes.byref(n)))
+        buf = ctypes.create_string_buffer(n.value)
+        _check(self.lib.gqa_block_describe_plan(self.handle, int(backward), B, L, buf, n.value, None))
+        return buf.value.decode()
 
     def set_timing(self, enable: bool):
         _check(self.lib.gqa_block_set_timing(self.handle, int(enable)))

@@ -130,6 +130,7 @@ struct Scope {
 };
 
 struct GemmPlan { int tile; int splits; int waves = 0; };
+constexpr int kStatusWords = 4;
 
 }  // namespace
 
@@ -140,7 +141,10 @@ struct gqa_block {
   size_t es = 4;           // activation / weight element size
   float* cos_tab = nullptr;
   float* sin_tab = nullptr;
-  int* status = nullptr;   // device word: non-finite input seen
+  // device words: [0] a non-finite input was seen, [1] the count of non-finite
+  // cached keys/values found by the GQA_CHECK_FINITE scan
+  int* status = nullptr;
+  bool check_finite = false;
   std::atomic<int> busy{0};
   KernelTimer timer;
 };
@@ -564,6 +568,11 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
   const float* o_bias = static_cast<const float*>(blk->w[W_OB]);
   const float* down_bias = static_cast<const float*>(blk->w[W_DB]);
 
+  // 0. (GQA_CHECK_FINITE) non-finite values among the rows' cached keys/values
+  if (st && blk->check_finite) {
+    Scope sc(tm, "check_cache", s);
+    HIP_TRY(launch_cache_nonfinite(st->k, st->v, lengths, et, B, c.n_kv_heads, st->capacity, hd, blk->status + 1, s));
+  }
   // 1. input norm (flags non-finite x)
   {
     NormArgs na{};
@@ -679,7 +688,7 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
     }
     na.norm = sandwich ? spec(W_PRE_FF, W_PRE_FFB) : spec(W_POST_NORM, W_POST_NB);
     na.out = h2;
-    if (int r = norm(fuse_o || sandwich ? "resid_rmsnorm" : "rmsnorm", na)) return r;
+    if (int r = norm(fuse_o || sandwich ? "resid_rmsnorm" : "rmsnorm_post", na)) return r;
   }
   if (recompute_only) return GQA_OK;
   // 7. gate/up (+ biases) and act(gate) * up; ungated MLPs: act(up (+ bias))
@@ -773,6 +782,15 @@ int trans_splits(int M, int N, int K) {
   int sp = 1;
   while (sp < 8 && tiles * sp < 192 && K % (128 * sp) == 0 && K / (2 * sp) >= 256) sp *= 2;
   return sp;
+}
+
+// Plan of a backward product on K-contiguous operands: the forward's plan,
+// except that a grid of 256x256 tiles well short of the 256 CUs (the k/v
+// weight gradients: 64 tiles) takes 128x128 tiles instead.
+GemmPlan bwd_gemm_plan(int M, int N, int K) {
+  GemmPlan p = plan_gemm(M, N, K, false);
+  if (gemm_dma_tile(p.tile) && (long)((M + 255) / 256) * ((N + 255) / 256) < 192) p = GemmPlan{kTile128x128, 1, 0};
+  return p;
 }
 
 struct BwdLayout {
@@ -926,10 +944,7 @@ int run_backward(gqa_block* blk, const float* x, const float* dy, float* dx, flo
       HIP_TRY(launch_gemm_f32(a, kModeSeg, kEpiResid, s));
       return GQA_OK;
     }
-    GemmPlan p = plan_gemm(M, N, K, false);
-    // a grid of 256x256 tiles well short of the 256 CUs (the k/v weight
-    // gradients: 64 tiles) takes 128x128 tiles instead
-    if (gemm_dma_tile(p.tile) && (long)((M + 255) / 256) * ((N + 255) / 256) < 192) p = GemmPlan{kTile128x128, 1, 0};
+    const GemmPlan p = bwd_gemm_plan(M, N, K);
     a.wg_waves = p.waves;
     if (p.splits <= 1) {
       a.splits = 1;
@@ -1169,6 +1184,69 @@ int run_backward(gqa_block* blk, const float* x, const float* dy, float* dx, flo
   return GQA_OK;
 }
 
+// Text description of the launch plan (see gqa_block_describe_plan).
+std::string describe_plan(const gqa_block* blk, int kind, int B, int L) {
+  const auto& c = blk->cfg;
+  std::string out;
+  char line[160];
+  auto add = [&](const char* fmt, auto... v) {
+    snprintf(line, sizeof line, fmt, v...);
+    out += line;
+    out += '\n';
+  };
+  const int T = B * L, d = c.d_model, QW = blk->QW, KW = blk->KW, IT = c.intermediate;
+  const bool bf = is_bf16(blk);
+  add("dtype=%s", bf ? "bf16" : "f32");
+  if (kind == 0) {
+    const WsLayout lay = layout_for(blk, B, L);
+    auto g = [&](const char* name, const GemmPlan& p) {
+      if (bf) add("%s tile=%d splits=%d waves=%d", name, p.tile, p.splits, p.waves);
+      else add("%s f32", name);
+    };
+    g("gemm_qkv", lay.p_qkv);
+    g("gemm_o", lay.p_o);
+    g(mlp_gated(c.mlp) ? "gemm_gate_up" : "gemm_up", lay.p_gu);
+    g("gemm_down", lay.p_down);
+    add("attention=%s", bf && lay.decode_attn ? "decode_splitk"
+                        : bf && attention_prefill_bf16_supported(c.head_dim, blk->G) ? "prefill_mfma" : "generic");
+    add("workspace=%zu", lay.total);
+    return out;
+  }
+  const BwdLayout lay = bwd_layout_for(blk, B, L);
+  const bool mfma_attn = bf && !lay.fwd.decode_attn && attention_prefill_bf16_supported(c.head_dim, blk->G) &&
+                         attention_bwd_mfma_supported(c.head_dim, blk->G);
+  add("tr_dx=%d tr_dw=%d fuse_swiglu=%d mfma_attention=%d", lay.tr_dx, lay.tr_dw, lay.fuse_swiglu, mfma_attn);
+  if (!bf) return out;
+  const GemmPlan pgu = plan_gemm(T, IT, d, true);
+  add("bwd_gate_up tile=%d", pgu.tile);
+  const int Tp = lay.Tp, Kq = lay.Kq;
+  auto dx = [&](const char* name, int M, int N, int K) {
+    if (lay.tr_dx) add("%s transposed tile=%d splits=%d", name, (int)kTileDma256x256, trans_splits(M, N, K));
+    else {
+      const GemmPlan p = bwd_gemm_plan(M, N, K);
+      add("%s tile=%d splits=%d", name, p.tile, p.splits);
+    }
+  };
+  auto dw = [&](const char* name, int M, int N) {
+    if (lay.tr_dw) add("%s transposed tile=%d splits=%d", name, (int)kTileDma256x256, trans_splits(M, N, T));
+    else {
+      const GemmPlan p = bwd_gemm_plan(M, N, Tp);
+      add("%s tile=%d splits=%d", name, p.tile, p.splits);
+    }
+  };
+  if (lay.fuse_swiglu) add("da_swiglu transposed tile=%d splits=1", (int)kTileDma256x256);
+  else dx("da", T, IT, d);
+  dw("dWd", d, IT);
+  dx("dh2", T, d, 2 * IT);
+  dw("dWg_dWu", IT, d);
+  dx("dctx", T, QW, d);
+  dw("dWo", d, QW);
+  dx("dh", T, d, Kq);
+  dw("dWq", QW, d);
+  dw("dWk_dWv", KW, d);
+  return out;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1210,12 +1288,18 @@ int gqa_block_create(const gqa_block_config* cfg, const gqa_tensor* weights, int
     }
   hipError_t e;
   if ((e = hipMalloc(&blk->cos_tab, n * 4)) != hipSuccess || (e = hipMalloc(&blk->sin_tab, n * 4)) != hipSuccess ||
-      (e = hipMalloc(&blk->status, 4)) != hipSuccess)
+      (e = hipMalloc(&blk->status, kStatusWords * 4)) != hipSuccess)
     return cleanup(fail(GQA_ERR_HIP, "device allocation failed: %s", hipGetErrorString(e)));
   if ((e = hipMemcpy(blk->cos_tab, ct.data(), n * 4, hipMemcpyHostToDevice)) != hipSuccess ||
       (e = hipMemcpy(blk->sin_tab, sn.data(), n * 4, hipMemcpyHostToDevice)) != hipSuccess ||
-      (e = hipMemset(blk->status, 0, 4)) != hipSuccess)
+      (e = hipMemset(blk->status, 0, kStatusWords * 4)) != hipSuccess)
     return cleanup(fail(GQA_ERR_HIP, "device copy failed: %s", hipGetErrorString(e)));
+  {
+    // GQA_CHECK_FINITE=1: count non-finite cached keys/values at every call
+    // with a state (a debug option: it reads each row's used cache once more)
+    const char* cf = getenv("GQA_CHECK_FINITE");
+    blk->check_finite = cf && atoi(cf) != 0;
+  }
 
   // Non-finite weights are refused before any computation.
   const int64_t d = cfg->d_model, hd = cfg->head_dim, QW = blk->QW, KW = blk->KW, IT = cfg->intermediate;
@@ -1366,11 +1450,30 @@ int gqa_block_step(gqa_block* blk, gqa_state* st, const float* x, float* y, int3
 int gqa_block_status(gqa_block* blk, void* stream) {
   if (!blk) return fail(GQA_ERR_ARG, "block is NULL");
   HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
-  int flag = 0;
-  HIP_TRY(hipMemcpy(&flag, blk->status, 4, hipMemcpyDeviceToHost));
-  if (flag) {
-    HIP_TRY(hipMemset(blk->status, 0, 4));
-    return fail(GQA_ERR_NONFINITE, "a non-finite input value was seen");
+  int w[kStatusWords] = {};
+  HIP_TRY(hipMemcpy(w, blk->status, sizeof w, hipMemcpyDeviceToHost));
+  if (w[0] || w[1]) {
+    HIP_TRY(hipMemset(blk->status, 0, sizeof w));
+    if (w[0] && w[1])
+      return fail(GQA_ERR_NONFINITE, "a non-finite input value was seen; %d non-finite cached key/value values", w[1]);
+    if (w[0]) return fail(GQA_ERR_NONFINITE, "a non-finite input value was seen");
+    return fail(GQA_ERR_NONFINITE, "%d non-finite cached key/value values", w[1]);
+  }
+  return GQA_OK;
+}
+
+int gqa_block_describe_plan(const gqa_block* blk, int32_t kind, int32_t B, int32_t L, char* buf, size_t buf_bytes,
+                            size_t* needed) {
+  if (!blk) return fail(GQA_ERR_ARG, "block is NULL");
+  if (kind != 0 && kind != 1) return fail(GQA_ERR_ARG, "kind must be 0 (forward) or 1 (backward)");
+  if (B < 1 || L < 1) return fail(GQA_ERR_ARG, "B and L must be >= 1");
+  if ((int64_t)B * L > INT32_MAX / 2) return fail(GQA_ERR_ARG, "B * L is too large");
+  const std::string d = describe_plan(blk, kind, B, L);
+  if (needed) *needed = d.size() + 1;
+  if (buf && buf_bytes) {
+    const size_t n = std::min(buf_bytes - 1, d.size());
+    memcpy(buf, d.data(), n);
+    buf[n] = 0;
   }
   return GQA_OK;
 }

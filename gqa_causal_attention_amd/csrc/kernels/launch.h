@@ -217,6 +217,8 @@ hipError_t launch_attention_bwd_mfma(const BwdAttnArgs& a, void* dob, hipStream_
 
 hipError_t launch_count_nonfinite(const void* p, int elem, int64_t n, int* flag, hipStream_t s);
 hipError_t launch_bump_lengths(int* lengths, int n, int by, hipStream_t s);
+hipError_t launch_cache_nonfinite(const void* k, const void* v, const int* lengths, int elem, int B, int KV,
+                                  int cap, int hd, int* count, hipStream_t s);
 // y [B, L, d] float32: positions t >= lengths_host[b] of row b set to +0.0.
 hipError_t launch_zero_padding(float* y, const int32_t* lengths_host, int B, int L, int d, hipStream_t s);
 

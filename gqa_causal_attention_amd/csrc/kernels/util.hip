@@ -1,6 +1,8 @@
 // Small device utilities: a non-finite scan of a weight tensor (run once when
 // a block is created: the mojolearn page rejects non-finite weights before any
-// computation), a per-row length bump, and the zeroing of the padding positions
+// computation), the optional non-finite count over a state's cached keys and
+// values (the same page's check of cache values, a debug option here since it
+// reads the whole cache), a per-row length bump, and the zeroing of the padding positions
 // of a ragged prefill (mojolearn TransformerBlock.forward `lengths`: padding
 // positions output exactly +0.0).
 #include "common.h"
@@ -15,6 +17,28 @@ __global__ __launch_bounds__(256) void nonfinite_kernel(const T* __restrict__ p,
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
     bad |= !__builtin_isfinite(to_f32(p[i]));
   if (bad) *flag = 1;
+}
+
+// Non-finite values among the used slots of a state's cache: row b, kv head j
+// (blockIdx.y = b * KV + j) holds min(lengths[b], cap) used slots (slots 0 ..
+// lengths[b] - 1, or every slot of a full window ring) of hd values in k and
+// in v.  Each thread tests its elements of both and adds how many were inf or
+// NaN to *count (one atomic per thread that found any; a debug pass, plain
+// element loads).
+template <typename T>
+__global__ __launch_bounds__(256) void cache_nonfinite_kernel(const T* __restrict__ k, const T* __restrict__ v,
+                                                              const int* __restrict__ lengths, int KV, int cap,
+                                                              int hd, int* count) {
+  const int b = blockIdx.y / KV;
+  const int64_t slab = (int64_t)blockIdx.y * cap * hd;
+  const int used = min(max(lengths[b], 0), cap);
+  const int64_t n = (int64_t)used * hd;
+  int bad = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    bad += !__builtin_isfinite(to_f32(k[slab + i]));
+    bad += !__builtin_isfinite(to_f32(v[slab + i]));
+  }
+  if (bad) atomicAdd(count, bad);
 }
 
 __global__ void bump_kernel(int* lengths, int n, int by) {
@@ -67,6 +91,20 @@ hipError_t launch_count_nonfinite(const void* p, int elem, int64_t n, int* flag,
   else
     hipLaunchKernelGGL(nonfinite_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s,
                        static_cast<const float*>(p), n, flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_nonfinite(const void* k, const void* v, const int* lengths, int elem, int B, int KV,
+                                  int cap, int hd, int* count, hipStream_t s) {
+  if (B <= 0 || (int64_t)B * KV > 65535) return hipErrorInvalidValue;
+  const int64_t per = (int64_t)cap * hd;
+  const unsigned bx = (unsigned)std::min<int64_t>(std::max<int64_t>((per + 255) / 256, 1), 64);
+  if (elem == kBF16)
+    hipLaunchKernelGGL(cache_nonfinite_kernel<bf16>, dim3(bx, (unsigned)(B * KV)), dim3(256), 0, s,
+                       static_cast<const bf16*>(k), static_cast<const bf16*>(v), lengths, KV, cap, hd, count);
+  else
+    hipLaunchKernelGGL(cache_nonfinite_kernel<float>, dim3(bx, (unsigned)(B * KV)), dim3(256), 0, s,
+                       static_cast<const float*>(k), static_cast<const float*>(v), lengths, KV, cap, hd, count);
   return hipGetLastError();
 }
 

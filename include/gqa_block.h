@@ -2,9 +2,9 @@
  * gqa_block.h — C ABI of one Llama-shaped transformer decoder block on
  * AMD Instinct MI355X (gfx950).
  *
- * The operation is the block documented on the mojolearn
- * "mojolearn.transformer" API page (class TransformerBlock: "Computes Hugging
- * Face's LlamaDecoderLayer.forward"): input RMSNorm, q/k/v projections with
+ * The operation is the block documented on the mojolearn.transformer API page
+ * (class TransformerBlock, whose description states that it computes Hugging
+ * Face's LlamaDecoderLayer forward pass): input RMSNorm, q/k/v projections with
  * [out, in] weights keyed by Hugging Face names, RoPE, grouped-query causal
  * attention over a caller-owned KV cache (optionally a sliding window over a
  * ring of W slots), o_proj plus residual, post-attention RMSNorm, gated MLP
@@ -41,7 +41,7 @@ typedef enum {
   GQA_ERR_ARG = -1,          /* NULL pointer, bad enum, non-positive size */
   GQA_ERR_SHAPE = -2,        /* weight name missing/extra/misshapen, head geometry */
   GQA_ERR_DTYPE = -3,        /* tensor dtype differs from the block's */
-  GQA_ERR_NONFINITE = -4,    /* non-finite weight (create) or input (status) */
+  GQA_ERR_NONFINITE = -4,    /* non-finite weight (create), input or cache value (status) */
   GQA_ERR_CAPACITY = -5,     /* lengths[b] + L beyond the state's max_tokens */
   GQA_ERR_POSITION = -6,     /* a position at or beyond max_positions */
   GQA_ERR_STATE = -7,        /* state missing, from another block, or batch mismatch */
@@ -227,8 +227,30 @@ int gqa_block_step(gqa_block* blk, gqa_state* st, const float* x_dev, float* y_d
 
 /* Synchronise `stream` and report whether any x read since the last call was
  * non-finite (GQA_ERR_NONFINITE, flag cleared) — the input check the page
- * makes before computing, moved after it so the hot path never syncs. */
+ * makes before computing, moved after it so the hot path never syncs.
+ * Cache values (the page checks them too): with the environment variable
+ * GQA_CHECK_FINITE set to a non-zero integer when the block is created, every
+ * forward/step with a state first counts the non-finite values among each
+ * row's used slots of the cached keys and values (slots below the row's
+ * length, all W slots of a full window ring); a non-zero count is reported
+ * here as GQA_ERR_NONFINITE with the count in the message, and cleared.  Off
+ * by default: the scan reads the used cache once more, which would double a
+ * decode step's cache traffic. */
 int gqa_block_status(gqa_block* blk, void* hip_stream);
+
+/* Launch plan of a call, as text (introspection; no device work, nothing
+ * launched).  kind 0: a forward/step of B rows x L tokens -- per projection
+ * GEMM the kernel tile (a GemmTile value), K split and waves per workgroup,
+ * the attention form, the workspace size; kind 1: the backward of a
+ * zero-state prefill of B x L -- whether the gradient products read weights
+ * (tr_dx) and activations (tr_dw) in place, whether SwiGLU's backward runs in
+ * a product's epilogue, and each product's tile and K split.  One
+ * "name value ..." item per line.  Writes at most buf_bytes - 1 characters
+ * plus a terminating NUL into buf (which may be NULL with buf_bytes 0) and
+ * the full length + 1 into *needed (if not NULL).  Errors: ARG for a NULL
+ * block, another kind, or B or L below 1. */
+int gqa_block_describe_plan(const gqa_block* blk, int32_t kind, int32_t B, int32_t L, char* buf,
+                            size_t buf_bytes, size_t* needed);
 
 /* Per-kernel timing.  When enabled, each launch of a forward/step is
  * bracketed by HIP events on the caller's stream and its duration added to a

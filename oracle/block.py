@@ -5,9 +5,9 @@ executes this module: only the tests, the smoke check and the bench's CPU
 baseline leg do.  It shares no code with the HIP path (no kernels, tables,
 constants or helpers); the two meet only at the seeded inputs.
 
-What it computes is the block of the mojolearn ``TransformerBlock`` API page
-("Llama-style transformer decoder block"; the class description says it
-computes Hugging Face's LlamaDecoderLayer.forward): input RMSNorm, q/k/v
+What it computes is the decoder block of the mojolearn ``TransformerBlock`` API
+page (class description: a Llama-shaped block whose forward is Hugging Face's
+LlamaDecoderLayer forward pass): input RMSNorm, q/k/v
 projections with [out, in] weights, RoPE, grouped-query causal attention over
 a caller-owned KV cache (optionally a sliding window over a ring of W slots),
 o_proj plus residual, post-attention RMSNorm, gated MLP plus residual.  The

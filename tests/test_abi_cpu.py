@@ -187,3 +187,6 @@ def test_null_arguments():
     assert lib.gqa_workspace_bytes(None, 1, 1, ctypes.byref(n)) == -1
     assert lib.gqa_block_forward(None, None, None, None, 1, 1, None, 0, None) == -1
     assert lib.gqa_block_step(None, None, None, None, 1, None, 0, None) == -7
+    n = ctypes.c_size_t()
+    assert lib.gqa_block_describe_plan(None, 0, 1, 1, None, 0, ctypes.byref(n)) == -1
+    assert "NULL" in lib.gqa_last_error().decode()

@@ -130,3 +130,25 @@ def test_backward_errors(torch_cuda):
     with pytest.raises(GqaError) as e:
         blk.backward(x, torch.zeros_like(x))
     assert e.value.name == "POSITION"
+
+
+@pytest.mark.timeout(900)
+def test_backward_llama3_8b_same_plan_as_4k(torch_cuda):
+    """The 8B block's backward in the launch plan the bench times at B=1,
+    L=4096: B=2 rows of L=2048 make the same T=4096 tokens, so every gradient
+    product runs the same tiles, transposed-operand modes, K splits and fused
+    SwiGLU epilogue (asserted from the library's own plan), while the float64
+    oracle's attention stays at 2048 x 2048 per head."""
+    from gqa_causal_attention_amd import Block
+    from gqa_causal_attention_amd.workloads import LLAMA3_8B_BLOCK, draw_weights
+    cfg = dict(LLAMA3_8B_BLOCK)
+    W = draw_weights(cfg, np.random.default_rng(402))
+    blk = Block(cfg, W)
+    plan = blk.describe_plan(2, 2048, backward=True)
+    assert plan == blk.describe_plan(1, 4096, backward=True), plan
+    assert "tr_dx=1 tr_dw=1 fuse_swiglu=1 mfma_attention=1" in plan, plan
+    del blk
+    rng = np.random.default_rng(408)
+    x = rng.standard_normal((2, 2048, 4096), dtype=np.float32)
+    dy = rng.standard_normal((2, 2048, 4096), dtype=np.float32)
+    _check(cfg, W, x, dy, "bf16", "llama3_8b_B2_L2048 (the 4k plan)")
