@@ -23,7 +23,7 @@ STATUS = {0: "OK", -1: "ARG", -2: "SHAPE", -3: "DTYPE", -4: "NONFINITE", -5: "CA
 EXPORTS = ("gqa_block_create", "gqa_block_destroy", "gqa_state_bytes", "gqa_block_allocate_state",
            "gqa_state_set_lengths", "gqa_state_get_lengths", "gqa_state_free", "gqa_workspace_bytes",
            "gqa_block_forward", "gqa_block_forward_ragged", "gqa_backward_workspace_bytes", "gqa_block_backward",
-           "gqa_block_step", "gqa_block_status",
+           "gqa_block_step", "gqa_block_step_noalloc", "gqa_block_status",
            "gqa_block_describe_plan", "gqa_block_set_timing",
            "gqa_block_kernel_times", "gqa_last_error", "gqa_version")
 
@@ -83,6 +83,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "gqa_backward_workspace_bytes": ([P, I32, I32, ctypes.POINTER(SZ)], I32),
         "gqa_block_backward": ([P, P, P, P, ctypes.POINTER(P), I32, I32, P, SZ, P], I32),
         "gqa_block_step": ([P, P, P, P, I32, P, SZ, P], I32),
+        "gqa_block_step_noalloc": ([P, P, P, P, I32, P], I32),
         "gqa_block_status": ([P, P], I32),
         "gqa_block_describe_plan": ([P, I32, I32, I32, ctypes.c_char_p, SZ, ctypes.POINTER(SZ)], I32),
         "gqa_block_set_timing": ([P, I32], I32),
@@ -323,6 +324,25 @@ class Block:
         _check(self.lib.gqa_block_step(self.handle, state.handle if state else None,
                                        ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()), B,
                                        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream_ptr(stream)))
+        return y
+
+    def step_noalloc(self, x, state: "State", out=None, stream=None):
+        """step() through the entry point that allocates nothing: the library's
+        fixed per-GPU scratch replaces the workspace (``out`` must be given by a
+        caller that cannot allocate)."""
+        import torch
+        d = self.cfg["d_model"]
+        if not isinstance(x, torch.Tensor) or x.dim() not in (2, 3) or (x.dim() == 3 and x.shape[1] != 1):
+            raise ValueError("x must be a [B, d_model] or [B, 1, d_model] tensor")
+        B = x.shape[0]
+        _require(x, "x", (B, d) if x.dim() == 2 else (B, 1, d), self.device)
+        self._check_state(state)
+        y = torch.empty((B, 1, d), dtype=torch.float32, device=x.device) if out is None else out
+        if not isinstance(y, torch.Tensor) or y.numel() != B * d:
+            raise ValueError(f"out must hold B * d_model = {B * d} values")
+        _require(y, "out", tuple(y.shape), self.device)
+        _check(self.lib.gqa_block_step_noalloc(self.handle, state.handle, ctypes.c_void_p(x.data_ptr()),
+                                               ctypes.c_void_p(y.data_ptr()), B, _stream_ptr(stream)))
         return y
 
     def _check_state(self, state):

@@ -1249,6 +1249,19 @@ std::string describe_plan(const gqa_block* blk, int kind, int B, int L) {
 
 }  // namespace
 
+namespace gqa_host {
+// Sets the calling thread's last-error text (for the library's other entry
+// points compiled in other files) and returns `code`.
+int report(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  return fail(code, "%s", buf);
+}
+}  // namespace gqa_host
+
 extern "C" {
 
 const char* gqa_last_error(void) { return g_last_error.c_str(); }

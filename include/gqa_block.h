@@ -225,6 +225,22 @@ int gqa_block_backward(gqa_block* blk, const float* x_dev, const float* grad_out
 int gqa_block_step(gqa_block* blk, gqa_state* st, const float* x_dev, float* y_dev, int32_t B,
                    void* workspace_dev, size_t workspace_bytes, void* hip_stream);
 
+/* gqa_block_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same step, with its workspace taken from a fixed array of this library
+ * in device memory instead of a caller-supplied buffer.  The caller still
+ * passes the state, x_dev and y_dev as for gqa_block_step.  The array holds
+ * 64 MiB (67108864 bytes) on each GPU the call runs on, from the first call on
+ * that GPU until the process ends; a step whose workspace
+ * (gqa_workspace_bytes(blk, B, 1)) is larger returns GQA_ERR_WORKSPACE before
+ * any launch (the 8B-shaped block fits up to 64 rows).  No call allocates or
+ * frees memory.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (other streams, other threads, other blocks) race and
+ * must be serialised by the caller.  Errors: those of gqa_block_step, and
+ * WORKSPACE as above. */
+int gqa_block_step_noalloc(gqa_block* blk, gqa_state* st, const float* x_dev, float* y_dev, int32_t B,
+                           void* hip_stream);
+
 /* Synchronise `stream` and report whether any x read since the last call was
  * non-finite (GQA_ERR_NONFINITE, flag cleared) — the input check the page
  * makes before computing, moved after it so the hot path never syncs.
