@@ -148,11 +148,46 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_kernel(AttnArgs a, in
     for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qr + ks * 16);
   }
 
-  // ---- one K/V tile: C::NI load instructions each, spread over the waves ----
+  // ---- one K/V tile: C::NI load instructions each, spread over the waves.
+  // A tile wholly of this call's keys (the usual case) takes per-lane offsets
+  // fixed per pass plus one add; tiles reaching into the cache or past the
+  // last key take the general row lookup. ----
+  constexpr int MI = (C::NI + NW - 1) / NW;  // load instructions per wave per operand
+  constexpr int MK = MI <= 2 ? MI : 1;       // offsets kept in registers (else formed per load)
+  auto k_off = [&](int i) {
+    const int r = i * C::RPI + lane / C::CR;
+    return r * HD + ((lane % C::CR) ^ C::kkey(r)) * 8;
+  };
+  auto v_off = [&](int i) {
+    const int r = i * C::RPI + lane / C::CR;
+    return r * HD + ((lane % C::CR) ^ C::vkey(r)) * 8;
+  };
+  int koffs[MK], voffs[MK];
+#pragma unroll
+  for (int m = 0; m < MK; ++m) {
+    koffs[m] = k_off(w + NW * m);
+    voffs[m] = v_off(w + NW * m);
+  }
+  // row kp of this call's keys / values is at fresh + kp * HD (kp >= start)
+  const int64_t fresh_row0 = ((int64_t)b * a.KV + j) * a.L - start;
+  const bf16* kfresh = static_cast<const bf16*>(a.knew) + fresh_row0 * HD;
+  const bf16* vfresh = static_cast<const bf16*>(a.vnew) + fresh_row0 * HD;
   auto issue = [&](int t, int stage) {
     const int kb = klo + t * BKV;
     char* sK = smem + stage * C::STAGE;
     char* sV = sK + C::TILE;
+    if (kb >= start && kb + BKV <= kend) {
+#pragma unroll
+      for (int m = 0; m < MI; ++m) {
+        const int i = w + NW * m;
+        if (MI * NW == C::NI || i < C::NI) {
+          const int ko = MI <= 2 ? koffs[m % MK] : k_off(i), vo = MI <= 2 ? voffs[m % MK] : v_off(i);
+          load_lds16(kfresh + (int64_t)kb * HD + ko, sK + i * 1024);
+          load_lds16(vfresh + (int64_t)kb * HD + vo, sV + i * 1024);
+        }
+      }
+      return;
+    }
     for (int i = w; i < C::NI; i += NW) {
       const int r = i * C::RPI + lane / C::CR, sl = lane % C::CR;
       const int kp = min(kb + r, kend - 1);
@@ -241,12 +276,199 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_kernel(AttnArgs a, in
     }
   };
 
-  // ---- pipeline: tile t + 1 is in flight while tile t is multiplied ----
+  // ---- interior tiles (every key visible to every query of the wave):
+  // the two sub-tiles' matrix products overlap the other sub-tile's softmax.
+  // QK(1) is issued step by step with P(0) = exp2 of sub-tile 0's scores
+  // spread between its MFMAs; PV(0) likewise carries P(1).  The MFMAs run in
+  // the matrix pipe while the same wave issues the independent VALU work.
+  // Maxima are taken on the raw scores (the scale, and tanh of the softcap,
+  // are increasing), and the scale folds into the exponent's fma. ----
+  constexpr int EPS = 16 / KS;  // elements of the previous sub-tile per QK step
+  const float s_k2 = 2.0f * kLog2e * inv_cap;       // softcap: tanh argument, times 2 log2e
+  // scaled score of a raw maximum (log2 units)
+  auto scaled = [&](float mx) {
+    return CAP ? cap_log2 * (1.0f - 2.0f * __builtin_amdgcn_rcpf(exp2_fast(mx * s_k2) + 1.0f)) : mx * s_log2;
+  };
+  // exp2(scaled(s) - m) with nm = -m
+  auto prob = [&](float sv, float nm) {
+    if constexpr (CAP) {
+      const float r = __builtin_amdgcn_rcpf(exp2_fast(sv * s_k2) + 1.0f);
+      return exp2_fast(__builtin_fmaf(r, -2.0f * cap_log2, cap_log2 + nm));
+    } else {
+      return exp2_fast(__builtin_fmaf(sv, s_log2, nm));
+    }
+  };
+  auto max16 = [&](const f32x16& v) {
+    float m0 = fmaxf(fmaxf(v[0], v[1]), v[2]), m1 = fmaxf(fmaxf(v[3], v[4]), v[5]);
+    float m2 = fmaxf(fmaxf(v[6], v[7]), v[8]), m3 = fmaxf(fmaxf(v[9], v[10]), v[11]);
+    float m4 = fmaxf(fmaxf(v[12], v[13]), v[14]);
+    return fmaxf(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)), fmaxf(m4, v[15]));
+  };
+  // raise the reference when a column's max outgrew it by the slack; returns
+  // the factor the accumulated output was multiplied by (1 if unchanged)
+  auto raise_ref = [&](float mxs) {
+    float alpha = 1.f;
+    if (__builtin_amdgcn_ballot_w64(mxs > m_ref + kRescaleSlack)) {
+      const float m_new = fmaxf(m_ref, fmaxf(mxs, xor32(mxs)));
+      alpha = m_ref == -INFINITY ? 1.f : exp2_fast(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[r][e] *= alpha;
+    }
+    return alpha;
+  };
+  // V^T fragment pair of 16-key step k16 of sub-tile sb, output rows r*32..: two
+  // transposing reads of 4 keys each
+  auto vfrag = [&](const char* sV, int sb, int k16, int r) {
+    const int row = sb * 32 + k16 * 16 + vrow;
+    const int d = r * 32 + vdim;
+    const int off = ((d >> 3) ^ vkey) * 16 + (d & 7) * 2;
+    const s16x4 lo = lds_read_tr16(sV + row * RB + off);
+    const s16x4 hi = lds_read_tr16(sV + (row + 8) * RB + off);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // One interior tile.  Fragment reads run two MFMA steps ahead: K fragments
+  // (2 KS steps of QK(0) and QK(1)) through a two-slot ring of ordinary LDS
+  // reads; V^T fragment pairs (4 RT steps of PV(0) and PV(1)) through a
+  // three-slot ring of transposing reads issued as inline asm with explicit
+  // lgkmcnt waits -- the builtin form would make the compiler wait for every
+  // global load in flight first (vmcnt 0), i.e. for the next tile's
+  // direct-to-LDS loads in the middle of this tile.  A V^T slot is refilled
+  // one step after the MFMA that read it.  Each step is pinned as "MFMA, its
+  // reads, its VALU share".
+  auto tile_fast = [&](const char* sK, const char* sV) __attribute__((always_inline)) {
+    const char* kb0 = sK + kfrag;
+    auto kread = [&](int i) {  // K fragment i of 2 KS: sub-tile i / KS, step i % KS
+      const char* base = kb0 + (i / KS) * 32 * RB;
+      return *reinterpret_cast<const bf16x8*>(base + (((2 * (i % KS) + khi) ^ kkey) * 16));
+    };
+    s16x4 vlo[3], vhi[3];
+    auto vissue = [&](int v) {  // V^T fragment v of 4 RT: sub-tile v / (2 RT), k16, r
+      const int sb = v / (2 * RT), j = v % (2 * RT), k16 = j / RT, r = j % RT;
+      const int row = sb * 32 + k16 * 16 + vrow;
+      const int d = r * 32 + vdim;
+      const char* p = sV + row * RB + ((d >> 3) ^ vkey) * 16 + (d & 7) * 2;
+      vlo[v % 3] = lds_read_tr16_nowait(p);
+      vhi[v % 3] = lds_read_tr16_nowait(p + 8 * RB);
+    };
+    constexpr int NK = 2 * KS, NV = 4 * RT;
+    // V^T fragment v for its MFMA: every LDS operation issued after its two
+    // reads is the next fragment's pair (issued one step earlier), if any
+    auto vtake = [&](int v) {
+      if (v + 1 < NV) lgkm_wait<2>();
+      else lgkm_wait<0>();
+      tie(vlo[v % 3]);
+      tie(vhi[v % 3]);
+      const bf16x8 f = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[v % 3], vhi[v % 3], 0, 1, 2, 3, 4, 5, 6, 7));
+      if (v + 2 < NV) vissue(v + 2);
+      return f;
+    };
+    bf16x8 kring[2];
+    kring[0] = kread(0);
+    kring[1] = kread(1);
+    auto ktake = [&](int i) {  // K fragment i; refills its slot with i + 2 (past the K steps: V^T 0, 1)
+      const bf16x8 f = kring[i & 1];
+      if (i + 2 < NK) kring[i & 1] = kread(i + 2);
+      else vissue(i + 2 - NK);
+      return f;
+    };
+    // stage 1: S0 = K0 Q^T
+    f32x16 s0, s1;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s0[e] = s1[e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktake(ks), qf[ks], s0, 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the first MFMA of QK(1) goes ahead of sub-tile 0's statistics
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktake(KS), qf[0], s1, 0, 0, 0);
+    raise_ref(scaled(max16(s0)));
+    float nm = -m_ref;
+    // stage 2: the rest of S1 = K1 Q^T, with P0 = exp2(scaled(S0) - m) between its MFMAs
+    float ls = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks > 0) s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktake(KS + ks), qf[ks], s1, 0, 0, 0);
+#pragma unroll
+      for (int e = ks * EPS; e < (ks + 1) * EPS; ++e) {
+        s0[e] = prob(s0[e], nm);  // in place: sub-tile 0's probabilities
+        ls += s0[e];
+      }
+      if (ks > 0) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x002, 4 * EPS, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += ls;
+    bf16x8 p0[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p0[h2][e] = from_f32<bf16>(s0[h2 * 8 + e]);
+    // sub-tile 1's maximum; a raised reference also scales P0 (not yet added)
+    const float alpha = raise_ref(scaled(max16(s1)));
+    if (alpha != 1.f) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p0[h2][e] = from_f32<bf16>(static_cast<float>(p0[h2][e]) * alpha);
+    }
+    nm = -m_ref;
+    // stage 3: O += V0 P0, with P1 between its MFMAs
+    ls = 0.f;
+    constexpr int PER = 16 / (2 * RT);
+#pragma unroll
+    for (int j = 0; j < 2 * RT; ++j) {
+      o[j % RT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vtake(j), p0[j / RT], o[j % RT], 0, 0, 0);
+#pragma unroll
+      for (int e = j * PER; e < (j + 1) * PER; ++e) {
+        s1[e] = prob(s1[e], nm);
+        ls += s1[e];
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4 * PER, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += ls;
+    // stage 4: O += V1 P1
+    bf16x8 p1[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p1[h2][e] = from_f32<bf16>(s1[h2 * 8 + e]);
+#pragma unroll
+    for (int j = 0; j < 2 * RT; ++j) {
+      o[j % RT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vtake(2 * RT + j), p1[j / RT], o[j % RT], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- pipeline: tile t + 1 is in flight while tile t is multiplied.  Each
+  // wave walks its tiles in three runs -- tiles at the window's lower edge
+  // (masked), interior tiles (every key visible to every query of the wave:
+  // tile_fast), tiles crossing the diagonal (masked) -- with one barrier per
+  // tile in every run, so all waves stay in step.  (Separate loops keep the
+  // two paths' registers apart.) ----
   if (ntiles > 0) issue(0, 0);
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of tile 0 (and Q) are done
   lds_sync();
   if (ntiles > 1) issue(1, 1);
-  for (int t = 0; t < ntiles; ++t) {
+  auto next_tile = [&](int t) {
+    if (t + 1 < ntiles) {
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of tile t + 1 are done
+      lds_sync();                          // ... everyone's; and stage t & 1 is free
+      if (t + 2 < ntiles) issue(t + 2, t & 1);
+    }
+  };
+  auto tile_masked = [&](int t) {
     const int stage = t & 1;
     const char* sK = smem + stage * C::STAGE;
     const char* sV = sK + C::TILE;
@@ -269,11 +491,29 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_kernel(AttnArgs a, in
       softmax(s1, kb + 32);
       pv(sV, s1, 1);
     }
-    if (t + 1 < ntiles) {
-      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of tile t + 1 are done
-      lds_sync();                          // ... everyone's; and stage t & 1 is free
-      if (t + 2 < ntiles) issue(t + 2, stage);
-    }
+  };
+  // interior run [t_lo, t_hi): tile t's keys klo + 64 t .. + 63 are all at or
+  // below the wave's first query and (windowed) inside its last query's window
+  int t_lo = 0, t_hi = 0;
+  if (wave_valid) {
+    if (W > 0) t_lo = max(0, (qp_hi - W + 1 - klo + BKV - 1) / BKV);
+    t_hi = qp_lo - (BKV - 1) - klo >= 0 ? (qp_lo - (BKV - 1) - klo) / BKV + 1 : 0;
+    t_lo = min(t_lo, ntiles);
+    t_hi = min(max(t_hi, t_lo), ntiles);
+  }
+  int t = 0;
+  for (; t < t_lo; ++t) {
+    tile_masked(t);
+    next_tile(t);
+  }
+  for (; t < t_hi; ++t) {
+    const char* sK = smem + (t & 1) * C::STAGE;
+    tile_fast(sK, sK + C::TILE);
+    next_tile(t);
+  }
+  for (; t < ntiles; ++t) {
+    tile_masked(t);
+    next_tile(t);
   }
 
   // ---- normalise and write ctx[token, h*HD + d] (and, when asked, the row's
