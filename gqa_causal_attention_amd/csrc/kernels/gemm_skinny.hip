@@ -118,6 +118,12 @@ __global__ __launch_bounds__(NWV * 64, 1) void gemm_skinny_kernel(GemmArgs a) {
   // repeats the last piece and is not stored) and stores piece kp of row m at
   // fragment (kp / 4) * MT + m / 16, lane m % 16 + 16 (kp % 4) ----
   const bf16* xbase = static_cast<const bf16*>(a.A) + kb;
+  // Slot of operand lane l in a fragment of k-step group g (fragment index / MT):
+  // lane l ^ (2 (l / 16) + g % 2).  Eight consecutive writer lanes hold the
+  // eight 16-byte pieces kp of one row -- lanes 16 (kp % 4) + row of two
+  // fragment groups -- and land in eight distinct 16-byte bank groups; eight
+  // consecutive reader lanes (l / 16 fixed) stay eight distinct slots.
+  auto xslot = [](int l, int g) { return l ^ ((((l >> 4) & 3) << 1) | (g & 1)); };
   bf16x8 xr[XT];
   auto load_x = [&](int sc) {
 #pragma unroll
@@ -134,7 +140,7 @@ __global__ __launch_bounds__(NWV * 64, 1) void gemm_skinny_kernel(GemmArgs a) {
       const int p = threadIdx.x + NT * i;
       if (XP % NT == 0 || p < XP) {
         const int m = p / 32, kp = p % 32;
-        xs[buf][(kp / 4) * MT + m / 16][(m % 16) + 16 * (kp % 4)] = xr[i];
+        xs[buf][(kp / 4) * MT + m / 16][xslot((m % 16) + 16 * (kp % 4), kp / 4)] = xr[i];
       }
     }
   };
@@ -156,7 +162,7 @@ __global__ __launch_bounds__(NWV * 64, 1) void gemm_skinny_kernel(GemmArgs a) {
       const bf16x8 wf = slab[lr * 16 + ((4 * ks + lg) ^ lr)];
       bf16x8 xf[MT];
 #pragma unroll
-      for (int t = 0; t < MT; ++t) xf[t] = xs[buf][(cl * SK_KS + ks) * MT + t][lane];
+      for (int t = 0; t < MT; ++t) xf[t] = xs[buf][(cl * SK_KS + ks) * MT + t][xslot(lane, cl * SK_KS + ks)];
 #pragma unroll
       for (int t = 0; t < MT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[t], acc[t], 0, 0, 0);
     }
