@@ -562,6 +562,57 @@ def leg_decode(args, torch, leg, flusher, variant="plain", steps=None, keep_fill
     return res
 
 
+def leg_ragged(args, torch, steps=None):
+    """A ragged batch of the 8B-shaped block (mojolearn forward with
+    ``lengths``): 4 rows padded to 4096 tokens, real lengths drawn from
+    [256, 4096] (seeded), run packed (only the real tokens through the norms,
+    GEMMs and attention); beside it the same batch run unragged, so the time
+    can be set against the share of real tokens."""
+    from gqa_causal_attention_amd import Block
+    from gqa_causal_attention_amd.workloads import make_workload
+    steps = steps or args.steps
+    wl = make_workload("llama3_8b_prefill_4k", batch=4)
+    cfg = wl["cfg"]
+    B, L = wl["batch"], wl["seq_len"]
+    lens = [int(v) for v in np.random.default_rng(21).integers(256, L + 1, size=B)]
+    blk = Block(cfg, wl["weights"])
+    x = torch.from_numpy(wl["x"]).cuda()
+    y = torch.empty_like(x)
+    res, per = {}, {}
+    for name, kw in (("ragged", {"lengths": lens}), ("padded", {})):
+        for _ in range(args.warmup):
+            blk.forward(x, out=y, **kw)
+        torch.cuda.synchronize()
+        blk.set_timing(True)
+        for _ in range(3):
+            blk.forward(x, out=y, **kw)
+        torch.cuda.synchronize()
+        per[name] = {k: round(v[0] / max(v[1], 1), 4) for k, v in blk.kernel_times().items()}
+        blk.set_timing(False)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            blk.forward(x, out=y, **kw)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        res[name] = timed_replays(torch, graph, steps)
+        del graph
+    real = sum(lens)
+    log(f"[c2r] lengths {lens}: ragged {res['ragged']:.4f} ms, padded batch {res['padded']:.4f} ms "
+        f"(real tokens {real} of {B * L})")
+    for k in per["padded"]:
+        log(f"   {k:16s} ragged {per['ragged'].get(k, 0.0):.4f} ms  padded {per['padded'][k]:.4f} ms")
+    for k in set(per["ragged"]) - set(per["padded"]):
+        log(f"   {k:16s} ragged {per['ragged'][k]:.4f} ms")
+    del blk, x, y
+    torch.cuda.empty_cache()
+    return {"workload": f"llama3_8b_prefill_4k ragged: B={B} rows padded to L={L}, lengths {lens} (seeded U[256, 4096])",
+            "ms_per_step": round(res["ragged"], 4), "ms_per_step_padded_batch": round(res["padded"], 4),
+            "real_tokens": real, "padded_tokens": B * L, "real_token_share": round(real / (B * L), 4),
+            "time_share": round(res["ragged"] / res["padded"], 4),
+            "real_tokens_per_s": round(real / (res["ragged"] * 1e-3), 1), "steps": steps}
+
+
 def leg_backward(args, torch, wl):
     """Gradients of a zero-state prefill on the prefill workload (x, and a seeded
     N(0, 1) grad_output): the forward recompute plus the backward, timed over
@@ -764,8 +815,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="c2,c3,bwd,c4,c5p,c5d",
-                    help="comma list of legs: c2 (headline, always run), c3, bwd, c4, c5p, c5d")
+    ap.add_argument("--legs", default="c2,c3,bwd,c2r,c4,c5p,c5d",
+                    help="comma list of legs: c2 (headline, always run), c3, bwd, c2r, c4, c5p, c5d")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--variant", choices=list(VARIANTS), default="plain",
                     help="block options on the 8B shapes (default: the plain Llama-shaped block)")
@@ -844,6 +895,8 @@ def main():
         out["decode"] = dec["summary"]
     if "bwd" in legs and args.variant == "plain":
         out["backward"] = leg_backward(args, torch, pre["wl"])
+    if "c2r" in legs and args.variant == "plain":
+        out["ragged_prefill"] = leg_ragged(args, torch, steps=min(args.steps, 10))
     for leg in ("c4", "c5p"):
         if leg in legs:
             r = leg_prefill(args, torch, leg, flusher, steps=min(args.steps, 10))

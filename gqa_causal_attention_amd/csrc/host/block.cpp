@@ -129,7 +129,11 @@ struct Scope {
   }
 };
 
-struct GemmPlan { int tile; int splits; int waves = 0; };
+// tile: GemmTile; splits: K splits (partials + ordered reduce); waves: per
+// workgroup (decode kernel).  m1 / tail_splits (large-M tiles only): rows
+// [m1, M) -- the tiles past the last full wave of the CUs -- run as a
+// separate launch with tail_splits K splits, so the tail fills the machine.
+struct GemmPlan { int tile; int splits; int waves = 0; int m1 = 0; int tail_splits = 0; };
 constexpr int kStatusWords = 4;
 
 }  // namespace
@@ -211,6 +215,33 @@ int big_tile_192() {
 // fills the 256 CUs better) 256x192 tiles.  129..512: 128x128 tiles.  65..128:
 // 64x128 tiles with a K split.  M <= 64 (decode): the weight-streaming kernel
 // (below), else 64x64 tiles split while there are fewer than 256 tiles.
+// A large-M plan whose last wave of tiles fills at most half of the CUs:
+// rows covered by the full waves stay as they are; the remaining rows are
+// split along K so that their tiles x splits come close to one full wave
+// (splits 64-aligned and at least 512 deep).
+// Partials of the largest tail with_tail plans: at most one wave (256 units)
+// of tile x split, each 256 rows x at most 256 float32 columns.
+constexpr size_t kTailPartBytes = (size_t)256 * 256 * 256 * 4;
+
+GemmPlan with_tail(GemmPlan p, int M, int N, int K, int cols) {
+  // the CU count the waves are counted in (GQA_GEMM_TAIL_CUS overrides it,
+  // read per plan so a test can exercise tails at small sizes; 0: no tails)
+  const char* e = getenv("GQA_GEMM_TAIL_CUS");
+  const int cus = e ? atoi(e) : 256;
+  if (cus <= 0) return p;
+  const long ntn = (N + cols - 1) / cols, ntm = (M + 255) / 256, tiles = ntm * ntn;
+  if (tiles <= cus || tiles % cus == 0 || tiles % cus > cus / 2) return p;
+  const long m1_tiles = (tiles / cus) * cus / ntn;  // M-tile rows wholly inside the full waves
+  if (m1_tiles <= 0 || m1_tiles >= ntm) return p;
+  const long t2 = (ntm - m1_tiles) * ntn;
+  int sp = (int)std::min<long>(8, cus / t2);
+  while (sp > 1 && (K % (64 * sp) != 0 || K / sp < 512)) --sp;
+  if (sp < 2) return p;
+  p.m1 = (int)(m1_tiles * 256);
+  p.tail_splits = sp;
+  return p;
+}
+
 GemmPlan plan_gemm(int M, int N, int K, bool gated) {
   if (M > 128) {
     if (M <= 512) return {kTile128x128, 1};
@@ -219,9 +250,9 @@ GemmPlan plan_gemm(int M, int N, int K, bool gated) {
     if (!gated && N % 192 == 0) {
       const long t192 = (long)((M + 255) / 256) * (N / 192);
       auto eff = [](long t) { return (double)t / (double)(((t + 255) / 256) * 256); };
-      if (eff(t192) > eff(t256) + 0.05) return {big_tile_192(), 1};
+      if (eff(t192) > eff(t256) + 0.05) return with_tail({big_tile_192(), 1}, M, N, K, 192);
     }
-    return {big_tile(), 1};
+    return with_tail({big_tile(), 1}, M, N, K, cols256);
   }
   if (M > 64) {
     const int cols = gated ? 64 : 128;
@@ -241,9 +272,12 @@ GemmPlan plan_gemm(int M, int N, int K, bool gated) {
     const char* e = getenv("GQA_SKINNY_CUS");  // tuning override
     return e ? atoi(e) : 256;
   }();
+  // Splits at least 1024 deep: on the 8B decode shapes a shallower o_proj
+  // split (8 x 512) streams no faster and doubles the partials the next
+  // kernel sums (measured 14.9 + 9.9 us against 13.1 + 8.5 us).
   static const int kmin = [] {
     const char* e = getenv("GQA_SKINNY_KMIN");  // tuning override
-    return e ? atoi(e) : 512;
+    return e ? atoi(e) : 1024;
   }();
   if (M <= 64 && K % 256 == 0) {
     const long groups = gemm_skinny_groups(N, gated);
@@ -273,8 +307,18 @@ GemmPlan plan_gemm(int M, int N, int K, bool gated) {
   return {kTile64x64, splits};
 }
 
+// Bytes of float32 K-split partials a plan needs for M rows of nb columns
+// (nb: N, or 2 N for the gated pair): its K splits over all rows, or its tail
+// splits over the tail rows.
+size_t plan_part_bytes(const GemmPlan& p, int M, size_t nb) {
+  size_t b = 0;
+  if (p.splits > 1) b = (size_t)p.splits * M * nb * 4;
+  if (p.tail_splits > 1 && p.m1 > 0 && p.m1 < M) b = std::max(b, (size_t)p.tail_splits * (M - p.m1) * nb * 4);
+  return b;
+}
+
 struct WsLayout {
-  size_t h, qkv, knew, vnew, ctx, x1, h2, act, part, attn_part, total;
+  size_t h, qkv, knew, vnew, ctx, x1, h2, act, part, attn_part, rows, total;
   GemmPlan p_qkv, p_o, p_gu, p_down;
   bool decode_attn;
 };
@@ -294,6 +338,7 @@ WsLayout layout_for(const gqa_block* blk, int B, int L) {
   w.x1 = take(T * d * 4);
   w.h2 = take(T * d * es);
   w.act = take(T * IT * es);
+  w.rows = take((size_t)B * 2 * 4);  // packed ragged rows: row_start[B], row_len[B]
   w.part = w.attn_part = 0;
   w.decode_attn = false;
   if (is_bf16(blk)) {
@@ -304,13 +349,14 @@ WsLayout layout_for(const gqa_block* blk, int B, int L) {
     w.p_gu = plan_gemm(M, IT, d, gated);
     w.p_down = plan_gemm(M, d, IT, false);
     size_t part = 0;
-    auto need = [&](const GemmPlan& p, size_t nb) {
-      if (p.splits > 1) part = std::max(part, (size_t)p.splits * M * nb * 4);
-    };
+    auto need = [&](const GemmPlan& p, size_t nb) { part = std::max(part, plan_part_bytes(p, M, nb)); };
     need(w.p_qkv, QW + 2 * (size_t)KW);
     need(w.p_o, d);
     need(w.p_gu, (gated ? 2 : 1) * (size_t)IT);
     need(w.p_down, d);
+    // a prefill of any fewer rows (a packed ragged batch) may split a tail of
+    // at most one wave of 256 x 256 tiles (with_tail): room for its partials
+    if (M > 512 && L > 1) part = std::max(part, kTailPartBytes);
     if (part) w.part = take(part);
     if (L == 1 && attention_decode_bf16_supported(c.head_dim, blk->G) && B <= attention_decode_max_rows()) {
       w.decode_attn = true;
@@ -468,10 +514,23 @@ struct BusyGuard {
   }
 };
 
+// Packed ragged rows (a ragged prefill): `rows` tokens, row b's real tokens at
+// packed rows row_start[b] .. + row_len[b] - 1 (device tables), with GEMM
+// plans for that many rows.
+struct PackedRows {
+  const int* row_start;
+  const int* row_len;
+  int rows;
+  GemmPlan p_qkv, p_o, p_gu, p_down;
+};
+
 // recompute_only: stop after the MLP's input norm (h2), the activations the
 // backward reads (no MLP, no y); the backward holds the busy guard itself.
+// pk: the tokens are packed ragged rows (x and y are [pk->rows, d]; the
+// caller holds the busy guard).
 int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, int L, void* ws, size_t wsb,
-              hipStream_t s, float* attn_lse = nullptr, bool recompute_only = false) {
+              hipStream_t s, float* attn_lse = nullptr, bool recompute_only = false,
+              const PackedRows* pk = nullptr) {
   if (!blk) return fail(GQA_ERR_ARG, "block is NULL");
   const auto& c = blk->cfg;
   if (B < 0 || L < 0) return fail(GQA_ERR_ARG, "B and L must be >= 0");
@@ -490,14 +549,21 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
       return fail(GQA_ERR_POSITION, "row %d: position %ld is at or beyond max_positions %d", b, start + L - 1,
                   c.max_positions);
   }
-  const WsLayout lay = layout_for(blk, B, L);
+  WsLayout lay = layout_for(blk, B, L);
   if (!ws || wsb < lay.total)
     return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? wsb : (size_t)0, lay.total);
-  BusyGuard guard(blk->busy, !recompute_only);
+  if (pk) {
+    lay.p_qkv = pk->p_qkv;
+    lay.p_o = pk->p_o;
+    lay.p_gu = pk->p_gu;
+    lay.p_down = pk->p_down;
+  }
+  BusyGuard guard(blk->busy, !recompute_only && !pk);
   if (!guard.ok) return fail(GQA_ERR_BUSY, "block is in use by another call");
 
   char* base = static_cast<char*>(ws);
-  const int T = B * L, d = c.d_model, QW = blk->QW, KW = blk->KW, IT = c.intermediate, hd = c.head_dim;
+  const int T = pk ? pk->rows : B * L, d = c.d_model, QW = blk->QW, KW = blk->KW, IT = c.intermediate,
+            hd = c.head_dim;
   const bool bf = is_bf16(blk);
   const int et = bf ? kBF16 : kF32;
   void* h = base + lay.h;
@@ -523,6 +589,33 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
     if (!bf) {
       Scope sc(tm, name, s);
       HIP_TRY(launch_gemm_f32(a, mode, epi, s));
+      return GQA_OK;
+    }
+    if (p.splits <= 1 && p.tail_splits > 1 && p.m1 > 0 && p.m1 < a.M && !defer_reduce) {
+      // rows [0, m1): the full waves of tiles; rows [m1, M): K-split, then the
+      // ordered reduce applies the epilogue to them
+      const int es_out = epi == kEpiResid ? 4 : (int)blk->es;
+      const size_t a_es = blk->es;
+      GemmArgs a1 = a;
+      a1.M = p.m1;
+      a1.splits = 1;
+      a1.k_split = a.K;
+      GemmArgs a2 = a;
+      a2.M = a.M - p.m1;
+      a2.A = static_cast<const char*>(a.A) + (size_t)p.m1 * a.lda * a_es;
+      a2.C = static_cast<char*>(a.C) + (size_t)p.m1 * a.ldc * es_out;
+      if (a.resid) a2.resid = a.resid + (size_t)p.m1 * a.ldr;
+      a2.bump = nullptr;
+      GemmArgs pa = a2;
+      pa.splits = p.tail_splits;
+      pa.k_split = a.K / p.tail_splits;
+      pa.partial = part;
+      Scope sc(tm, name, s);
+      HIP_TRY(launch_gemm_bf16(a1, mode, epi, p.tile, s));
+      HIP_TRY(launch_gemm_bf16(pa, mode, kEpiPartial, p.tile, s));
+      a2.splits = p.tail_splits;
+      a2.partial = part;
+      HIP_TRY(launch_splitk_reduce(a2, mode, epi, et, s));
       return GQA_OK;
     }
     if (p.splits <= 1) {
@@ -608,6 +701,11 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
     r.B = B; r.L = L; r.H = c.n_heads; r.KV = c.n_kv_heads; r.hd = hd; r.rd = c.rope_dim;
     r.cap = st ? st->capacity : 0; r.window = c.window; r.offset = offset; r.eps = c.norm_eps;
     r.defer_append = st && c.window > 0 && L > 1;
+    if (pk) {
+      r.row_start = pk->row_start;
+      r.row_len = pk->row_len;
+    }
+    r.prows = T;
     if (fuse_qkv) {
       r.part = part;
       r.splits = lay.p_qkv.splits;
@@ -646,6 +744,10 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
       HIP_TRY(launch_attention_decode_combine(a, s));
     } else if (bf && attention_prefill_bf16_supported(hd, blk->G)) {
       a.lse = attn_lse;
+      if (pk) {
+        a.row_start = pk->row_start;
+        a.row_len = pk->row_len;
+      }
       Scope sc(tm, "attn_prefill", s);
       HIP_TRY(launch_attention_prefill_bf16(a, s));
     } else {
@@ -1200,7 +1302,9 @@ std::string describe_plan(const gqa_block* blk, int kind, int B, int L) {
   if (kind == 0) {
     const WsLayout lay = layout_for(blk, B, L);
     auto g = [&](const char* name, const GemmPlan& p) {
-      if (bf) add("%s tile=%d splits=%d waves=%d", name, p.tile, p.splits, p.waves);
+      if (bf && p.tail_splits > 1) add("%s tile=%d splits=%d waves=%d tail_rows_from=%d tail_splits=%d", name, p.tile,
+                                       p.splits, p.waves, p.m1, p.tail_splits);
+      else if (bf) add("%s tile=%d splits=%d waves=%d", name, p.tile, p.splits, p.waves);
       else add("%s f32", name);
     };
     g("gemm_qkv", lay.p_qkv);
@@ -1432,13 +1536,68 @@ int gqa_block_forward_ragged(gqa_block* blk, const float* x, float* y, int32_t B
   for (int b = 0; b < B && L > 0; ++b)
     if (lengths[b] < 1 || lengths[b] > L)
       return fail(GQA_ERR_ARG, "row %d: length %d outside [1, %d]", b, lengths[b], L);
-  // Causal (and windowed) attention never lets a real position read a later
-  // one, and every other step is per token, so the real positions of the
-  // padded batch are exactly those of each row run alone; the padding
-  // positions are then overwritten with +0.0.
-  if (int r = run_block(blk, nullptr, x, y, B, L, ws, wsb, static_cast<hipStream_t>(stream))) return r;
-  if (B == 0 || L == 0) return GQA_OK;
-  HIP_TRY(launch_zero_padding(y, lengths, B, L, blk->cfg.d_model, static_cast<hipStream_t>(stream)));
+  if (B == 0 || L == 0) return run_block(blk, nullptr, x, y, B, L, ws, wsb, static_cast<hipStream_t>(stream));
+  const auto& c = blk->cfg;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int d = c.d_model;
+  int64_t rows = 0;
+  for (int b = 0; b < B; ++b) rows += lengths[b];
+  // Packed path: only the real tokens go through the norms, GEMMs, RoPE and
+  // attention (cost proportional to the sum of the lengths).  The matrix-core
+  // prefill attention takes per-row tables; the residual stream lives in the
+  // workspace's float32 x1 buffer (gathered from x, updated in place by the
+  // o_proj and down residual epilogues, scattered to y with +0.0 padding).
+  // Other blocks (float32, sandwich norms, L = 1) take the padded path.
+  const WsLayout lay = layout_for(blk, B, L);
+  bool packed = is_bf16(blk) && attention_prefill_bf16_supported(c.head_dim, blk->G) && !c.sandwich_norms && L > 1 &&
+                d % 4 == 0 && ws && wsb >= lay.total;
+  PackedRows pk{};
+  if (packed) {
+    const int M = (int)rows, QW = blk->QW, KW = blk->KW, IT = c.intermediate;
+    const bool gated = mlp_gated(c.mlp);
+    pk.p_qkv = plan_gemm(M, QW + 2 * KW, d, false);
+    pk.p_o = plan_gemm(M, d, QW, false);
+    pk.p_gu = plan_gemm(M, IT, d, gated);
+    pk.p_down = plan_gemm(M, d, IT, false);
+    size_t part = 0;
+    auto need = [&](const GemmPlan& p, size_t nb) { part = std::max(part, plan_part_bytes(p, M, nb)); };
+    need(pk.p_qkv, QW + 2 * (size_t)KW);
+    need(pk.p_o, d);
+    need(pk.p_gu, (gated ? 2 : 1) * (size_t)IT);
+    need(pk.p_down, d);
+    // the workspace holds the K-split partials of the padded batch's plans;
+    // packed plans needing more fall back to the padded path
+    const size_t have = lay.part ? (lay.attn_part ? lay.attn_part : lay.total) - lay.part : 0;
+    packed = part <= have;
+  }
+  if (!packed) {
+    // Causal (and windowed) attention never lets a real position read a later
+    // one, and every other step is per token, so the real positions of the
+    // padded batch are exactly those of each row run alone; the padding
+    // positions are then overwritten with +0.0.
+    if (int r = run_block(blk, nullptr, x, y, B, L, ws, wsb, s)) return r;
+    HIP_TRY(launch_zero_padding(y, lengths, B, L, d, s));
+    return GQA_OK;
+  }
+  if (!x || !y) return fail(GQA_ERR_ARG, "x or y is NULL");
+  BusyGuard guard(blk->busy);
+  if (!guard.ok) return fail(GQA_ERR_BUSY, "block is in use by another call");
+  char* base = static_cast<char*>(ws);
+  int* row_start = reinterpret_cast<int*>(base + lay.rows);
+  int* row_len = row_start + B;
+  float* xp = reinterpret_cast<float*>(base + lay.x1);
+  pk.row_start = row_start;
+  pk.row_len = row_len;
+  pk.rows = (int)rows;
+  KernelTimer* tm = &blk->timer;
+  {
+    Scope sc(tm, "ragged_gather", s);
+    HIP_TRY(launch_row_tables(lengths, B, row_start, row_len, s));
+    HIP_TRY(launch_gather_rows(x, xp, row_start, row_len, B, L, d, s));
+  }
+  if (int r = run_block(blk, nullptr, xp, xp, B, L, ws, wsb, s, nullptr, false, &pk)) return r;
+  Scope sc(tm, "ragged_scatter", s);
+  HIP_TRY(launch_scatter_rows(xp, y, row_start, row_len, B, L, d, s));
   return GQA_OK;
 }
 

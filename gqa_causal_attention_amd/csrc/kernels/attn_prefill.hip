@@ -104,7 +104,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_kernel(AttnArgs a, in
   const int bj = blockIdx.x % bkv;
   const int b = bj / a.KV, j = bj % a.KV;
   const int start = a.lengths ? a.lengths[b] : 0;
-  const int L = a.L, W = a.window;
+  // this row's tokens (a packed ragged row: its own length; row of token t in q / ctx)
+  const int L = a.row_len ? a.row_len[b] : a.L, W = a.window;
+  const int64_t row0 = a.row_start ? (int64_t)a.row_start[b] : (int64_t)b * a.L;
   const int npass = paired && slot < nqb - 1 - slot ? 2 : 1;
 
   // per-lane constants of the fragment reads
@@ -125,6 +127,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_kernel(AttnArgs a, in
   if (pass > 0) __syncthreads();  // the previous block's last LDS reads are done
   const int qb = pass == 0 ? nqb - 1 - slot : slot;
   const int q0 = qb * BQ;
+  if (q0 >= L) continue;  // past a ragged row's end (uniform over the workgroup)
   const int hh = w / wph, sub = w % wph;
   const int h = j * G + hh;
   const int qt0 = q0 + sub * 32;                     // first token of this wave
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_kernel(AttnArgs a, in
   bf16x8 qf[KS];
   {
     const int tok = min(qt0 + (lane & 31), L - 1);
-    const bf16* qr = static_cast<const bf16*>(a.q) + ((int64_t)b * L + tok) * a.ldq + (int64_t)h * HD + khi * 8;
+    const bf16* qr = static_cast<const bf16*>(a.q) + (row0 + tok) * a.ldq + (int64_t)h * HD + khi * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qr + ks * 16);
   }
@@ -521,10 +524,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_kernel(AttnArgs a, in
   const int tok = qt0 + (lane & 31);
   const float lt = l_run + xor32(l_run);
   if (a.lse && wave_valid && tok < L && lane < 32)
-    a.lse[((int64_t)b * a.H + h) * ((L + 3) & ~3) + tok] = m_ref + __log2f(lt);
+    a.lse[((int64_t)b * a.H + h) * ((a.L + 3) & ~3) + tok] = m_ref + __log2f(lt);
   if (wave_valid && tok < L) {
     const float inv = 1.0f / lt;
-    bf16* out = static_cast<bf16*>(a.ctx) + ((int64_t)b * L + tok) * ((int64_t)a.H * HD) + (int64_t)h * HD;
+    bf16* out = static_cast<bf16*>(a.ctx) + (row0 + tok) * ((int64_t)a.H * HD) + (int64_t)h * HD;
 #pragma unroll
     for (int r = 0; r < RT; ++r)
 #pragma unroll
@@ -555,8 +558,11 @@ bool pair_blocks(const AttnArgs& a, int nqb) {
     const char* e = getenv("GQA_ATTN_PAIR");
     return e ? atoi(e) : -1;
   }();
-  if (forced >= 0) return forced != 0 && a.window == 0;
-  return a.window == 0 && (int64_t)nqb * a.B * a.KV <= 4096;
+  if (forced >= 0) return forced != 0 && a.window == 0 && !a.row_len;
+  // (packed ragged rows: a block's work depends on its position only, so the
+  // longest-first order balances rows of any length; pairing by the padded
+  // index would not)
+  return a.window == 0 && !a.row_len && (int64_t)nqb * a.B * a.KV <= 4096;
 }
 
 template <int HD, int NW>

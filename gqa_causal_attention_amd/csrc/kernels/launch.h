@@ -133,6 +133,12 @@ struct RopeArgs {
   const float* part;
   int splits;
   const float* bias[3];    // q, k, v biases (may be null)
+  // Packed ragged rows (a ragged prefill with no state): row b's t-th token
+  // (t < row_len[b]) is q|k|v row row_start[b] + t; tokens t >= row_len[b]
+  // are padding and skipped.  Null: token (b, t) is row b * L + t.
+  const int* row_start;
+  const int* row_len;
+  int64_t prows;           // rows of the q|k|v activations (and of each K split of `part`); 0: B * L
 };
 // True if launch_rope_append takes `part` for this shape and element type.
 bool rope_append_fuses_reduce(int hd, int rd, int64_t ld, int elem);
@@ -154,6 +160,11 @@ struct AttnArgs {
   int nseg, rec_stride;    // decode: key segments per kv head; records per head (>= nseg + B)
   float* lse;              // prefill (bf16 kernel): if set, [B, H, Lp] log2-sum-exp2 of the scaled scores,
                            //   Lp = L rounded up to a multiple of 4
+  // Packed ragged rows (prefill bf16 kernel): query / output token t < row_len[b]
+  // of row b is row row_start[b] + t of q and ctx; its keys/values stay in
+  // knew/vnew [B, KV, L, hd].  Null: token (b, t) is row b * L + t.
+  const int* row_start;
+  const int* row_len;
 };
 hipError_t launch_attention_generic(const AttnArgs& a, int elem, hipStream_t s);
 hipError_t launch_attention_prefill_bf16(const AttnArgs& a, hipStream_t s);
@@ -217,6 +228,14 @@ hipError_t launch_attention_bwd_mfma(const BwdAttnArgs& a, void* dob, hipStream_
 
 hipError_t launch_count_nonfinite(const void* p, int elem, int64_t n, int* flag, hipStream_t s);
 hipError_t launch_bump_lengths(int* lengths, int n, int by, hipStream_t s);
+// Packed ragged rows: device tables row_start[b] (prefix of the lengths) and
+// row_len[b] from host lengths; x [B, L, d] real tokens -> packed rows xp; and
+// packed rows -> y [B, L, d] with +0.0 at padding positions (d % 4 == 0).
+hipError_t launch_row_tables(const int32_t* lengths_host, int B, int* row_start, int* row_len, hipStream_t s);
+hipError_t launch_gather_rows(const float* x, float* xp, const int* row_start, const int* row_len, int B, int L, int d,
+                              hipStream_t s);
+hipError_t launch_scatter_rows(const float* xp, float* y, const int* row_start, const int* row_len, int B, int L,
+                               int d, hipStream_t s);
 hipError_t launch_cache_nonfinite(const void* k, const void* v, const int* lengths, int elem, int B, int KV,
                                   int cap, int hd, int* count, hipStream_t s);
 // y [B, L, d] float32: positions t >= lengths_host[b] of row b set to +0.0.

@@ -41,11 +41,13 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
   const int64_t tok = gw / slots;
   const int slot = (int)(gw % slots);
   const int b = (int)(tok / a.L), t = (int)(tok % a.L);
+  if (a.row_len && t >= a.row_len[b]) return;  // padding of a packed ragged row
+  const int64_t prow = a.row_start ? a.row_start[b] + t : tok;
   const int start = a.lengths ? a.lengths[b] : 0;
   const int pos = start + t;
   const int hd = a.hd, half = hd / 2;
   const int QW = a.H * hd, KW = a.KV * hd;
-  T* row = static_cast<T*>(a.qkv) + tok * a.ld;
+  T* row = static_cast<T*>(a.qkv) + prow * a.ld;
 
   int kind, head;  // 0 = q, 1 = k, 2 = v
   T* src;
@@ -143,15 +145,18 @@ __global__ __launch_bounds__(256) void rope_append_vec_kernel(RopeArgs a) {
   const int slots = a.H + 2 * a.KV;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t T_ = (int64_t)a.B * a.L;
-  const bool live = idx < T_ * slots * GH;
+  bool live = idx < T_ * slots * GH;
   const int64_t hs = live ? idx / GH : 0;     // (token, slot)
   const int g = (int)(idx % GH);
   const int64_t tok = hs / slots;
   const int slot = (int)(hs % slots);
   const int b = (int)(tok / a.L), t = (int)(tok % a.L);
+  // padding of a packed ragged row: not live (a whole head slot's lanes alike)
+  if (a.row_len && t >= a.row_len[b]) live = false;
+  const int64_t prow = a.row_start && live ? a.row_start[b] + t : (a.row_start ? 0 : tok);
   const int pos = (a.lengths ? a.lengths[b] : 0) + t;
   const int QW = a.H * HD, KW = a.KV * HD;
-  bf16* row = static_cast<bf16*>(a.qkv) + tok * a.ld;
+  bf16* row = static_cast<bf16*>(a.qkv) + prow * a.ld;
   int kind, head;  // 0 = q, 1 = k, 2 = v
   bf16* src;
   if (slot < a.H) { kind = 0; head = slot; src = row + head * HD; }
@@ -168,8 +173,8 @@ __global__ __launch_bounds__(256) void rope_append_vec_kernel(RopeArgs a) {
     // summed over the splits in order, plus the segment's bias, rounded as the
     // GEMM epilogue would have stored them
     const int64_t c = (src - row) + o1;
-    const int64_t pstride = T_ * a.ld;
-    const float* pr = a.part + tok * a.ld + c;
+    const int64_t pstride = (a.prows ? a.prows : T_) * a.ld;
+    const float* pr = a.part + prow * a.ld + c;
     f32x4 sl = f32x4{0.f, 0.f, 0.f, 0.f}, sh = sl;
     for (int z0 = 0; z0 < a.splits; z0 += 4) {  // 4 splits' loads in flight together
       f32x4 tl[4], th[4];

@@ -82,6 +82,76 @@ hipError_t launch_zero_padding(float* y, const int32_t* lengths_host, int B, int
   return hipSuccess;
 }
 
+// Packed ragged rows: row tables written from host values passed by value
+// (first row `first`, `count` rows), the gather of the real tokens of x
+// [B, L, d] into packed rows, and the scatter back with +0.0 padding.
+struct RowTableChunk {
+  int32_t start[kPadRows];
+  int32_t len[kPadRows];
+};
+__global__ __launch_bounds__(256) void row_tables_kernel(RowTableChunk c, int first, int count, int* row_start,
+                                                         int* row_len) {
+  const int i = threadIdx.x;
+  if (i < count) {
+    row_start[first + i] = c.start[i];
+    row_len[first + i] = c.len[i];
+  }
+}
+// grid (token blocks of 4, B): 64 threads per token row, float4 pieces
+__global__ __launch_bounds__(256) void gather_rows_kernel(const float* __restrict__ x, float* __restrict__ xp,
+                                                          const int* row_start, const int* row_len, int L, int d) {
+  const int b = blockIdx.y, t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= row_len[b]) return;
+  const float4* src = reinterpret_cast<const float4*>(x + ((int64_t)b * L + t) * d);
+  float4* dst = reinterpret_cast<float4*>(xp + ((int64_t)row_start[b] + t) * d);
+  for (int i = threadIdx.x & 63; i < d / 4; i += 64) dst[i] = src[i];
+}
+__global__ __launch_bounds__(256) void scatter_rows_kernel(const float* __restrict__ xp, float* __restrict__ y,
+                                                           const int* row_start, const int* row_len, int L, int d) {
+  const int b = blockIdx.y, t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= L) return;
+  float4* dst = reinterpret_cast<float4*>(y + ((int64_t)b * L + t) * d);
+  if (t < row_len[b]) {
+    const float4* src = reinterpret_cast<const float4*>(xp + ((int64_t)row_start[b] + t) * d);
+    for (int i = threadIdx.x & 63; i < d / 4; i += 64) dst[i] = src[i];
+  } else {
+    for (int i = threadIdx.x & 63; i < d / 4; i += 64) dst[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+hipError_t launch_row_tables(const int32_t* lengths_host, int B, int* row_start, int* row_len, hipStream_t s) {
+  int64_t acc = 0;
+  for (int first = 0; first < B; first += kPadRows) {
+    const int count = B - first < kPadRows ? B - first : kPadRows;
+    RowTableChunk c{};
+    for (int r = 0; r < count; ++r) {
+      c.start[r] = (int32_t)acc;
+      c.len[r] = lengths_host[first + r];
+      acc += lengths_host[first + r];
+    }
+    hipLaunchKernelGGL(row_tables_kernel, dim3(1), dim3(256), 0, s, c, first, count, row_start, row_len);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_gather_rows(const float* x, float* xp, const int* row_start, const int* row_len, int B, int L, int d,
+                              hipStream_t s) {
+  if (B <= 0 || L <= 0 || d % 4 != 0) return B <= 0 || L <= 0 ? hipSuccess : hipErrorInvalidValue;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)((L + 3) / 4), (unsigned)B), dim3(256), 0, s, x, xp,
+                     row_start, row_len, L, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_rows(const float* xp, float* y, const int* row_start, const int* row_len, int B, int L,
+                               int d, hipStream_t s) {
+  if (B <= 0 || L <= 0 || d % 4 != 0) return B <= 0 || L <= 0 ? hipSuccess : hipErrorInvalidValue;
+  hipLaunchKernelGGL(scatter_rows_kernel, dim3((unsigned)((L + 3) / 4), (unsigned)B), dim3(256), 0, s, xp, y,
+                     row_start, row_len, L, d);
+  return hipGetLastError();
+}
+
 hipError_t launch_count_nonfinite(const void* p, int elem, int64_t n, int* flag, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);

@@ -146,19 +146,19 @@ def test_bf16_decode_ragged_rows_prefilled_cache(torch_cuda):
 
 
 DECODE_GEMM_BLOCKS = {
-    # q/k/v, o_proj and gate/up K-split in two (512 deep: 4-chunk weight ring);
-    # down unsplit, 1280 deep (10 chunks: 2-chunk ring), fused residual
-    "split": dict(d_model=1024, n_heads=8, n_kv_heads=2, head_dim=128, intermediate=1280, qkv_bias=True),
+    # q/k/v, o_proj and gate/up K-split in two (1024 deep); down unsplit, 1280
+    # deep (10 chunks), fused residual
+    "split": dict(d_model=2048, n_heads=16, n_kv_heads=4, head_dim=128, intermediate=1280, qkv_bias=True),
     # no split: the fused bias / residual / gated epilogues (4- and 6-chunk depths)
     "fused": dict(d_model=512, n_heads=8, n_kv_heads=2, head_dim=64, intermediate=768, qkv_bias=True,
                   mlp="geglu_tanh"),
     # split q/k/v GEMM with partial rotary: the RoPE kernel sums the partials
     # of rotated and pass-through columns alike
-    "split_partial_rotary": dict(d_model=1024, n_heads=8, n_kv_heads=2, head_dim=128, intermediate=1280,
+    "split_partial_rotary": dict(d_model=2048, n_heads=16, n_kv_heads=4, head_dim=128, intermediate=1280,
                                  qkv_bias=True, rope_dim=64, rope_theta=5e5, rope_scaling=LLAMA31_ROPE),
     # sandwich norms with biases: the norm kernels sum the o_proj and down
     # K-split partials (+ bias) before the output norm and the residual add
-    "split_sandwich_biases": dict(d_model=1024, n_heads=8, n_kv_heads=2, head_dim=128, intermediate=1280,
+    "split_sandwich_biases": dict(d_model=2048, n_heads=16, n_kv_heads=4, head_dim=128, intermediate=2560,
                                   sandwich_norms=True, o_bias=True, mlp_bias=True, mlp="geglu",
                                   norm="rmsnorm_offset"),
     # ungated MLP: the up GEMM stores act(up + bias)
@@ -175,6 +175,11 @@ def test_bf16_decode_gemm_batch_sizes(torch_cuda, kind, B):
     cfg, W = random_block(210 + list(DECODE_GEMM_BLOCKS).index(kind), dtype="bf16", **DECODE_GEMM_BLOCKS[kind])
     rng = np.random.default_rng(12 + B)
     blk = _block(cfg, W)
+    plan = blk.describe_plan(B, 1)
+    if kind.startswith("split"):   # the K-split partial paths this case is for
+        assert "gemm_qkv tile=6 splits=2" in plan and "gemm_o tile=6 splits=2" in plan, plan
+    if kind == "split_sandwich_biases":
+        assert "gemm_down tile=6 splits=2" in plan, plan
     st = blk.allocate_state(B, 8)
     ost = OracleState(cfg, B, 8)
     x = rng.standard_normal((B, 5, cfg["d_model"]), dtype=np.float32)
@@ -254,6 +259,55 @@ def test_f32_block_variants(torch_cuda, name):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("window,softcap", [(0, 0.0), (200, 30.0)])
+def test_ragged_prefill_packed_multiblock(torch_cuda, window, softcap):
+    """The packed ragged path at a size that runs the large-M GEMM tiles (1278
+    real tokens of 2800 padded) and several attention query blocks per row,
+    rows of 700, 513, 64 and 1 tokens, with and without a window and softcap:
+    against the oracle, padding +0.0, and that the packed path ran (its
+    gather / scatter launches appear in the library's timing table)."""
+    cfg, W = random_block(43 + window, dtype="bf16", d_model=512, n_heads=8, n_kv_heads=2, head_dim=128,
+                          intermediate=1024, window=window, attn_softcap=softcap)
+    B, L, lens = 4, 700, [700, 513, 64, 1]
+    rng = np.random.default_rng(18)
+    x = rng.standard_normal((B, L, cfg["d_model"]), dtype=np.float32)
+    blk = _block(cfg, W)
+    y = blk.forward(to_gpu(x), lengths=lens).cpu().numpy()
+    ref = block_forward(cfg, W, x, dtype=np.float32, lengths=lens)
+    for i, n in enumerate(lens):
+        check_close(y[i, :n], ref[i, :n], x[i, :n], "bf16", f"packed ragged row {i} (length {n})")
+        assert np.all(y[i, n:] == 0.0) and not np.any(np.signbit(y[i, n:]))
+    # the packed path ran: its gather / scatter launches are in the timing table
+    blk.set_timing(True)
+    blk.forward(to_gpu(x), lengths=lens)
+    names = set(blk.kernel_times())
+    blk.set_timing(False)
+    assert {"ragged_gather", "ragged_scatter"} <= names, names
+
+
+def test_bf16_gemm_tail_split(torch_cuda, monkeypatch):
+    """Large-M GEMMs whose last wave of tiles is at most half full run that
+    tail as a separate K-split launch plus ordered reduce.  Counting waves in
+    8 CUs (the tuning override) makes o_proj and down at M = 1100 take that
+    path (rows from 1024, 2 splits), checked in the library's plan, against
+    the oracle and against the same prefill without tail splits."""
+    cfg, W = random_block(44, dtype="bf16", d_model=1024, n_heads=8, n_kv_heads=2, head_dim=128,
+                          intermediate=2048)
+    rng = np.random.default_rng(19)
+    x = rng.standard_normal((1, 1100, 1024), dtype=np.float32)
+    blk = _block(cfg, W)
+    monkeypatch.setenv("GQA_GEMM_TAIL_CUS", "0")
+    plain = blk.forward(to_gpu(x)).cpu().numpy()
+    monkeypatch.setenv("GQA_GEMM_TAIL_CUS", "8")
+    plan = blk.describe_plan(1, 1100)
+    assert "gemm_o tile=7 splits=1 waves=0 tail_rows_from=1024 tail_splits=2" in plan, plan
+    assert "gemm_down tile=7 splits=1 waves=0 tail_rows_from=1024 tail_splits=2" in plan, plan
+    y = blk.forward(to_gpu(x)).cpu().numpy()
+    monkeypatch.delenv("GQA_GEMM_TAIL_CUS")
+    check_close(y, block_forward(cfg, W, x, dtype=np.float32), x, "bf16", "tail-split GEMMs")
+    check_close(y, plain, x, "bf16", "tail-split vs whole-wave GEMMs")
+
+
 def test_page_worked_example_golden(torch_cuda):
     """The HIP block on the mojolearn page's usage example (float32 weights,
     TransformerBlock(weights, n_heads=4) on x of shape (2, 16, 64)) against the
@@ -284,9 +338,11 @@ def test_page_worked_example_golden(torch_cuda):
 def test_ragged_prefill_lengths(torch_cuda, dtype):
     """mojolearn forward(x, lengths=...): a ragged batch against the oracle's
     reading of it (each row alone at its own length, padding +0.0), padding
-    exactly positive zero, real positions bitwise equal to the unragged run's
-    (causality), padding inputs changing nothing, and the argument errors.
-    The bf16 case has T = 600 tokens, so it runs the large-M GEMM tiles."""
+    exactly positive zero, real positions equal to the unragged run's
+    (causality: bitwise on the float32 padded path; to the bf16 bar on the
+    packed path, whose GEMMs see 258 rows instead of 600 and so run other
+    tiles), padding inputs changing nothing (bitwise), and the argument
+    errors."""
     import torch
     from gqa_causal_attention_amd.binding import GqaError
     if dtype == "bf16":
@@ -307,7 +363,10 @@ def test_ragged_prefill_lengths(torch_cuda, dtype):
     for i, n in enumerate(lens):
         pad = y[i, n:]
         assert np.all(pad == 0.0) and not np.any(np.signbit(pad)), f"row {i}: padding not +0.0"
-        np.testing.assert_array_equal(y[i, :n], full[i, :n])
+        if dtype == "f32":
+            np.testing.assert_array_equal(y[i, :n], full[i, :n])
+        else:
+            check_close(y[i, :n], full[i, :n], x[i, :n], dtype, f"ragged row {i} vs unragged")
         x2[i, n:] = rng.standard_normal((L - n, cfg["d_model"]), dtype=np.float32) * 3
     np.testing.assert_array_equal(blk.forward(to_gpu(x2), lengths=lens).cpu().numpy(), y)
     with pytest.raises(GqaError):
