@@ -164,6 +164,12 @@ DECODE_GEMM_BLOCKS = {
     # ungated MLP: the up GEMM stores act(up + bias)
     "ungated_biases": dict(d_model=1024, n_heads=8, n_kv_heads=2, head_dim=128, intermediate=1280,
                            mlp="gelu_tanh", mlp_bias=True, o_bias=True, norm="layernorm", norm_bias=True),
+    # o_proj and down K-split around an unsplit gate/up: the norm kernel sums
+    # o_proj's partials (+ bias), down's reduce kernel adds bias and residual
+    # (offset RMSNorm weights)
+    "split_o_down_offset_biases": dict(d_model=1024, n_heads=16, n_kv_heads=4, head_dim=128,
+                                       intermediate=2048, o_bias=True, mlp_bias=True, mlp="geglu",
+                                       norm="rmsnorm_offset"),
 }
 
 
@@ -176,10 +182,15 @@ def test_bf16_decode_gemm_batch_sizes(torch_cuda, kind, B):
     rng = np.random.default_rng(12 + B)
     blk = _block(cfg, W)
     plan = blk.describe_plan(B, 1)
-    if kind.startswith("split"):   # the K-split partial paths this case is for
-        assert "gemm_qkv tile=6 splits=2" in plan and "gemm_o tile=6 splits=2" in plan, plan
+    splits = {ln.split()[0]: int(ln.split("splits=")[1].split()[0]) for ln in plan.splitlines() if "splits=" in ln}
+    if kind.startswith("split") and kind != "split_o_down_offset_biases":   # the K-split partial paths
+        assert "gemm_qkv tile=6" in plan and "gemm_o tile=6" in plan, plan
+        assert splits["gemm_qkv"] >= 2 and splits["gemm_o"] >= 2, plan
     if kind == "split_sandwich_biases":
-        assert "gemm_down tile=6 splits=2" in plan, plan
+        assert "gemm_down tile=6" in plan and splits["gemm_down"] >= 2, plan
+    if kind == "split_o_down_offset_biases":
+        assert "gemm_o tile=6" in plan and "gemm_down tile=6" in plan, plan
+        assert splits["gemm_o"] >= 2 and splits["gemm_down"] >= 2 and splits["gemm_gate_up"] == 1, plan
     st = blk.allocate_state(B, 8)
     ost = OracleState(cfg, B, 8)
     x = rng.standard_normal((B, 5, cfg["d_model"]), dtype=np.float32)
