@@ -130,10 +130,11 @@ struct Scope {
 };
 
 // tile: GemmTile; splits: K splits (partials + ordered reduce); waves: per
-// workgroup (decode kernel).  m1 / tail_splits (large-M tiles only): rows
-// [m1, M) -- the tiles past the last full wave of the CUs -- run as a
-// separate launch with tail_splits K splits, so the tail fills the machine.
-struct GemmPlan { int tile; int splits; int waves = 0; int m1 = 0; int tail_splits = 0; };
+// workgroup (decode kernel).  m1 / n1 / tail_splits (large-M tiles only):
+// rows [m1, M), or else columns [n1, N) -- the tiles past the last full wave
+// of the CUs -- run as a separate launch with tail_splits K splits, so the
+// tail fills the machine.
+struct GemmPlan { int tile; int splits; int waves = 0; int m1 = 0; int tail_splits = 0; int n1 = 0; int n = 0; };
 constexpr int kStatusWords = 4;
 
 }  // namespace
@@ -231,14 +232,35 @@ GemmPlan with_tail(GemmPlan p, int M, int N, int K, int cols) {
   if (cus <= 0) return p;
   const long ntn = (N + cols - 1) / cols, ntm = (M + 255) / 256, tiles = ntm * ntn;
   if (tiles <= cus || tiles % cus == 0 || tiles % cus > cus / 2) return p;
-  const long m1_tiles = (tiles / cus) * cus / ntn;  // M-tile rows wholly inside the full waves
-  if (m1_tiles <= 0 || m1_tiles >= ntm) return p;
-  const long t2 = (ntm - m1_tiles) * ntn;
-  int sp = (int)std::min<long>(8, cus / t2);
-  while (sp > 1 && (K % (64 * sp) != 0 || K / sp < 512)) --sp;
-  if (sp < 2) return p;
-  p.m1 = (int)(m1_tiles * 256);
-  p.tail_splits = sp;
+  const long full = (tiles / cus) * cus;  // tiles in the full waves
+  // K splits of a tail of t2 tiles: as many as fit one wave, 64-aligned, at least 512 deep
+  auto splits_for = [&](long t2) {
+    int sp = (int)std::min<long>(8, cus / t2);
+    while (sp > 1 && (K % (64 * sp) != 0 || K / sp < 512)) --sp;
+    return sp;
+  };
+  // rows: the M-tile rows wholly inside the full waves
+  const long m1_tiles = full / ntn;
+  if (m1_tiles > 0 && m1_tiles < ntm) {
+    const int sp = splits_for((ntm - m1_tiles) * ntn);
+    if (sp >= 2) {
+      p.m1 = (int)(m1_tiles * 256);
+      p.tail_splits = sp;
+      return p;
+    }
+  }
+  // columns: when the full waves hold whole N-tile columns
+  if (full % ntm == 0) {
+    const long n1_tiles = full / ntm;
+    if (n1_tiles > 0 && n1_tiles < ntn) {
+      const int sp = splits_for(ntm * (ntn - n1_tiles));
+      if (sp >= 2) {
+        p.n1 = (int)(n1_tiles * cols);
+        p.n = N;
+        p.tail_splits = sp;
+      }
+    }
+  }
   return p;
 }
 
@@ -247,7 +269,8 @@ GemmPlan plan_gemm(int M, int N, int K, bool gated) {
     if (M <= 512) return {kTile128x128, 1};
     const int cols256 = gated ? 128 : 256;
     const long t256 = (long)((M + 255) / 256) * ((N + cols256 - 1) / cols256);
-    if (!gated && N % 192 == 0) {
+    const char* e192 = getenv("GQA_GEMM_TILE192");  // tuning override (0: never the 256x192 tile)
+    if (!gated && N % 192 == 0 && !(e192 && atoi(e192) == 0)) {
       const long t192 = (long)((M + 255) / 256) * (N / 192);
       auto eff = [](long t) { return (double)t / (double)(((t + 255) / 256) * 256); };
       if (eff(t192) > eff(t256) + 0.05) return with_tail({big_tile_192(), 1}, M, N, K, 192);
@@ -314,6 +337,8 @@ size_t plan_part_bytes(const GemmPlan& p, int M, size_t nb) {
   size_t b = 0;
   if (p.splits > 1) b = (size_t)p.splits * M * nb * 4;
   if (p.tail_splits > 1 && p.m1 > 0 && p.m1 < M) b = std::max(b, (size_t)p.tail_splits * (M - p.m1) * nb * 4);
+  if (p.tail_splits > 1 && p.n1 > 0 && p.n1 < p.n)
+    b = std::max(b, (size_t)p.tail_splits * M * (nb / p.n) * (p.n - p.n1) * 4);
   return b;
 }
 
@@ -589,6 +614,58 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
     if (!bf) {
       Scope sc(tm, name, s);
       HIP_TRY(launch_gemm_f32(a, mode, epi, s));
+      return GQA_OK;
+    }
+    if (p.splits <= 1 && p.tail_splits > 1 && p.n1 > 0 && p.n1 < a.N && p.n == a.N && !defer_reduce) {
+      // columns [0, n1): the full waves of tiles; columns [n1, N): K-split, then
+      // the ordered reduce applies the epilogue to them.  Each part is the same
+      // GEMM over a column range: the weight segments, biases and outputs of
+      // that range.
+      const int es_out = epi == kEpiResid ? 4 : (int)blk->es;
+      auto columns = [&](int n0, int nend) {
+        GemmArgs r = a;
+        r.N = nend - n0;
+        r.C = static_cast<char*>(a.C) + (size_t)n0 * es_out;
+        if (a.resid) r.resid = a.resid + n0;
+        if (mode == kModeGated) {  // gate / up rows n0 .. of both matrices
+          for (int q = 0; q < 2; ++q) {
+            r.B[q] = static_cast<const char*>(a.B[q]) + (size_t)n0 * a.K * blk->es;
+            r.bias[q] = a.bias[q] ? a.bias[q] + n0 : nullptr;
+          }
+          return r;
+        }
+        const int64_t starts[3] = {0, a.seg_end[0], a.seg_end[1]};
+        int k = 0;
+        for (int q = 0; q < 3; ++q) {
+          const int64_t lo = std::max<int64_t>(starts[q], n0), hi = std::min<int64_t>(a.seg_end[q], nend);
+          if (lo >= hi) continue;
+          r.B[k] = static_cast<const char*>(a.B[q]) + (size_t)(lo - starts[q]) * a.K * blk->es;
+          r.bias[k] = a.bias[q] ? a.bias[q] + (lo - starts[q]) : nullptr;
+          r.seg_end[k] = hi - n0;
+          ++k;
+        }
+        for (; k < 3; ++k) {
+          r.B[k] = r.B[k - 1];
+          r.bias[k] = r.bias[k - 1];
+          r.seg_end[k] = r.seg_end[k - 1];
+        }
+        return r;
+      };
+      GemmArgs a1 = columns(0, p.n1);
+      a1.splits = 1;
+      a1.k_split = a.K;
+      GemmArgs a2 = columns(p.n1, a.N);
+      a2.bump = nullptr;
+      GemmArgs pa = a2;
+      pa.splits = p.tail_splits;
+      pa.k_split = a.K / p.tail_splits;
+      pa.partial = part;
+      Scope sc(tm, name, s);
+      HIP_TRY(launch_gemm_bf16(a1, mode, epi, p.tile, s));
+      HIP_TRY(launch_gemm_bf16(pa, mode, kEpiPartial, p.tile, s));
+      a2.splits = p.tail_splits;
+      a2.partial = part;
+      HIP_TRY(launch_splitk_reduce(a2, mode, epi, et, s));
       return GQA_OK;
     }
     if (p.splits <= 1 && p.tail_splits > 1 && p.m1 > 0 && p.m1 < a.M && !defer_reduce) {
@@ -1302,8 +1379,12 @@ std::string describe_plan(const gqa_block* blk, int kind, int B, int L) {
   if (kind == 0) {
     const WsLayout lay = layout_for(blk, B, L);
     auto g = [&](const char* name, const GemmPlan& p) {
-      if (bf && p.tail_splits > 1) add("%s tile=%d splits=%d waves=%d tail_rows_from=%d tail_splits=%d", name, p.tile,
-                                       p.splits, p.waves, p.m1, p.tail_splits);
+      if (bf && p.tail_splits > 1 && p.n1 > 0)
+        add("%s tile=%d splits=%d waves=%d tail_cols_from=%d tail_splits=%d", name, p.tile, p.splits, p.waves, p.n1,
+            p.tail_splits);
+      else if (bf && p.tail_splits > 1)
+        add("%s tile=%d splits=%d waves=%d tail_rows_from=%d tail_splits=%d", name, p.tile, p.splits, p.waves, p.m1,
+            p.tail_splits);
       else if (bf) add("%s tile=%d splits=%d waves=%d", name, p.tile, p.splits, p.waves);
       else add("%s f32", name);
     };

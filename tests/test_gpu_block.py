@@ -319,6 +319,31 @@ def test_bf16_gemm_tail_split(torch_cuda, monkeypatch):
     check_close(y, plain, x, "bf16", "tail-split vs whole-wave GEMMs")
 
 
+def test_bf16_gemm_column_tail_split(torch_cuda, monkeypatch):
+    """When the full waves hold whole columns of tiles rather than whole rows,
+    the tail is the remaining columns.  Counting waves in 32 CUs, o_proj and
+    down (N = 3072, 4 x 12 tiles at M = 1024) run columns [0, 2048) as one
+    wave and columns [2048, 3072) in 2 K splits; checked in the plan, against
+    the oracle and against the same prefill without tail splits."""
+    cfg, W = random_block(45, dtype="bf16", d_model=3072, n_heads=8, n_kv_heads=2, head_dim=128,
+                          intermediate=1024, o_bias=True, mlp_bias=True)
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((2, 512, 3072), dtype=np.float32)
+    blk = _block(cfg, W)
+    monkeypatch.setenv("GQA_GEMM_TILE192", "0")  # 256-wide tiles (the shape would take 256 x 192)
+    monkeypatch.setenv("GQA_GEMM_TAIL_CUS", "0")
+    plain = blk.forward(to_gpu(x)).cpu().numpy()
+    monkeypatch.setenv("GQA_GEMM_TAIL_CUS", "32")
+    plan = blk.describe_plan(2, 512)
+    assert "gemm_o tile=7 splits=1 waves=0 tail_cols_from=2048 tail_splits=2" in plan, plan
+    assert "gemm_down tile=7 splits=1 waves=0 tail_cols_from=2048 tail_splits=2" in plan, plan
+    y = blk.forward(to_gpu(x)).cpu().numpy()
+    monkeypatch.delenv("GQA_GEMM_TAIL_CUS")
+    monkeypatch.delenv("GQA_GEMM_TILE192")
+    check_close(y, block_forward(cfg, W, x, dtype=np.float32), x, "bf16", "column-tail GEMMs")
+    check_close(y, plain, x, "bf16", "column-tail vs whole-wave GEMMs")
+
+
 def test_page_worked_example_golden(torch_cuda):
     """The HIP block on the mojolearn page's usage example (float32 weights,
     TransformerBlock(weights, n_heads=4) on x of shape (2, 16, 64)) against the
