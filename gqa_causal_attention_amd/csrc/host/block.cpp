@@ -147,7 +147,8 @@ struct gqa_block {
   float* cos_tab = nullptr;
   float* sin_tab = nullptr;
   // device words: [0] a non-finite input was seen, [1] the count of non-finite
-  // cached keys/values found by the GQA_CHECK_FINITE scan
+  // cached keys/values found by the GQA_CHECK_FINITE scan, [2] a device start
+  // position was out of range (clamped)
   int* status = nullptr;
   bool check_finite = false;
   std::atomic<int> busy{0};
@@ -777,6 +778,7 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
     r.k_norm = static_cast<const float*>(blk->w[W_KN]);
     r.B = B; r.L = L; r.H = c.n_heads; r.KV = c.n_kv_heads; r.hd = hd; r.rd = c.rope_dim;
     r.cap = st ? st->capacity : 0; r.window = c.window; r.offset = offset; r.eps = c.norm_eps;
+    r.max_pos = c.max_positions; r.pos_flag = blk->status + 2;
     r.defer_append = st && c.window > 0 && L > 1;
     if (pk) {
       r.row_start = pk->row_start;
@@ -802,6 +804,7 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
     a.lengths = lengths; a.ctx = ctx;
     a.B = B; a.L = L; a.H = c.n_heads; a.KV = c.n_kv_heads; a.hd = hd;
     a.cap = st ? st->capacity : 0; a.window = c.window; a.softcap = c.attn_softcap;
+    a.max_pos = c.max_positions;
     if (bf && lay.decode_attn) {
       a.part = reinterpret_cast<float*>(base + lay.attn_part);
       // equal key segments over the rows' attended keys (host mirror of the
@@ -1705,8 +1708,12 @@ int gqa_block_status(gqa_block* blk, void* stream) {
   HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
   int w[kStatusWords] = {};
   HIP_TRY(hipMemcpy(w, blk->status, sizeof w, hipMemcpyDeviceToHost));
-  if (w[0] || w[1]) {
+  if (w[0] || w[1] || w[2]) {
     HIP_TRY(hipMemset(blk->status, 0, sizeof w));
+    if (w[2])
+      return fail(GQA_ERR_POSITION, "a device position was beyond the state's capacity or max_positions (clamped; "
+                                    "outputs since the last check are not valid): a replayed captured step must "
+                                    "restore the rows' lengths");
     if (w[0] && w[1])
       return fail(GQA_ERR_NONFINITE, "a non-finite input value was seen; %d non-finite cached key/value values", w[1]);
     if (w[0]) return fail(GQA_ERR_NONFINITE, "a non-finite input value was seen");

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs a) {
       const int bb = base + lane;
       int v = 0;
       if (bb < a.B) {
-        const int pb = a.lengths ? a.lengths[bb] : 0;
+        const int pb = guarded_start(a.lengths, bb, 1, position_limit(W, a.cap, a.max_pos), nullptr);
         v = pb + 1 - (W > 0 ? max(0, pb - W + 1) : 0);
       }
 #pragma unroll
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(NT) void attn_decode_kernel(AttnArgs a) {
   }
   for (bool first_piece = true; b < a.B && pre[b] < seg_hi; ++b, first_piece = false) {
   if (!first_piece) __syncthreads();  // the previous piece's LDS slabs have been read
-  const int start = a.lengths ? a.lengths[b] : 0;
+  const int start = guarded_start(a.lengths, b, 1, position_limit(W, a.cap, a.max_pos), nullptr);
   const int p = start;                  // the new token's position (L = 1)
   const int klo = W > 0 ? max(0, p - W + 1) : 0;
   const int ks0 = klo + (int)(max(seg_lo, (int64_t)pre[b]) - pre[b]);

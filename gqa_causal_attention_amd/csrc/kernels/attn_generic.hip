@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
   const int h = active ? (int)(gw % a.H) : 0;
   const int b = (int)(tok / a.L), t = (int)(tok % a.L);
   const int G = a.H / a.KV, j = h / G, hd = a.hd;
-  const int start = a.lengths ? a.lengths[b] : 0;
+  const int start = guarded_start(a.lengths, b, a.L, position_limit(a.window, a.cap, a.max_pos), nullptr);
   const int p = start + t;
   const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
   const float scale = 1.0f / sqrtf((float)hd);

@@ -103,7 +103,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_kernel(AttnArgs a, in
   const int slot = (int)(blockIdx.x / bkv);
   const int bj = blockIdx.x % bkv;
   const int b = bj / a.KV, j = bj % a.KV;
-  const int start = a.lengths ? a.lengths[b] : 0;
+  const int start = guarded_start(a.lengths, b, a.L, position_limit(a.window, a.cap, a.max_pos), nullptr);
   // this row's tokens (a packed ragged row: its own length; row of token t in q / ctx)
   const int L = a.row_len ? a.row_len[b] : a.L, W = a.window;
   const int64_t row0 = a.row_start ? (int64_t)a.row_start[b] : (int64_t)b * a.L;

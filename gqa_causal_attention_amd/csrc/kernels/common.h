@@ -98,6 +98,28 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // Value of lane (l ^ 32): the gfx950 swap of the upper half of one register
 // with the lower half of another (v_permlane32_swap), no LDS round trip.
+// Start position of row b for a call of L tokens, from the device lengths.
+// A start that would put a position below zero or at / past `limit` (the
+// cache capacity without a window, else the RoPE tables' rows) is clamped
+// into range, so no access leaves the cache or the tables, and *flag (if
+// given) is set; the host reports it as a position error.  The host checks
+// its own mirror of the lengths before every call; this guards replays of
+// captured steps, which advance only the device copy.
+__device__ __forceinline__ int guarded_start(const int* lengths, int b, int L, int limit, int* flag) {
+  const int s = lengths ? lengths[b] : 0;
+  const int hi = max(limit - L, 0);
+  if (s < 0 || s > hi) {
+    if (flag) *flag = 1;
+    return min(max(s, 0), hi);
+  }
+  return s;
+}
+// The limit above for a cache of `cap` slots (window 0: slot = position) and
+// tables of max_pos rows.
+__device__ __forceinline__ int position_limit(int window, int cap, int max_pos) {
+  return window > 0 ? max_pos : min(cap, max_pos);
+}
+
 __device__ __forceinline__ float xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);

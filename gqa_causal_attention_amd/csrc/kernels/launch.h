@@ -123,6 +123,8 @@ struct RopeArgs {
   const float* q_norm;     // [hd] or null
   const float* k_norm;
   int B, L, H, KV, hd, cap, window, offset;
+  int max_pos;             // rows of the cos/sin tables (device starts past them are clamped, *pos_flag set)
+  int* pos_flag;
   int rd;                  // rotated dimensions (even, <= hd); hd .. rd-1 pass through
   int defer_append;        // 1: leave the cache to launch_kv_append (after attention)
   float eps;
@@ -155,6 +157,7 @@ struct AttnArgs {
   const int* lengths;      // [B] start positions (null: zeros)
   void* ctx;               // [T, H*hd]
   int B, L, H, KV, hd, cap, window;
+  int max_pos;             // positions the block allows (device starts are clamped into range)
   float softcap;           // 0 = off
   float* part;             // decode partials [H, rec_stride, hd + 2]: record s + b = row b's piece of segment s
   int nseg, rec_stride;    // decode: key segments per kv head; records per head (>= nseg + B)

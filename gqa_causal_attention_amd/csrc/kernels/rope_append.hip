@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
   const int b = (int)(tok / a.L), t = (int)(tok % a.L);
   if (a.row_len && t >= a.row_len[b]) return;  // padding of a packed ragged row
   const int64_t prow = a.row_start ? a.row_start[b] + t : tok;
-  const int start = a.lengths ? a.lengths[b] : 0;
+  const int start = guarded_start(a.lengths, b, a.L, position_limit(a.window, a.cap, a.max_pos), a.pos_flag);
   const int pos = start + t;
   const int hd = a.hd, half = hd / 2;
   const int QW = a.H * hd, KW = a.KV * hd;
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void rope_append_vec_kernel(RopeArgs a) {
   // padding of a packed ragged row: not live (a whole head slot's lanes alike)
   if (a.row_len && t >= a.row_len[b]) live = false;
   const int64_t prow = a.row_start && live ? a.row_start[b] + t : (a.row_start ? 0 : tok);
-  const int pos = (a.lengths ? a.lengths[b] : 0) + t;
+  const int pos = guarded_start(a.lengths, b, a.L, position_limit(a.window, a.cap, a.max_pos), a.pos_flag) + t;
   const int QW = a.H * HD, KW = a.KV * HD;
   bf16* row = static_cast<bf16*>(a.qkv) + prow * a.ld;
   int kind, head;  // 0 = q, 1 = k, 2 = v
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(RopeArgs a) {
   const int64_t bh = i / per;
   const int b = (int)(bh / a.KV), head = (int)(bh % a.KV);
   const int t = a.L - keep + (int)((i % per) / a.hd), e = (int)(i % a.hd);
-  const int pos = (a.lengths ? a.lengths[b] : 0) + t;
+  const int pos = guarded_start(a.lengths, b, a.L, position_limit(a.window, a.cap, a.max_pos), nullptr) + t;
   const int slot = a.window > 0 ? pos % a.window : pos;
   const int64_t src = (((int64_t)b * a.KV + head) * a.L + t) * a.hd + e;
   const int64_t dst = (((int64_t)b * a.KV + head) * a.cap + slot) * a.hd + e;

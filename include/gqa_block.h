@@ -251,7 +251,16 @@ int gqa_block_step_noalloc(gqa_block* blk, gqa_state* st, const float* x_dev, fl
  * length, all W slots of a full window ring); a non-zero count is reported
  * here as GQA_ERR_NONFINITE with the count in the message, and cleared.  Off
  * by default: the scan reads the used cache once more, which would double a
- * decode step's cache traffic. */
+ * decode step's cache traffic.
+ * Positions: the capacity and max_positions checks of each call read the
+ * state's host copy of the lengths.  A forward/step captured into a HIP graph
+ * advances only the device lengths when replayed, so a replayed step must
+ * restore them itself (a device copy in the graph, or gqa_state_set_lengths)
+ * or the host copy no longer describes the cache.  As a guard, the kernels
+ * clamp any device start position that would fall outside the cache or the
+ * RoPE tables (so nothing is read or written out of bounds) and raise a flag
+ * reported here as GQA_ERR_POSITION (cleared); outputs since the previous
+ * check are then not valid.  Non-finite reports take second place. */
 int gqa_block_status(gqa_block* blk, void* hip_stream);
 
 /* Launch plan of a call, as text (introspection; no device work, nothing

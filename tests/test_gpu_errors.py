@@ -104,3 +104,43 @@ def test_check_finite_counts_cached_values(torch_cuda, dtype, window, monkeypatc
         else:
             blk.status()
     monkeypatch.delenv("GQA_CHECK_FINITE", raising=False)
+
+
+@pytest.mark.parametrize("dtype,window,L,dev_len", [
+    ("bf16", 0, 1, 16 + 5),     # decode step, device start past the capacity
+    ("bf16", 0, 1, -7),         # decode step, negative device start
+    ("f32", 0, 3, 15),          # continuation: start + L past the capacity
+    ("bf16", 0, 5, 14),         # bf16 continuation (matrix-core prefill attention)
+    ("bf16", 8, 5, 8192 + 1),   # window ring: start past the RoPE tables (max_positions)
+])
+def test_device_position_guard(torch_cuda, dtype, window, L, dev_len):
+    """A device start position the host mirror does not know of (what a replayed
+    captured step leaves when it does not restore the lengths), outside the
+    cache or the RoPE tables, is clamped by the kernels and reported by
+    status() as a position error; restoring the lengths recovers."""
+    torch = torch_cuda
+    from gqa_causal_attention_amd import Block
+    from gqa_causal_attention_amd.binding import GqaError
+    cfg, W = random_block(503, dtype=dtype, d_model=128, n_heads=4, n_kv_heads=2, head_dim=64, intermediate=256,
+                          window=window, max_positions=8192)
+    if dtype == "bf16":     # the matrix-core attention kernels take these shapes
+        plan = blk_plan = Block(cfg, W).describe_plan(2, L)
+        assert ("decode_splitk" if L == 1 else "prefill_mfma") in blk_plan, plan
+    rng = np.random.default_rng(504)
+    blk = Block(cfg, W)
+    st = blk.allocate_state(2, 16)
+    blk.forward(torch.from_numpy(rng.standard_normal((2, 4, 128), dtype=np.float32)).cuda(), st)
+    blk.status()
+    shape = (2, 128) if L == 1 else (2, L, 128)
+    x = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).cuda()
+    st.lengths.fill_(dev_len)           # device copy only; the host mirror still says 4
+    y = blk.step(x, st) if L == 1 else blk.forward(x, st)
+    torch.cuda.synchronize()
+    with pytest.raises(GqaError) as e:
+        blk.status()
+    assert e.value.name == "POSITION" and "restore" in str(e.value), str(e.value)
+    blk.status()                        # cleared
+    st.set_lengths([4, 4])
+    y = blk.step(x, st) if L == 1 else blk.forward(x, st)
+    blk.status()
+    assert torch.isfinite(y).all()
