@@ -287,11 +287,15 @@ GemmPlan plan_gemm(int M, int N, int K, bool gated) {
   }
   // M <= 64: the weight-streaming kernel, one 16-row weight group per wave.
   // Choose the K split s (a divisor of K / 256, splits at least kmin deep) and
-  // the waves per workgroup w (4..8, dividing the group count) by a simple
-  // cost: the bytes moved (weights, plus for s > 1 the float32 partials,
-  // written and read back: 2 * s * M * 4 bytes per weight row) over the rate,
-  // taken as full with 6 or more waves streaming per CU and proportional
-  // below, divided by the share of CU slots the grid's last round uses.
+  // the waves per workgroup w (4..8, dividing the group count) by a time
+  // model fitted to measurements on the 8B and Qwen-style decode shapes:
+  // workgroups run in rounds of one per CU, each round costing a fixed
+  // 4.5 us (prologue, pipeline fill, drain) plus its weight bytes (and its
+  // float32 partials) at 28 GB/s per CU with 6 or more waves, proportionally
+  // less below; K-split partials are read back at 2 TB/s, and a gated split
+  // needs its own reduce launch (5 us).  (Measured: Qwen-style gate/up, M = 16,
+  // 3456 groups, K = 5120, unsplit in 432 workgroups of 8 waves 92.9 us
+  // against 120.8 + 6.7 us in 4 splits over 2304 workgroups of 6.)
   static const int cus = [] {
     const char* e = getenv("GQA_SKINNY_CUS");  // tuning override
     return e ? atoi(e) : 256;
@@ -305,7 +309,6 @@ GemmPlan plan_gemm(int M, int N, int K, bool gated) {
   }();
   if (M <= 64 && K % 256 == 0) {
     const long groups = gemm_skinny_groups(N, gated);
-    const double rows = 16.0 * (double)groups;
     GemmPlan best{kTileSkinny, 0, 0};
     double best_cost = 0.0;
     for (int w = 8; w >= 4; --w)
@@ -313,9 +316,12 @@ GemmPlan plan_gemm(int M, int N, int K, bool gated) {
         if ((K / 256) % sp != 0 || (sp > 1 && K / sp < kmin)) continue;
         if (!gemm_skinny_supported(M, N, K, K / sp, w, gated)) continue;
         const long wgs = groups / w * sp;
-        const double fill = (double)wgs / (double)(((wgs + cus - 1) / cus) * cus);
-        const double bytes = rows * K * 2.0 + (sp > 1 ? 2.0 * sp * M * 4.0 * rows : 0.0);
-        const double cost = bytes / (w >= 6 ? 1.0 : w / 6.0) / fill;
+        const long rounds = (wgs + cus - 1) / cus;
+        const double part_wg = sp > 1 ? 16.0 * w * M * 4.0 : 0.0;          // partial bytes per workgroup
+        const double wg_bytes = 16.0 * w * (double)(K / sp) * 2.0 + part_wg;
+        const double rate = 28e3 * (w >= 6 ? 1.0 : w / 6.0);                // bytes per us per CU
+        double cost = rounds * (4.5 + wg_bytes / rate);
+        if (sp > 1) cost += part_wg * wgs / 2e6 + (gated ? 5.0 : 0.0);
         if (best.waves == 0 || cost < best_cost * (1.0 - 1e-9)) {
           best_cost = cost;
           best = {kTileSkinny, sp, w};
