@@ -270,13 +270,26 @@ GemmPlan plan_gemm(int M, int N, int K, bool gated) {
     if (M <= 512) return {kTile128x128, 1};
     const int cols256 = gated ? 128 : 256;
     const long t256 = (long)((M + 255) / 256) * ((N + cols256 - 1) / cols256);
+    const GemmPlan p256 = with_tail({big_tile(), 1}, M, N, K, cols256);
     const char* e192 = getenv("GQA_GEMM_TILE192");  // tuning override (0: never the 256x192 tile)
     if (!gated && N % 192 == 0 && !(e192 && atoi(e192) == 0)) {
+      // Estimated time in 64-deep slices of one 256x256 tile (1.84 us measured):
+      // a wave of 256x192 tiles takes 0.87 of a 256x256 wave of the same depth
+      // (8B q/k/v, Gemma2-style down); a tail split adds its depth per split and
+      // its float32 partials, written and read back at ~2.5 TB/s.
+      const double slices = K / 64.0;
       const long t192 = (long)((M + 255) / 256) * (N / 192);
-      auto eff = [](long t) { return (double)t / (double)(((t + 255) / 256) * 256); };
-      if (eff(t192) > eff(t256) + 0.05) return with_tail({big_tile_192(), 1}, M, N, K, 192);
+      const double est192 = (double)((t192 + 255) / 256) * 0.87 * slices;
+      double est256 = (double)((t256 + 255) / 256) * slices;
+      if (p256.tail_splits > 1) {
+        const long tail_tiles = p256.m1 > 0 ? ((M - p256.m1 + 255) / 256) * ((N + cols256 - 1) / cols256)
+                                            : ((M + 255) / 256) * ((N - p256.n1 + cols256 - 1) / cols256);
+        const double part = (double)tail_tiles * p256.tail_splits * 256.0 * 256.0 * 4.0 * 2.0;
+        est256 = (double)(t256 / 256) * slices + slices / p256.tail_splits + part / (2.5e12 * 1.84e-6);
+      }
+      if (est192 < est256) return with_tail({big_tile_192(), 1}, M, N, K, 192);
     }
-    return with_tail({big_tile(), 1}, M, N, K, cols256);
+    return p256;
   }
   if (M > 64) {
     const int cols = gated ? 64 : 128;
