@@ -201,6 +201,33 @@ def test_bf16_decode_gemm_batch_sizes(torch_cuda, kind, B):
                     f"{kind} B={B} step {i}")
 
 
+@pytest.mark.parametrize("B", [100, 520, 2100])
+def test_bf16_decode_many_rows(torch_cuda, B):
+    """Decode batches past the weight-streaming GEMM's 64 rows: 64x128 tiles
+    (M = 100), the pipelined large-M tiles (M = 520), and more rows than the
+    split-K decode attention's prefix table holds (2100: the matrix-core
+    prefill attention at L = 1 over the cache); each after a short prefill,
+    against the oracle."""
+    cfg, W = random_block(215, dtype="bf16", d_model=256, n_heads=8, n_kv_heads=2, head_dim=128,
+                          intermediate=512)
+    rng = np.random.default_rng(16 + B)
+    blk = _block(cfg, W)
+    plan = blk.describe_plan(B, 1)
+    want = {100: "gemm_o tile=2", 520: "gemm_o tile=7", 2100: "attention=prefill_mfma"}[B]
+    assert want in plan, plan
+    if B <= 520:
+        assert "attention=decode_splitk" in plan, plan
+    st = blk.allocate_state(B, 8)
+    ost = OracleState(cfg, B, 8)
+    x = rng.standard_normal((B, 3, cfg["d_model"]), dtype=np.float32)
+    check_close(blk.forward(to_gpu(x), st).cpu().numpy(), block_forward(cfg, W, x, ost), x, "bf16",
+                f"B={B} prefill")
+    for i in range(2):
+        xt = rng.standard_normal((B, cfg["d_model"]), dtype=np.float32)
+        check_close(blk.step(to_gpu(xt), st).cpu().numpy(), block_step(cfg, W, xt, ost), xt, "bf16",
+                    f"B={B} step {i}")
+
+
 def test_bf16_window_ring_wraps(torch_cuda):
     """Prefill longer than the window (in-call keys from the fresh K/V), then
     decode steps through the ring's wrap-around."""
