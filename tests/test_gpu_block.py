@@ -228,6 +228,51 @@ def test_bf16_decode_many_rows(torch_cuda, B):
                     f"B={B} step {i}")
 
 
+@pytest.mark.parametrize("dtype,window", [("bf16", 1), ("bf16", 2), ("f32", 1), ("bf16", 31)])
+def test_degenerate_windows(torch_cuda, dtype, window):
+    """The smallest windows: W = 1 (every position attends itself only, so the
+    attention output is its own value row) and W = 2, plus a window one
+    short of the prefill, through prefill, continuation and decode steps over
+    the ring, against the oracle."""
+    cfg, W = random_block(216 + window, dtype=dtype, d_model=256, n_heads=8, n_kv_heads=2, head_dim=128,
+                          intermediate=256, window=window)
+    rng = np.random.default_rng(30 + window)
+    blk = _block(cfg, W)
+    st = blk.allocate_state(2, 64)
+    ost = OracleState(cfg, 2, 64)
+    for L in (32, 5):
+        x = rng.standard_normal((2, L, 256), dtype=np.float32)
+        check_close(blk.forward(to_gpu(x), st).cpu().numpy(), block_forward(cfg, W, x, ost), x, dtype,
+                    f"W={window} L={L}")
+    for i in range(3):
+        xt = rng.standard_normal((2, 256), dtype=np.float32)
+        check_close(blk.step(to_gpu(xt), st).cpu().numpy(), block_step(cfg, W, xt, ost), xt, dtype,
+                    f"W={window} step {i}")
+
+
+def test_last_position(torch_cuda):
+    """Positions up to max_positions - 1 (the RoPE table's last row) match the
+    oracle; one more step is refused before any launch and leaves the state
+    unchanged."""
+    from gqa_causal_attention_amd.binding import GqaError
+    cfg, W = random_block(220, dtype="bf16", d_model=256, n_heads=8, n_kv_heads=2, head_dim=128,
+                          intermediate=256, max_positions=40)
+    rng = np.random.default_rng(40)
+    blk = _block(cfg, W)
+    st = blk.allocate_state(1, 64)
+    ost = OracleState(cfg, 1, 64)
+    x = rng.standard_normal((1, 36, 256), dtype=np.float32)
+    check_close(blk.forward(to_gpu(x), st).cpu().numpy(), block_forward(cfg, W, x, ost), x, "bf16", "prefill")
+    for i in range(4):   # positions 36 .. 39
+        xt = rng.standard_normal((1, 256), dtype=np.float32)
+        check_close(blk.step(to_gpu(xt), st).cpu().numpy(), block_step(cfg, W, xt, ost), xt, "bf16",
+                    f"position {36 + i}")
+    with pytest.raises(GqaError) as e:
+        blk.step(to_gpu(rng.standard_normal((1, 256), dtype=np.float32)), st)
+    assert e.value.name == "POSITION"
+    assert st.host_lengths().tolist() == [40]
+
+
 def test_bf16_window_ring_wraps(torch_cuda):
     """Prefill longer than the window (in-call keys from the fresh K/V), then
     decode steps through the ring's wrap-around."""
