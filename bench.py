@@ -393,8 +393,25 @@ def timed_replays(torch, graph, steps):
     return (time.perf_counter() - t1) * 1e3 / steps
 
 
+def merge_tails(times):
+    """A tail-split GEMM's launches (name, name_tail, name_tail_reduce) as one
+    entry: its whole time against its whole work."""
+    out = {}
+    for name, (tot, cnt) in times.items():
+        base = name[:-len("_tail_reduce")] if name.endswith("_tail_reduce") else (
+            name[:-len("_tail")] if name.endswith("_tail") else name)
+        if base != name and base in times:
+            t, c = out.get(base, (0.0, 0))
+            out[base] = (t + tot, c)
+        else:
+            t, c = out.get(name, (0.0, 0))
+            out[name] = (t + tot, c + cnt)
+    return out
+
+
 def breakdown_of(times, work, unit):
     out = {}
+    times = merge_tails(times)
     for name, (tot, cnt) in times.items():
         avg_ms = tot / max(cnt, 1)
         e = {"avg_us": round(avg_ms * 1e3, 2), "launches": cnt}
@@ -587,7 +604,7 @@ def leg_ragged(args, torch, steps=None):
         for _ in range(3):
             blk.forward(x, out=y, **kw)
         torch.cuda.synchronize()
-        per[name] = {k: round(v[0] / max(v[1], 1), 4) for k, v in blk.kernel_times().items()}
+        per[name] = {k: round(v[0] / max(v[1], 1), 4) for k, v in merge_tails(blk.kernel_times()).items()}
         blk.set_timing(False)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):

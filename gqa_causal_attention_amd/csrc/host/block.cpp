@@ -624,6 +624,31 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
   const int offset = c.norm == GQA_NORM_RMS_OFFSET;
   KernelTimer* tm = &blk->timer;
 
+  // A tail-split plan's launches: a1 = the full waves of tiles, then the tail
+  // a2 as K-split partials and the ordered reduce that applies the epilogue
+  // (timed as name, name_tail and name_tail_reduce: one launch each).
+  auto run_tail = [&](const char* name, const GemmArgs& a1, GemmArgs a2, int mode, int epi,
+                      const GemmPlan& p) -> int {
+    a2.bump = nullptr;  // a1 advances the lengths
+    GemmArgs pa = a2;
+    pa.splits = p.tail_splits;
+    pa.k_split = a2.K / p.tail_splits;
+    pa.partial = part;
+    const std::string tn = std::string(name) + "_tail", rn = tn + "_reduce";
+    {
+      Scope sc(tm, name, s);
+      HIP_TRY(launch_gemm_bf16(a1, mode, epi, p.tile, s));
+    }
+    {
+      Scope sc(tm, tn.c_str(), s);
+      HIP_TRY(launch_gemm_bf16(pa, mode, kEpiPartial, p.tile, s));
+    }
+    a2.splits = p.tail_splits;
+    a2.partial = part;
+    Scope sc(tm, rn.c_str(), s);
+    HIP_TRY(launch_splitk_reduce(a2, mode, epi, et, s));
+    return GQA_OK;
+  };
   // GEMM helper: fused epilogue, or K-split partials + ordered reduce.
   // (defer_reduce: leave the K-split partials in `part` for the next kernel,
   // which sums them itself)
@@ -674,19 +699,7 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
       GemmArgs a1 = columns(0, p.n1);
       a1.splits = 1;
       a1.k_split = a.K;
-      GemmArgs a2 = columns(p.n1, a.N);
-      a2.bump = nullptr;
-      GemmArgs pa = a2;
-      pa.splits = p.tail_splits;
-      pa.k_split = a.K / p.tail_splits;
-      pa.partial = part;
-      Scope sc(tm, name, s);
-      HIP_TRY(launch_gemm_bf16(a1, mode, epi, p.tile, s));
-      HIP_TRY(launch_gemm_bf16(pa, mode, kEpiPartial, p.tile, s));
-      a2.splits = p.tail_splits;
-      a2.partial = part;
-      HIP_TRY(launch_splitk_reduce(a2, mode, epi, et, s));
-      return GQA_OK;
+      return run_tail(name, a1, columns(p.n1, a.N), mode, epi, p);
     }
     if (p.splits <= 1 && p.tail_splits > 1 && p.m1 > 0 && p.m1 < a.M && !defer_reduce) {
       // rows [0, m1): the full waves of tiles; rows [m1, M): K-split, then the
@@ -702,18 +715,7 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
       a2.A = static_cast<const char*>(a.A) + (size_t)p.m1 * a.lda * a_es;
       a2.C = static_cast<char*>(a.C) + (size_t)p.m1 * a.ldc * es_out;
       if (a.resid) a2.resid = a.resid + (size_t)p.m1 * a.ldr;
-      a2.bump = nullptr;
-      GemmArgs pa = a2;
-      pa.splits = p.tail_splits;
-      pa.k_split = a.K / p.tail_splits;
-      pa.partial = part;
-      Scope sc(tm, name, s);
-      HIP_TRY(launch_gemm_bf16(a1, mode, epi, p.tile, s));
-      HIP_TRY(launch_gemm_bf16(pa, mode, kEpiPartial, p.tile, s));
-      a2.splits = p.tail_splits;
-      a2.partial = part;
-      HIP_TRY(launch_splitk_reduce(a2, mode, epi, et, s));
-      return GQA_OK;
+      return run_tail(name, a1, a2, mode, epi, p);
     }
     if (p.splits <= 1) {
       a.splits = 1;
