@@ -164,15 +164,20 @@ def family_of(role):
 
 
 def sources_hash(files):
+    """Hash of the code (comments and whitespace removed, so a reworded comment
+    keeps the stored counters) of the files and shared regions."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f, begin, end in [(f, None, None) for f in files] + SHARED_SOURCES:
-        with open(os.path.join(ROOT, "gqa_causal_attention_amd", f), "rb") as fh:
+        with open(os.path.join(ROOT, "gqa_causal_attention_amd", f), encoding="utf-8") as fh:
             data = fh.read()
         if begin is not None:
-            i = data.index(begin.encode())
-            data = data[i:data.index(end.encode(), i)]
-        h.update(data)
+            i = data.index(begin)
+            data = data[i:data.index(end, i)]
+        data = re.sub(r"/\*.*?\*/", " ", data, flags=re.S)
+        data = re.sub(r"//[^\n]*", " ", data)
+        h.update(" ".join(data.split()).encode())
     return h.hexdigest()[:16]
 
 

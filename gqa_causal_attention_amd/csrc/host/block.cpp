@@ -213,13 +213,14 @@ int big_tile_192() {
 }
 
 // Tile and K-split choice for a bf16 GEMM with M rows, N output columns, K
-// depth.  M > 512: the pipelined direct-to-LDS kernel, 256x256 or (when it
-// fills the 256 CUs better) 256x192 tiles.  129..512: 128x128 tiles.  65..128:
+// depth.  M > 512: the pipelined direct-to-LDS kernel, 256x256 or (when its
+// estimated time is lower) 256x192 tiles.  129..512: 128x128 tiles.  65..128:
 // 64x128 tiles with a K split.  M <= 64 (decode): the weight-streaming kernel
 // (below), else 64x64 tiles split while there are fewer than 256 tiles.
 // A large-M plan whose last wave of tiles fills at most half of the CUs:
-// rows covered by the full waves stay as they are; the remaining rows are
-// split along K so that their tiles x splits come close to one full wave
+// rows (or else columns) covered by the full waves stay as they are; the
+// remaining ones are split along K so that their tiles x splits come close
+// to one full wave
 // (splits 64-aligned and at least 512 deep).
 // Partials of the largest tail with_tail plans: at most one wave (256 units)
 // of tile x split, each 256 rows x at most 256 float32 columns.
