@@ -201,21 +201,21 @@ def test_bf16_decode_gemm_batch_sizes(torch_cuda, kind, B):
                     f"{kind} B={B} step {i}")
 
 
-@pytest.mark.parametrize("B", [100, 520, 2100])
+@pytest.mark.parametrize("B", [100, 520, 2048, 2100])
 def test_bf16_decode_many_rows(torch_cuda, B):
     """Decode batches past the weight-streaming GEMM's 64 rows: 64x128 tiles
-    (M = 100), the pipelined large-M tiles (M = 520), and more rows than the
-    split-K decode attention's prefix table holds (2100: the matrix-core
-    prefill attention at L = 1 over the cache); each after a short prefill,
-    against the oracle."""
+    (M = 100), the pipelined large-M tiles (M = 520), the split-K decode
+    attention at its largest row table (2048), and more rows than that table
+    holds (2100: the matrix-core prefill attention at L = 1 over the cache);
+    each after a short prefill, against the oracle."""
     cfg, W = random_block(215, dtype="bf16", d_model=256, n_heads=8, n_kv_heads=2, head_dim=128,
                           intermediate=512)
     rng = np.random.default_rng(16 + B)
     blk = _block(cfg, W)
     plan = blk.describe_plan(B, 1)
-    want = {100: "gemm_o tile=2", 520: "gemm_o tile=7", 2100: "attention=prefill_mfma"}[B]
+    want = {100: "gemm_o tile=2", 520: "gemm_o tile=7", 2048: "gemm_o tile=7", 2100: "attention=prefill_mfma"}[B]
     assert want in plan, plan
-    if B <= 520:
+    if B <= 2048:   # (2048: the split-K decode attention's largest row table)
         assert "attention=decode_splitk" in plan, plan
     st = blk.allocate_state(B, 8)
     ost = OracleState(cfg, B, 8)
