@@ -11,8 +11,16 @@
 // barrier per slice, placed after the last fragment reads of slice kt and
 // before that k-step's MFMAs: it publishes slice kt + 1 (every wave has waited
 // for its own loads of it) and frees slice kt's stage, which is refilled with
-// slice kt + ST at once; the MFMAs of the last k-step then overlap the first
-// fragment reads of slice kt + 1.
+// slice kt + ST; the MFMAs of the last k-step then overlap the first
+// fragment reads of slice kt + 1.  The refill's load instructions are spread
+// over that k-step, one group after the first MFMA of each row of MFMAs,
+// rather than issued in one burst: a wave issues in order, and while the L1's
+// queue of outstanding L2 requests is full (misses to the Infinity Cache or
+// HBM hold their entries for hundreds of cycles) a burst of loads keeps the
+// wave -- and, with every wave released by the same barrier, the SIMD -- from
+// issuing MFMAs (measured on the 4k-token prefill: gate/up 0.83 -> 0.78 ms;
+// spreading them over two k-steps leaves the later loads too little time to
+// land and is slower than the burst).
 //
 // A load instruction writes 64 lanes x 16 bytes contiguously into LDS, so the
 // LDS layout is chosen through the global address each lane reads: lane l of
@@ -312,6 +320,17 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
     }
   };
 
+  // Load instruction j of slice kt into `stage` (A's first), for the spread
+  // refill (non-transposed operands, A re-read schedule): LPR per row of MFMAs.
+  constexpr bool SPREAD = TR == 0 && SCHED == 1;
+  constexpr int LPR = (NLD + FM - 1) / FM;
+  auto issue_one = [&](int kt, int stage, int j) __attribute__((always_inline)) {
+    char* sA = smem + stage * STAGE_BYTES;
+    char* sB = sA + A_BYTES;
+    if (j < IA) load_lds16(gA[j] + (int64_t)kt * BK, sA + (wave + NW * j) * 1024);
+    else load_lds16(gB[j - IA] + (int64_t)kt * BK, sB + (wave + NW * (j - IA)) * 1024);
+  };
+
   // ---- fragment addressing: row lane % MF of an MF-row block, chunk CPF ks + lane / MF ----
   // (MF-row blocks start at multiples of 16 rows, so the XOR key is a function of lane % MF)
   const int frow = lane % MF, fhi = lane / MF;
@@ -392,7 +411,8 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
     constexpr int NWT = NW_A < NW_B ? NW_A : NW_B;
     if constexpr (NWT < 64) lgkm_wait<(NWT < 15 ? NWT : 15)>();
   };
-  auto step = [&](int cur, int stage, auto ks) __attribute__((always_inline)) {
+  // ldkt >= 0: spread the loads of slice ldkt into stage ldstage over this step
+  auto step = [&](int cur, int stage, auto ks, int ldkt = -1, int ldstage = 0) __attribute__((always_inline)) {
     if constexpr (SCHED == 1) {
       static_for<0, FM>([&](auto i_c) {
         constexpr int i = decltype(i_c)::value;
@@ -408,6 +428,12 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
         for (int j = 0; j < FN; ++j) {
           acc[i][j] = MM::run(fa[0][i], fb[cur][j], acc[i][j]);
           if (j < BPR && i * BPR + j < FN) rd(stage, ks, cur ^ 1, FM + i * BPR + j);
+          if constexpr (SPREAD) {
+            if (j == 0 && ldkt >= 0) {
+#pragma unroll
+              for (int q = i * LPR; q < (i + 1) * LPR && q < NLD; ++q) issue_one(ldkt, ldstage, q);
+            }
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
         rd(stage, ks, 0, i);
@@ -448,11 +474,11 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
       wait_slices<NLD, ST - 2>(min(ST - 2, nk - 2 - kt));
       if constexpr (TR != 0) lgkm_wait<0>();
       lds_sync();  // publishes slice kt + 1; every wave is done reading stage `stage`
-      if (kt + ST < nk) issue(kt + ST, stage);
+      if (!SPREAD && kt + ST < nk) issue(kt + ST, stage);
     }
     // (after the last slice these reads fetch an unused stage: harmless, and it
     // keeps a single copy of the MFMA sequence in the loop)
-    step((KS - 1) & 1, (kt + 1) % ST, IntC<0>{});
+    step((KS - 1) & 1, (kt + 1) % ST, IntC<0>{}, (SPREAD && kt + ST < nk) ? kt + ST : -1, stage);
   }
   if constexpr (TR != 0) lgkm_wait<0>();  // the last step's reads, before LDS is reused
 
