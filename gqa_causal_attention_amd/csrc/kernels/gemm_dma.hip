@@ -502,19 +502,54 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
   // staging tile, then all threads read it back row-major and apply the
   // epilogue with 16-byte loads and stores, whole rows per wave.  (The gated
   // gate/up epilogue stays direct: its tiles are many per CU, so their
-  // stores overlap other tiles' main loops, and measured slower staged.) ----
+  // stores overlap other tiles' main loops, and measured slower staged.)
+  // A pass's global operands (residual and bias, the backward's gate / up
+  // pre-activations) are all loaded before its staging writes: the output may
+  // alias them, so loads interleaved with the stores would each wait for the
+  // previous piece's round trip (one HBM latency per piece, every CU at once
+  // on the shapes with one tile per CU).  The barriers order LDS only, so
+  // the loads and the previous pass's stores stay in flight across them. ----
   if constexpr (MF == 16 && (EPI == kEpiResid || EPI == kEpiStore || EPI == kEpiSwigluBwd)) {
     constexpr int COLS = MODE == kModeGated ? BN / 2 : BN;  // output columns of the tile
     constexpr int SW = COLS + 4;                            // staging row stride (floats): 4 rows per
                                                             // write land 16 banks apart
     constexpr int PR = 64;                                  // rows per pass
+    constexpr int PIT = PR * (COLS / 4) / NT;               // 16-byte pieces per thread per pass
     static_assert(PR * SW * 4 <= ST * STAGE_BYTES, "staging tile fits in the pipeline's LDS");
     static_assert(COLS % 4 == 0 && WTM % PR == 0 || PR % WTM == 0, "pass rows cover whole wave rows");
+    static_assert(PR * (COLS / 4) % NT == 0, "a pass's pieces split evenly over the threads");
+    constexpr bool GU = EPI == kEpiSwigluBwd, PRE = EPI != kEpiStore;  // PRE: operands loaded up front
     float* stg = reinterpret_cast<float*>(smem);
     const int col0 = tn * COLS;
 #pragma unroll 1
     for (int pass = 0; pass < BM / PR; ++pass) {
-      __syncthreads();  // the previous pass's reads (or the main loop's) are done
+      // piece it of this thread: row r, columns c .. c + 3 of the pass
+      auto piece = [&](int it, int& r, int& c) {
+        const int idx = tid + it * NT;
+        r = idx / (COLS / 4);
+        c = (idx % (COLS / 4)) * 4;
+      };
+      // residual and bias (added when the piece is stored, so neither load
+      // waits for the other) / gate and up
+      f32x4 g0[PRE ? PIT : 1], g1[PRE ? PIT : 1];
+#pragma unroll
+      for (int it = 0; it < (PRE ? PIT : 0); ++it) {
+        int r, c;
+        piece(it, r, c);
+        const int m = m0 + pass * PR + r, n = col0 + c;
+        g0[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+        g1[it] = g0[it];
+        if (m >= a.M || n >= a.N) continue;
+        if constexpr (GU) {
+          const float* gu = a.resid + (int64_t)m * a.ldr + n;
+          g0[it] = *reinterpret_cast<const f32x4*>(gu);
+          g1[it] = *reinterpret_cast<const f32x4*>(gu + a.N);
+        } else {
+          if (a.resid) g0[it] = *reinterpret_cast<const f32x4*>(a.resid + (int64_t)m * a.ldr + n);
+          if (a.bias[0]) g1[it] = *reinterpret_cast<const f32x4*>(a.bias[0] + n);
+        }
+      }
+      lds_sync();  // the previous pass's staging reads (or the main loop's fragment reads) are done
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int rb = wm * WTM + i * 16;  // first tile row of block i
@@ -534,48 +569,47 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
           }
         }
       }
-      __syncthreads();
-      for (int idx = tid; idx < PR * (COLS / 4); idx += NT) {
-        const int r = idx / (COLS / 4), c = (idx % (COLS / 4)) * 4;
-        const int m = m0 + pass * PR + r;
-        const int n = col0 + c;
-        if (m >= a.M || n >= a.N) continue;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(stg + r * SW + c);
-        if constexpr (EPI == kEpiSwigluBwd) {
-          // v = da; the recomputed gate / up pre-activations of the same columns
-          const float* gu = a.resid + (int64_t)m * a.ldr + n;
-          const f32x4 g4 = *reinterpret_cast<const f32x4*>(gu);
-          const f32x4 u4 = *reinterpret_cast<const f32x4*>(gu + a.N);
-          bf16x4 ov, og, ou;
+      lds_sync();
+      if constexpr (PRE) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float g = g4[e], u = u4[e];
-            const float sg = 1.0f / (1.0f + __expf(-g));
-            const float sl = g * sg;
-            ov[e] = from_f32<bf16>(sl * u);
-            og[e] = from_f32<bf16>(v[e] * u * sg * (1.0f + g * (1.0f - sg)));
-            ou[e] = from_f32<bf16>(v[e] * sl);
+        for (int it = 0; it < PIT; ++it) {
+          int r, c;
+          piece(it, r, c);
+          const int m = m0 + pass * PR + r, n = col0 + c;
+          if (m >= a.M || n >= a.N) continue;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(stg + r * SW + c);
+          if constexpr (GU) {
+            // v = da; g0 / g1 the recomputed gate / up pre-activations of the same columns
+            bf16x4 ov, og, ou;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float g = g0[it][e], u = g1[it][e];
+              const float sg = 1.0f / (1.0f + __expf(-g));
+              const float sl = g * sg;
+              ov[e] = from_f32<bf16>(sl * u);
+              og[e] = from_f32<bf16>(v[e] * u * sg * (1.0f + g * (1.0f - sg)));
+              ou[e] = from_f32<bf16>(v[e] * sl);
+            }
+            bf16* c2 = static_cast<bf16*>(a.C2) + (int64_t)m * a.ldc2 + n;
+            *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.C) + (int64_t)m * a.ldc + n) = ov;
+            *reinterpret_cast<bf16x4*>(c2) = og;
+            *reinterpret_cast<bf16x4*>(c2 + a.N) = ou;
+          } else {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(a.C) + (int64_t)m * a.ldc + n) = g0[it] + (v + g1[it]);
           }
-          bf16* c2 = static_cast<bf16*>(a.C2) + (int64_t)m * a.ldc2 + n;
-          *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.C) + (int64_t)m * a.ldc + n) = ov;
-          *reinterpret_cast<bf16x4*>(c2) = og;
-          *reinterpret_cast<bf16x4*>(c2 + a.N) = ou;
-        } else if constexpr (EPI == kEpiResid) {
-          f32x4 t = v;
-          if (a.bias[0]) t += *reinterpret_cast<const f32x4*>(a.bias[0] + n);
-          if (a.resid) t = *reinterpret_cast<const f32x4*>(a.resid + (int64_t)m * a.ldr + n) + t;
-          *reinterpret_cast<f32x4*>(static_cast<float*>(a.C) + (int64_t)m * a.ldc + n) = t;
-        } else {
+        }
+      } else {  // kEpiStore (+ segment bias, act): no residual, the bias reads are L2 hits
+        for (int idx = tid; idx < PR * (COLS / 4); idx += NT) {
+          const int r = idx / (COLS / 4), c = (idx % (COLS / 4)) * 4;
+          const int m = m0 + pass * PR + r, n = col0 + c;
+          if (m >= a.M || n >= a.N) continue;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(stg + r * SW + c);
           bf16x4 o;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float x = v[e];
-            if constexpr (EPI == kEpiStore) {
-              const int sg = seg_of(a, n + e);
-              if (a.bias[sg]) x += a.bias[sg][n + e - (sg == 0 ? 0 : a.seg_end[sg - 1])];
-              x = act_t<ACT>(x);
-            }
-            o[e] = from_f32<bf16>(x);
+            const int sg = seg_of(a, n + e);
+            const float b = a.bias[sg] ? a.bias[sg][n + e - (sg == 0 ? 0 : a.seg_end[sg - 1])] : 0.f;
+            o[e] = from_f32<bf16>(act_t<ACT>(v[e] + b));
           }
           *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.C) + (int64_t)m * a.ldc + n) = o;
         }
