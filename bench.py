@@ -288,16 +288,20 @@ def ingest_counters(leg, name, dirs):
         with open(path) as f:
             old = json.load(f)
         if old.get("leg") == leg:
+            kept = False  # does any value of the old record survive (then its commands stay listed)?
             for role, k in old.get("kernels", {}).items():
                 if role in out["kernels"] and k.get("sources_hash") == out["kernels"][role]["sources_hash"]:
                     merged = dict(k)
+                    kept = kept or any(c not in out["kernels"][role]["avg"] for c in k.get("avg", {}))
                     merged["avg"] = dict(k.get("avg", {}), **out["kernels"][role]["avg"])
                     merged.update({kk: vv for kk, vv in out["kernels"][role].items() if kk != "avg"})
                     out["kernels"][role] = merged
                 elif role not in out["kernels"]:
                     out["kernels"][role] = k
-            out["commands"] = sorted(set(old.get("commands", [])) | set(cmds))
-            out["calibration"] = dict(old.get("calibration", {}), **calib)
+                    kept = True
+            if kept:
+                out["commands"] = sorted(set(old.get("commands", [])) | set(cmds))
+                out["calibration"] = dict(old.get("calibration", {}), **calib)
     except (OSError, ValueError):
         pass
     os.makedirs(os.path.dirname(path), exist_ok=True)
