@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict
   const int64_t r = i / IT;
   const int c = (int)(i % IT);
   const float g = gu[r * 2 * IT + c], u = gu[r * 2 * IT + IT + c];
-  const float s = 1.0f / (1.0f + __expf(-g));
+  const float s = sigmoid(g);
   const float sl = g * s;
   act[i] = from_f32<T>(sl * u);
   const float d = da[i];

@@ -33,15 +33,21 @@ __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr float kLog2e = 1.4426950408889634f;
 
+// 1 / x with the hardware reciprocal (1 ulp): the elementwise activations are
+// rounded to bf16 (or feed bf16 products) right after, so IEEE division's
+// ~10-instruction sequence buys nothing.  rcp(inf) = 0.
+__device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
+
 // tanh from its definition tanh(x) = 1 - 2 / (e^{2x} + 1); saturates to +-1
 // (e^{2x} -> inf gives 1, e^{2x} -> 0 gives -1).
 __device__ __forceinline__ float tanh_exp(float x) {
   float e = exp2_fast(2.0f * kLog2e * x);
-  return 1.0f - 2.0f / (e + 1.0f);
+  return 1.0f - 2.0f * rcp_fast(e + 1.0f);
 }
 
-// SiLU(z) = z / (1 + e^{-z}).
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + exp2_fast(-kLog2e * z)); }
+// Logistic sigmoid 1 / (1 + e^{-z}) and SiLU(z) = z * sigmoid(z).
+__device__ __forceinline__ float sigmoid(float z) { return rcp_fast(1.0f + exp2_fast(-kLog2e * z)); }
+__device__ __forceinline__ float silu(float z) { return z * sigmoid(z); }
 
 // GELU, tanh form: 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
 __device__ __forceinline__ float gelu_tanh(float z) {

@@ -584,7 +584,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const float g = g0[it][e], u = g1[it][e];
-              const float sg = 1.0f / (1.0f + __expf(-g));
+              const float sg = sigmoid(g);
               const float sl = g * sg;
               ov[e] = from_f32<bf16>(sl * u);
               og[e] = from_f32<bf16>(v[e] * u * sg * (1.0f + g * (1.0f - sg)));
