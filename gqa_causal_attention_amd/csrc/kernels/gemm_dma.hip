@@ -632,6 +632,37 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
       buv[j] = a.bias[1] ? a.bias[1][n] : 0.f;
     }
   }
+  if constexpr (EPI == kEpiGated && MF == 16) {
+    // A tile wholly inside the output (every gate/up tile at the 8B shapes)
+    // stores without bounds tests: the row base is wave-uniform (scalar
+    // registers), the lane's offset one 32-bit register, and the column
+    // blocks immediate offsets -- with the tests, every 2-byte store sat in
+    // its own masked block behind a 64-bit address computation.
+    if (m0 + BM <= a.M && tn * (BN / 2) + BN / 2 <= a.N && a.ldc <= (int64_t)1 << 28) {  // (32-bit lane offsets)
+      const int wu = __builtin_amdgcn_readfirstlane(wave);
+      const int64_t ldc = a.ldc;
+      const bf16* base = static_cast<const bf16*>(a.C) + (int64_t)(m0 + (wu / WGN) * WTM) * ldc + tn * (BN / 2) +
+                         (wu % WGN) * (WTN / 2);
+      const uint32_t loff = (uint32_t)((lane >> 4) * 4) * (uint32_t)ldc + (uint32_t)lcol;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bf16* row = const_cast<bf16*>(base) + (int64_t)(i * MF + e) * ldc;
+#pragma unroll
+          for (int j = 0; j < FN / 2; ++j) {
+            float g = acc[i][j][e], u = acc[i][j + FN / 2][e];
+            if constexpr (GBIAS) {
+              g += bgv[j];
+              u += buv[j];
+            }
+            row[loff + j * MF] = from_f32<bf16>(act_t<ACT>(g) * u);
+          }
+        }
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
