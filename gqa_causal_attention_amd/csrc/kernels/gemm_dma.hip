@@ -521,6 +521,10 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
     constexpr bool GU = EPI == kEpiSwigluBwd, PRE = EPI != kEpiStore;  // PRE: operands loaded up front
     float* stg = reinterpret_cast<float*>(smem);
     const int col0 = tn * COLS;
+    // A store-epilogue tile wholly inside the output, with no bias, skips the
+    // bounds tests and the per-element bias segment lookups and addresses its
+    // pieces from a per-pass (wave-uniform) base with 32-bit offsets
+    const bool full = EPI == kEpiStore && m0 + BM <= a.M && col0 + COLS <= a.N && a.ldc <= (int64_t)1 << 24;  // (r * ldc + c < 2^31)
 #pragma unroll 1
     for (int pass = 0; pass < BM / PR; ++pass) {
       // piece it of this thread: row r, columns c .. c + 3 of the pass
@@ -532,6 +536,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
       // residual and bias (added when the piece is stored, so neither load
       // waits for the other) / gate and up
       f32x4 g0[PRE ? PIT : 1], g1[PRE ? PIT : 1];
+      const int64_t prow = m0 + pass * PR;  // first row of the pass
 #pragma unroll
       for (int it = 0; it < (PRE ? PIT : 0); ++it) {
         int r, c;
@@ -597,6 +602,18 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
           } else {
             *reinterpret_cast<f32x4*>(static_cast<float*>(a.C) + (int64_t)m * a.ldc + n) = g0[it] + (v + g1[it]);
           }
+        }
+      } else if (full && !a.bias[0] && !a.bias[1] && !a.bias[2]) {  // kEpiStore, no bias
+        bf16* cb = static_cast<bf16*>(a.C) + prow * a.ldc + col0;
+#pragma unroll
+        for (int it = 0; it < PIT; ++it) {
+          int r, c;
+          piece(it, r, c);
+          const f32x4 v = *reinterpret_cast<const f32x4*>(stg + r * SW + c);
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = from_f32<bf16>(act_t<ACT>(v[e]));
+          *reinterpret_cast<bf16x4*>(cb + (uint32_t)(r * (int)a.ldc + c)) = o;
         }
       } else {  // kEpiStore (+ segment bias, act): no residual, the bias reads are L2 hits
         for (int idx = tid; idx < PR * (COLS / 4); idx += NT) {
