@@ -521,18 +521,37 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
     constexpr bool GU = EPI == kEpiSwigluBwd, PRE = EPI != kEpiStore;  // PRE: operands loaded up front
     float* stg = reinterpret_cast<float*>(smem);
     const int col0 = tn * COLS;
-    // A store-epilogue tile wholly inside the output, with no bias, skips the
-    // bounds tests and the per-element bias segment lookups and addresses its
-    // pieces from a per-pass (wave-uniform) base with 32-bit offsets
+    // A store-epilogue tile wholly inside the output skips the bounds tests,
+    // addresses its pieces from a per-pass (wave-uniform) base with 32-bit
+    // offsets, and takes each piece's biases (segment lookups included) from
+    // registers filled once: a thread's columns are the same in every pass.
     const bool full = EPI == kEpiStore && m0 + BM <= a.M && col0 + COLS <= a.N && a.ldc <= (int64_t)1 << 24;  // (r * ldc + c < 2^31)
+    // piece it of this thread: row r (within the pass), columns c .. c + 3
+    auto piece = [&](int it, int& r, int& c) {
+      const int idx = tid + it * NT;
+      r = idx / (COLS / 4);
+      c = (idx % (COLS / 4)) * 4;
+    };
+    f32x4 sbias[EPI == kEpiStore ? PIT : 1];
+    if constexpr (EPI == kEpiStore) {
+#pragma unroll
+      for (int it = 0; it < PIT; ++it) sbias[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (full && (a.bias[0] || a.bias[1] || a.bias[2])) {
+#pragma unroll
+        for (int it = 0; it < PIT; ++it) {
+          int r, c;
+          piece(it, r, c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int n = col0 + c + e;
+            const int sg = seg_of(a, n);
+            sbias[it][e] = a.bias[sg] ? a.bias[sg][n - (sg == 0 ? 0 : a.seg_end[sg - 1])] : 0.f;
+          }
+        }
+      }
+    }
 #pragma unroll 1
     for (int pass = 0; pass < BM / PR; ++pass) {
-      // piece it of this thread: row r, columns c .. c + 3 of the pass
-      auto piece = [&](int it, int& r, int& c) {
-        const int idx = tid + it * NT;
-        r = idx / (COLS / 4);
-        c = (idx % (COLS / 4)) * 4;
-      };
       // residual and bias (added when the piece is stored, so neither load
       // waits for the other) / gate and up
       f32x4 g0[PRE ? PIT : 1], g1[PRE ? PIT : 1];
@@ -603,7 +622,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
             *reinterpret_cast<f32x4*>(static_cast<float*>(a.C) + (int64_t)m * a.ldc + n) = g0[it] + (v + g1[it]);
           }
         }
-      } else if (full && !a.bias[0] && !a.bias[1] && !a.bias[2]) {  // kEpiStore, no bias
+      } else if (full) {  // kEpiStore, whole tile
         bf16* cb = static_cast<bf16*>(a.C) + prow * a.ldc + col0;
 #pragma unroll
         for (int it = 0; it < PIT; ++it) {
@@ -612,7 +631,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_dma_kernel(GemmArgs a) 
           const f32x4 v = *reinterpret_cast<const f32x4*>(stg + r * SW + c);
           bf16x4 o;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = from_f32<bf16>(act_t<ACT>(v[e]));
+          for (int e = 0; e < 4; ++e) o[e] = from_f32<bf16>(act_t<ACT>(v[e] + sbias[EPI == kEpiStore ? it : 0][e]));
           *reinterpret_cast<bf16x4*>(cb + (uint32_t)(r * (int)a.ldc + c)) = o;
         }
       } else {  // kEpiStore (+ segment bias, act): no residual, the bias reads are L2 hits
