@@ -139,18 +139,21 @@ __global__ __launch_bounds__(256) void rope_append_kernel(RopeArgs a) {
 // (4g .. 4g+3, 4g+r/2 .. 4g+r/2+3); lane g >= r/8 owns the pass-through
 // elements 8g .. 8g+7.  The qk-norm sum of squares is reduced across the
 // head's lanes with shuffles.
+// Grid: x = token (row-major over B, L), y = blocks of 256 (slot, lane)
+// pairs of the token, so a thread finds its token and slot without 64-bit
+// divisions (one uniform 32-bit division by L, a shift by the power-of-two GH).
 template <int HD>
 __global__ __launch_bounds__(256) void rope_append_vec_kernel(RopeArgs a) {
   constexpr int HALF = HD / 2, GH = HALF / 4;  // lanes per head slot
+  static_assert((GH & (GH - 1)) == 0, "lanes per head slot: a power of two");
   const int slots = a.H + 2 * a.KV;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t T_ = (int64_t)a.B * a.L;
-  bool live = idx < T_ * slots * GH;
-  const int64_t hs = live ? idx / GH : 0;     // (token, slot)
-  const int g = (int)(idx % GH);
-  const int64_t tok = hs / slots;
-  const int slot = (int)(hs % slots);
-  const int b = (int)(tok / a.L), t = (int)(tok % a.L);
+  const int tok = blockIdx.x;
+  const int hsl = blockIdx.y * 256 + threadIdx.x;  // (slot, lane) within the token
+  bool live = hsl < slots * GH;
+  const int slot = live ? hsl / GH : 0;
+  const int g = hsl % GH;
+  const int b = tok / a.L, t = tok - b * a.L;
   // padding of a packed ragged row: not live (a whole head slot's lanes alike)
   if (a.row_len && t >= a.row_len[b]) live = false;
   const int64_t prow = a.row_start && live ? a.row_start[b] + t : (a.row_start ? 0 : tok);
@@ -300,8 +303,11 @@ hipError_t launch_kv_append(const RopeArgs& a, int elem, hipStream_t s) {
 
 template <int HD>
 hipError_t launch_vec(const RopeArgs& a, hipStream_t s) {
-  const int64_t n = (int64_t)a.B * a.L * (a.H + 2 * a.KV) * (HD / 8);
-  hipLaunchKernelGGL(rope_append_vec_kernel<HD>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  const int64_t tokens = (int64_t)a.B * a.L;
+  const int per_token = (a.H + 2 * a.KV) * (HD / 8);
+  if (tokens > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rope_append_vec_kernel<HD>, dim3((unsigned)tokens, (unsigned)((per_token + 255) / 256)), dim3(256), 0,
+                     s, a);
   return hipGetLastError();
 }
 
