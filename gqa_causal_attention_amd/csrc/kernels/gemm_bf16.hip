@@ -238,13 +238,24 @@ __global__ __launch_bounds__(WGM* WGN * 64, 1) void gemm_bf16_kernel(GemmArgs a)
 
 // Sum of the K-split partials in split order, then the epilogue.
 template <typename OutT, int MODE, int EPI>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a) {
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a, int rows_in_y) {
   const int64_t N4 = a.N / 4;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (a.bump && blockIdx.x == 0)
+  if (a.bump && blockIdx.x == 0 && blockIdx.y == 0)
     for (int i = threadIdx.x; i < a.bump_n; i += 256) a.bump[i] += a.bump_by;
-  if (idx >= (int64_t)a.M * N4) return;
-  const int64_t m = idx / N4, n = (idx % N4) * 4;
+  // rows_in_y: grid y = row, x = blocks of 4-column groups (no 64-bit division);
+  // else a 1-D grid over row x group
+  int64_t m, n;
+  if (rows_in_y) {
+    const int q = blockIdx.x * 256 + threadIdx.x;
+    if (q >= N4) return;
+    m = blockIdx.y;
+    n = (int64_t)q * 4;
+  } else {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)a.M * N4) return;
+    m = idx / N4;
+    n = (idx % N4) * 4;
+  }
   const int64_t NB = MODE == kModeGated ? 2 * (int64_t)a.N : a.N;
   f32x4 s = {0.f, 0.f, 0.f, 0.f}, su = {0.f, 0.f, 0.f, 0.f};
   // (unrolled so the splits' loads are in flight together; the adds stay in split order)
@@ -332,20 +343,21 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, int mode, int epi, int tile, hipS
 
 hipError_t launch_splitk_reduce(const GemmArgs& a, int mode, int epi, int out_type, hipStream_t s) {
   const int64_t work = (int64_t)a.M * (a.N / 4);
-  dim3 grid((unsigned)((work + 255) / 256));
+  const int rows_in_y = a.M <= 65535 ? 1 : 0;
+  dim3 grid = rows_in_y ? dim3((unsigned)((a.N / 4 + 255) / 256), (unsigned)a.M) : dim3((unsigned)((work + 255) / 256));
   if (mode == kModeGated) {
     if (epi != kEpiGated) return hipErrorInvalidValue;
     if (out_type == kBF16)
-      hipLaunchKernelGGL((splitk_reduce_kernel<bf16, kModeGated, kEpiGated>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((splitk_reduce_kernel<bf16, kModeGated, kEpiGated>), grid, dim3(256), 0, s, a, rows_in_y);
     else
-      hipLaunchKernelGGL((splitk_reduce_kernel<float, kModeGated, kEpiGated>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((splitk_reduce_kernel<float, kModeGated, kEpiGated>), grid, dim3(256), 0, s, a, rows_in_y);
   } else if (epi == kEpiResid) {
-    hipLaunchKernelGGL((splitk_reduce_kernel<float, kModeSeg, kEpiResid>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((splitk_reduce_kernel<float, kModeSeg, kEpiResid>), grid, dim3(256), 0, s, a, rows_in_y);
   } else if (epi == kEpiStore) {
     if (out_type == kBF16)
-      hipLaunchKernelGGL((splitk_reduce_kernel<bf16, kModeSeg, kEpiStore>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((splitk_reduce_kernel<bf16, kModeSeg, kEpiStore>), grid, dim3(256), 0, s, a, rows_in_y);
     else
-      hipLaunchKernelGGL((splitk_reduce_kernel<float, kModeSeg, kEpiStore>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((splitk_reduce_kernel<float, kModeSeg, kEpiStore>), grid, dim3(256), 0, s, a, rows_in_y);
   } else {
     return hipErrorInvalidValue;
   }

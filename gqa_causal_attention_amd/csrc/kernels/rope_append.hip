@@ -287,12 +287,42 @@ __global__ __launch_bounds__(256) void kv_append_kernel(RopeArgs a) {
   static_cast<T*>(a.vcache)[dst] = static_cast<const T*>(a.vnew)[src];
 }
 
+// The same copy in 16-byte chunks: grid y = (row, kv head), x = blocks of
+// chunks of its last `keep` positions (cpr chunks per position).
+template <typename T>
+__global__ __launch_bounds__(256) void kv_append_vec_kernel(RopeArgs a, int keep, int cpr) {
+  const int q = blockIdx.x * 256 + threadIdx.x;
+  if (q >= keep * cpr) return;
+  const int bh = blockIdx.y;
+  const int b = bh / a.KV;
+  const int tr = q / cpr, ch = q - tr * cpr;
+  const int t = a.L - keep + tr;
+  const int pos = guarded_start(a.lengths, b, a.L, position_limit(a.window, a.cap, a.max_pos), nullptr) + t;
+  const int slot = a.window > 0 ? pos % a.window : pos;
+  constexpr int E = 16 / sizeof(T);  // elements per chunk
+  const int64_t src = ((int64_t)bh * a.L + t) * a.hd + ch * E;
+  const int64_t dst = ((int64_t)bh * a.cap + slot) * a.hd + ch * E;
+  *reinterpret_cast<uint4*>(static_cast<T*>(a.kcache) + dst) = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.knew) + src);
+  *reinterpret_cast<uint4*>(static_cast<T*>(a.vcache) + dst) = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.vnew) + src);
+}
+
 }  // namespace
 
 hipError_t launch_kv_append(const RopeArgs& a, int elem, hipStream_t s) {
   const int keep = a.window > 0 ? (a.L < a.window ? a.L : a.window) : a.L;
   const int64_t n = (int64_t)a.B * a.KV * keep * a.hd;
   if (n == 0 || !a.kcache) return hipSuccess;
+  const int es = elem == kBF16 ? 2 : 4;
+  const int64_t bh = (int64_t)a.B * a.KV;
+  if ((a.hd * es) % 16 == 0 && bh <= 65535 && (int64_t)keep * (a.hd * es / 16) < 0x7fffff00) {
+    const int cpr = a.hd * es / 16;
+    dim3 vgrid((unsigned)(((int64_t)keep * cpr + 255) / 256), (unsigned)bh);
+    if (elem == kBF16)
+      hipLaunchKernelGGL(kv_append_vec_kernel<bf16>, vgrid, dim3(256), 0, s, a, keep, cpr);
+    else
+      hipLaunchKernelGGL(kv_append_vec_kernel<float>, vgrid, dim3(256), 0, s, a, keep, cpr);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((n + 255) / 256));
   if (elem == kBF16)
     hipLaunchKernelGGL(kv_append_kernel<bf16>, grid, dim3(256), 0, s, a);
