@@ -788,7 +788,17 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
     if (int r = gemm("gemm_qkv", a, kModeSeg, kEpiStore, lay.p_qkv, fuse_qkv)) return r;
   }
   // 3. q/k norm + RoPE; keys/values of this call to knew/vnew and into the cache
-  // (a windowed call with L > 1 writes the ring after attention instead)
+  // (a windowed call with L > 1 writes the ring after attention instead).  On
+  // the matrix-core prefill path with whole-head rotation the attention kernel
+  // normalises and rotates q as it loads it, so this step handles k and v only
+  // (not for the backward, which reads the rotated q back).
+  static const bool rope_q_env = [] {
+    const char* e = getenv("GQA_ROPE_Q_IN_ATTN");  // tuning override (0: q rotated by the RoPE kernel)
+    return !(e && atoi(e) == 0);
+  }();
+  const bool rope_in_attn = rope_q_env && bf && !lay.decode_attn && !recompute_only && !fuse_qkv &&
+                            c.rope_dim == hd && hd <= 128 && attention_prefill_bf16_supported(hd, blk->G) &&
+                            rope_append_fuses_reduce(hd, c.rope_dim, QW + 2 * KW, et);
   RopeArgs r{};
   {
     r.qkv = qkv; r.ld = QW + 2 * KW;
@@ -807,6 +817,7 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
       r.row_len = pk->row_len;
     }
     r.prows = T;
+    r.skip_q = rope_in_attn;
     if (fuse_qkv) {
       r.part = part;
       r.splits = lay.p_qkv.splits;
@@ -846,6 +857,12 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
       HIP_TRY(launch_attention_decode_combine(a, s));
     } else if (bf && attention_prefill_bf16_supported(hd, blk->G)) {
       a.lse = attn_lse;
+      if (rope_in_attn) {
+        a.rope_q = 1;
+        a.cos_tab = blk->cos_tab; a.sin_tab = blk->sin_tab;
+        a.q_norm = static_cast<const float*>(blk->w[W_QN]);
+        a.rd = c.rope_dim; a.offset = offset; a.eps = c.norm_eps;
+      }
       if (pk) {
         a.row_start = pk->row_start;
         a.row_len = pk->row_len;

@@ -32,6 +32,11 @@
 //    through the global address each lane fetches) so that the fragment reads
 //    of 16 consecutive rows, or the 8 rows x 64 bytes of a transposing read,
 //    spread over all LDS banks.
+//  * With whole-head RoPE, q arrives as the projection left it: the kernel
+//    applies the per-head q norm and the rotation to its Q^T fragments in
+//    registers (each lane holds both halves of every rotation pair), once
+//    the first K/V tile's loads are in flight, which saves the RoPE kernel a
+//    read and a write of every query.
 //  * Softmax in float32 (dew CausalTransformer force_fp32_for_softmax) with
 //    base-2 exponentials; the scale is folded into one multiply.  The running
 //    reference max is raised lazily: the output is rescaled only when a
@@ -74,6 +79,53 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units: lazily rescale beyond 2^8
 __device__ __forceinline__ float tanh_rcp(float x) {
   const float e = exp2_fast(2.0f * kLog2e * x);
   return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+}
+
+// q norm and RoPE of a lane's Q^T fragments (8 dims ks * 16 + khi * 8 .. + 7
+// per step ks), for the whole-head rotation (rope_dim = head_dim): the
+// rotate-half partner of step ks < KS/2 is step ks + KS/2 of the same lane.
+// Same float32 arithmetic as the RoPE kernel; the head's sum of squares meets
+// the other half of its dims in lane ^ 32.  Applied after the first K/V
+// tile's loads are issued, so the cos / sin (and norm weight) loads wait
+// alongside them.
+template <int HD>
+__device__ __forceinline__ void rope_q_frags(bf16x8 (&qf)[HD / 16], const AttnArgs& a, int pos, int khi) {
+  constexpr int KS = HD / 16, HK = KS / 2, RH = HD / 2;
+  const float* ct = a.cos_tab + (int64_t)pos * RH + khi * 8;
+  const float* st = a.sin_tab + (int64_t)pos * RH + khi * 8;
+  float x[KS][8];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[ks][e] = to_f32(qf[ks][e]);
+  if (a.q_norm) {
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += x[ks][e] * x[ks][e];
+    ss += xor32(ss);
+    const float r = 1.0f / sqrtf(ss / (float)HD + a.eps);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float w = a.q_norm[ks * 16 + khi * 8 + e];
+        x[ks][e] *= r * (a.offset ? 1.0f + w : w);
+      }
+  }
+#pragma unroll
+  for (int ks = 0; ks < HK; ++ks) {
+    const f32x4 c0 = *reinterpret_cast<const f32x4*>(ct + ks * 16), c1 = *reinterpret_cast<const f32x4*>(ct + ks * 16 + 4);
+    const f32x4 s0 = *reinterpret_cast<const f32x4*>(st + ks * 16), s1 = *reinterpret_cast<const f32x4*>(st + ks * 16 + 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float c = e < 4 ? c0[e & 3] : c1[e & 3], sn = e < 4 ? s0[e & 3] : s1[e & 3];
+      const float x1 = x[ks][e], x2 = x[ks + HK][e];
+      qf[ks][e] = from_f32<bf16>(x1 * c - x2 * sn);
+      qf[ks + HK][e] = from_f32<bf16>(x2 * c + x1 * sn);
+    }
+  }
 }
 
 __device__ __forceinline__ const bf16* kv_row(const AttnArgs& a, const void* fresh, const void* cache, int b, int j,
@@ -144,11 +196,13 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_kernel(AttnArgs a, in
 
   // ---- Q^T fragments: column = query token, 8 consecutive dims per lane ----
   bf16x8 qf[KS];
+  int qpos;  // this lane's query position (clamped to the row's last token)
   {
     const int tok = min(qt0 + (lane & 31), L - 1);
     const bf16* qr = static_cast<const bf16*>(a.q) + (row0 + tok) * a.ldq + (int64_t)h * HD + khi * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qr + ks * 16);
+    qpos = start + tok;
   }
 
   // ---- one K/V tile: C::NI load instructions each, spread over the waves.
@@ -461,6 +515,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_prefill_kernel(AttnArgs a, in
   // tile in every run, so all waves stay in step.  (Separate loops keep the
   // two paths' registers apart.) ----
   if (ntiles > 0) issue(0, 0);
+  if constexpr (HD <= 128)  // (head_dim 256 has no registers to spare: q rotated by the RoPE kernel)
+    if (a.rope_q) rope_q_frags<HD>(qf, a, qpos, khi);
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of tile 0 (and Q) are done
   lds_sync();
   if (ntiles > 1) issue(1, 1);
@@ -600,6 +656,7 @@ bool attention_prefill_bf16_supported(int hd, int G) {
 
 hipError_t launch_attention_prefill_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.B * a.L == 0) return hipSuccess;
+  if (a.rope_q && (a.rd != a.hd || a.hd > 128 || !a.cos_tab || !a.sin_tab)) return hipErrorInvalidValue;
   switch (a.hd) {
     case 64: return launch_hd<64>(a, s);
     case 128: return launch_hd<128>(a, s);

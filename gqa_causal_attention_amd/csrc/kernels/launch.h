@@ -141,6 +141,7 @@ struct RopeArgs {
   const int* row_start;
   const int* row_len;
   int64_t prows;           // rows of the q|k|v activations (and of each K split of `part`); 0: B * L
+  int skip_q;              // vector form without `part`: leave q to the attention kernel (keys/values only)
 };
 // True if launch_rope_append takes `part` for this shape and element type.
 bool rope_append_fuses_reduce(int hd, int rd, int64_t ld, int elem);
@@ -168,6 +169,16 @@ struct AttnArgs {
   // knew/vnew [B, KV, L, hd].  Null: token (b, t) is row b * L + t.
   const int* row_start;
   const int* row_len;
+  // Prefill bf16 kernel: if rope_q, q is read as the projection left it and the
+  // kernel applies the per-head q norm (q_norm, eps, offset: weight 1 + w) and
+  // RoPE at positions start + t (tables [max_positions, rd/2], rd % 32 == 0)
+  // itself, rounding to bf16 as the RoPE kernel would have stored it.
+  int rope_q;
+  const float* cos_tab;
+  const float* sin_tab;
+  const float* q_norm;
+  int rd, offset;
+  float eps;
 };
 hipError_t launch_attention_generic(const AttnArgs& a, int elem, hipStream_t s);
 hipError_t launch_attention_prefill_bf16(const AttnArgs& a, hipStream_t s);

@@ -17,6 +17,10 @@
 // the vector form (a thread per 8 elements); other shapes the wave-per-head
 // form.
 //
+// With skip_q (vector form, no fused reduction) the grid covers the key and
+// value slots only: the prefill attention kernel normalises and rotates q as
+// it loads it.
+//
 // Outputs: q rotated in place; this call's keys (rotated) and values into
 // knew/vnew [B, KV, L, hd]; and, with a cache, the same keys/values into
 // slot p (full cache) or p mod W (sliding-window ring, mojolearn
@@ -146,12 +150,13 @@ template <int HD>
 __global__ __launch_bounds__(256) void rope_append_vec_kernel(RopeArgs a) {
   constexpr int HALF = HD / 2, GH = HALF / 4;  // lanes per head slot
   static_assert((GH & (GH - 1)) == 0, "lanes per head slot: a power of two");
-  const int slots = a.H + 2 * a.KV;
+  const int q0 = a.skip_q ? a.H : 0;  // first head slot of the grid
+  const int slots = a.H + 2 * a.KV - q0;
   const int64_t T_ = (int64_t)a.B * a.L;
   const int tok = blockIdx.x;
   const int hsl = blockIdx.y * 256 + threadIdx.x;  // (slot, lane) within the token
   bool live = hsl < slots * GH;
-  const int slot = live ? hsl / GH : 0;
+  const int slot = (live ? hsl / GH : 0) + q0;
   const int g = hsl % GH;
   const int b = tok / a.L, t = tok - b * a.L;
   // padding of a packed ragged row: not live (a whole head slot's lanes alike)
@@ -334,7 +339,7 @@ hipError_t launch_kv_append(const RopeArgs& a, int elem, hipStream_t s) {
 template <int HD>
 hipError_t launch_vec(const RopeArgs& a, hipStream_t s) {
   const int64_t tokens = (int64_t)a.B * a.L;
-  const int per_token = (a.H + 2 * a.KV) * (HD / 8);
+  const int per_token = (a.H + 2 * a.KV - (a.skip_q ? a.H : 0)) * (HD / 8);
   if (tokens > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(rope_append_vec_kernel<HD>, dim3((unsigned)tokens, (unsigned)((per_token + 255) / 256)), dim3(256), 0,
                      s, a);
@@ -353,6 +358,7 @@ hipError_t launch_rope_append(const RopeArgs& a, int elem, hipStream_t s) {
   if (a.rd < 2 || a.rd > a.hd || a.rd % 2) return hipErrorInvalidValue;
   const bool vec = rope_append_fuses_reduce(a.hd, a.rd, a.ld, elem);
   if (a.part && (!vec || a.splits < 1)) return hipErrorInvalidValue;
+  if (a.skip_q && (!vec || a.part)) return hipErrorInvalidValue;
   if (vec) {
     if (a.hd == 64) return launch_vec<64>(a, s);
     if (a.hd == 128) return launch_vec<128>(a, s);

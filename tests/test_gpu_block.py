@@ -66,6 +66,10 @@ BF16_CASES = {
     "qwen_bias_qknorm_g5": (dict(d_model=640, n_heads=10, n_kv_heads=2, head_dim=128,
                                  intermediate=640, qkv_bias=True, qk_norm=True), 1, 130, 5, 2),
     "mha_g1": (dict(d_model=256, n_heads=2, n_kv_heads=2, head_dim=128, intermediate=256), 1, 70, 0, 2),
+    # qk_norm with the (1 + w) norm weights, whole-head RoPE (the prefill
+    # attention kernel normalises and rotates q itself)
+    "qknorm_offset_hd64": (dict(d_model=256, n_heads=8, n_kv_heads=2, head_dim=64, intermediate=384,
+                                qk_norm=True, norm="rmsnorm_offset", mlp="geglu_tanh"), 2, 150, 20, 2),
     "big_m_tiles": (dict(d_model=512, n_heads=4, n_kv_heads=1, head_dim=128, intermediate=768,
                          rope_theta=5e5), 1, 1100, 0, 1),
     # RoPE options: the Llama 3.1 ramp; partial rotary with linear scaling and
