@@ -792,10 +792,8 @@ int run_block(gqa_block* blk, gqa_state* st, const float* x, float* y, int B, in
   // the matrix-core prefill path with whole-head rotation the attention kernel
   // normalises and rotates q as it loads it, so this step handles k and v only
   // (not for the backward, which reads the rotated q back).
-  static const bool rope_q_env = [] {
-    const char* e = getenv("GQA_ROPE_Q_IN_ATTN");  // tuning override (0: q rotated by the RoPE kernel)
-    return !(e && atoi(e) == 0);
-  }();
+  const char* rq_env = getenv("GQA_ROPE_Q_IN_ATTN");  // tuning override (0: q rotated by the RoPE kernel)
+  const bool rope_q_env = !(rq_env && atoi(rq_env) == 0);
   const bool rope_in_attn = rope_q_env && bf && !lay.decode_attn && !recompute_only && !fuse_qkv &&
                             c.rope_dim == hd && hd <= 128 && attention_prefill_bf16_supported(hd, blk->G) &&
                             rope_append_fuses_reduce(hd, c.rope_dim, QW + 2 * KW, et);

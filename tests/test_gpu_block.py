@@ -420,6 +420,27 @@ def test_bf16_gemm_column_tail_split(torch_cuda, monkeypatch):
     check_close(y, plain, x, "bf16", "column-tail vs whole-wave GEMMs")
 
 
+@pytest.mark.parametrize("qk_norm", [False, True])
+def test_bf16_rope_q_in_attention_matches_rope_kernel(torch_cuda, monkeypatch, qk_norm):
+    """The prefill attention kernel's own q norm + RoPE against the same
+    prefill with q rotated by the RoPE kernel (GQA_ROPE_Q_IN_ATTN=0): both round
+    float32 rotations of the same values to bf16 (contraction and the norm's
+    order of summation may differ in the last bits), so the sublayer outputs
+    agree far inside the bf16 tolerance, where a wrong rotation partner, sign or
+    position would not; the fused path also against the oracle."""
+    cfg, W = random_block(47 + qk_norm, dtype="bf16", d_model=512, n_heads=8, n_kv_heads=2, head_dim=128,
+                          intermediate=768, qk_norm=qk_norm, norm="rmsnorm_offset" if qk_norm else "rmsnorm")
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((2, 300, 512), dtype=np.float32)
+    blk = _block(cfg, W)
+    y = blk.forward(to_gpu(x)).cpu().numpy()
+    monkeypatch.setenv("GQA_ROPE_Q_IN_ATTN", "0")
+    y0 = blk.forward(to_gpu(x)).cpu().numpy()
+    monkeypatch.delenv("GQA_ROPE_Q_IN_ATTN")
+    assert rel_err(y - x, y0 - x) < 2e-3
+    check_close(y, block_forward(cfg, W, x, dtype=np.float32), x, "bf16", "q RoPE in attention")
+
+
 def test_page_worked_example_golden(torch_cuda):
     """The HIP block on the mojolearn page's usage example (float32 weights,
     TransformerBlock(weights, n_heads=4) on x of shape (2, 16, 64)) against the
